@@ -1,0 +1,171 @@
+"""Seeded synthetic inputs for Ring Self-Attention workloads.
+
+This module is shared by the CPU oracle's tests, the GPU parity tests and the
+bench. It holds none of the attention arithmetic: only random draws, a
+bf16 round-to-nearest-even helper that turns fp32 draws into bf16-representable
+values, the key-padding-mask constructor and the named workload shapes.
+
+The review page of "Sequence Parallelism: Making 4D Parallelism Possible"
+(ABSTRACT; proposed-method section) names no dataset: the method splits a
+sequence of attention embeddings into chunks. The workloads below stand in
+for those embeddings with i.i.d. normal draws at the shapes used to exercise
+and measure the method.
+
+Recipe (identical for every caller):
+  * generator ``numpy.random.Generator(PCG64(seed))``;
+  * ``standard_normal`` fp64 draws, in the order Q, K, V, then dO if asked;
+  * each draw multiplied by the workload's scale (exact for 0.5) and cast to
+    fp32; bf16 workloads are then rounded to bf16 by RNE (kept as fp32 values
+    that are exactly representable in bf16);
+  * if a valid-length range ``[lo, hi]`` is given, one integer per batch row
+    is drawn with ``integers(lo, hi + 1, size=B)`` after the tensors, and key
+    j of row b is valid iff ``j < valid_len[b]``.
+"""
+
+from __future__ import annotations
+
+import dataclasses
+from typing import Optional, Tuple
+
+import numpy as np
+
+__all__ = [
+    "bf16_round",
+    "bf16_bits",
+    "bits_to_f32",
+    "Workload",
+    "WORKLOADS",
+    "make_inputs",
+    "prefix_mask",
+]
+
+
+def bf16_round(x) -> np.ndarray:
+    """Round fp32 values to the nearest bf16 value (ties to even).
+
+    Returns fp32 values that are exactly representable in bf16. Inputs must be
+    finite (the generator never produces NaN or Inf).
+    """
+    x32 = np.ascontiguousarray(x, dtype=np.float32)
+    u = x32.view(np.uint32).astype(np.uint64)
+    keep_lsb = (u >> np.uint64(16)) & np.uint64(1)
+    r = (u + np.uint64(0x7FFF) + keep_lsb) & np.uint64(0xFFFF0000)
+    return r.astype(np.uint32).view(np.float32).reshape(x32.shape)
+
+
+def bf16_bits(x) -> np.ndarray:
+    """The 16-bit patterns of bf16-representable fp32 values (upper halves)."""
+    x32 = np.ascontiguousarray(x, dtype=np.float32)
+    u = x32.view(np.uint32)
+    if np.any(u & np.uint32(0xFFFF)):
+        raise ValueError("values are not bf16-representable; call bf16_round first")
+    return (u >> np.uint32(16)).astype(np.uint16)
+
+
+def bits_to_f32(bits) -> np.ndarray:
+    """Widen bf16 bit patterns (uint16) to fp32 values exactly."""
+    b = np.ascontiguousarray(bits, dtype=np.uint16)
+    return (b.astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def prefix_mask(valid_len, L: int) -> np.ndarray:
+    """Key-padding mask [B, L] uint8: key j of row b is valid iff j < valid_len[b]."""
+    vl = np.asarray(valid_len, dtype=np.int64).reshape(-1, 1)
+    return (np.arange(L, dtype=np.int64)[None, :] < vl).astype(np.uint8)
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    """One named RSA workload: shapes, element type, scale, mask and seed."""
+
+    name: str
+    B: int
+    H: int
+    L: int
+    d: int
+    N: int
+    dtype: str  # "f32" or "bf16"
+    seed: int
+    scale: float = 1.0
+    valid_range: Optional[Tuple[int, int]] = None
+    rank: Optional[int] = None  # one rank's share only (Q holds L/N rows)
+    backward: bool = False
+    description: str = ""
+
+    @property
+    def Lc(self) -> int:
+        return self.L // self.N
+
+    @property
+    def Lq(self) -> int:
+        return self.Lc if self.rank is not None else self.L
+
+
+# Named workloads. "share" workloads hold only one rank's query rows (L/N of
+# them) against all L keys, exactly as one device of the ring sees them.
+WORKLOADS = {
+    "fp32_small": Workload(
+        "fp32_small", B=1, H=2, L=256, d=64, N=4, dtype="f32", seed=1,
+        description="fp32, B=1 H=2 L=256 d=64, N=4 chunks of 64, no mask"),
+    "bert_base": Workload(
+        "bert_base", B=8, H=12, L=512, d=64, N=4, dtype="bf16", seed=2,
+        valid_range=(384, 512),
+        description="bf16 BERT-Base-shaped, B=8 H=12 L=512 d=64, N=4, key padding"),
+    "long_seq": Workload(
+        "long_seq", B=2, H=12, L=8192, d=64, N=16, dtype="bf16", seed=3,
+        description="bf16 long sequence, B=2 H=12 L=8192 d=64, N=16 chunks of 512, no mask"),
+    "rank_share": Workload(
+        "rank_share", B=1, H=16, L=32768, d=128, N=64, dtype="bf16", seed=4,
+        scale=0.5, valid_range=(24576, 32768), rank=0,
+        description="bf16 one rank's share: 512 query rows vs 32768 keys in 64 chunks, "
+                    "H=16 d=128, N(0,1)*0.5, key padding"),
+    "backward": Workload(
+        "backward", B=4, H=12, L=4096, d=64, N=8, dtype="bf16", seed=5,
+        valid_range=(3072, 4096), backward=True,
+        description="bf16 backward, B=4 H=12 L=4096 d=64, N=8, key padding"),
+    "backward_fd": Workload(
+        "backward_fd", B=1, H=1, L=32, d=64, N=8, dtype="f64", seed=6,
+        valid_range=(24, 32), backward=True,
+        description="fp64 finite-difference slice, B=1 H=1 L=32 d=64, N=8"),
+}
+
+
+def make_inputs(B: int, H: int, L: int, d: int, seed: int, dtype: str = "bf16",
+                scale: float = 1.0, valid_range: Optional[Tuple[int, int]] = None,
+                Lq: Optional[int] = None, with_dout: bool = False) -> dict:
+    """Draw seeded Q, K, V (and dO) following the module's recipe.
+
+    Q is [B, H, Lq, d] (Lq defaults to L); K and V are [B, H, L, d]; dO has
+    Q's shape. Returns numpy arrays: fp32 for "f32" and
+    "bf16" (bf16-representable values for the latter), fp64 for "f64". The
+    mask is None when ``valid_range`` is None.
+    """
+    if dtype not in ("f32", "bf16", "f64"):
+        raise ValueError(f"unknown dtype {dtype!r}")
+    Lq = L if Lq is None else Lq
+    rng = np.random.Generator(np.random.PCG64(seed))
+
+    def draw(shape):
+        x = rng.standard_normal(shape) * scale
+        if dtype == "f64":
+            return x
+        x = x.astype(np.float32)
+        return bf16_round(x) if dtype == "bf16" else x
+
+    out = {"q": draw((B, H, Lq, d)), "k": draw((B, H, L, d)), "v": draw((B, H, L, d))}
+    out["dout"] = draw((B, H, Lq, d)) if with_dout else None
+    if valid_range is not None:
+        lo, hi = valid_range
+        valid_len = rng.integers(lo, hi + 1, size=B)
+        out["valid_len"] = valid_len
+        out["mask"] = prefix_mask(valid_len, L)
+    else:
+        out["valid_len"] = None
+        out["mask"] = None
+    return out
+
+
+def workload_inputs(w: Workload) -> dict:
+    """Inputs of a named workload, following the module's recipe."""
+    return make_inputs(w.B, w.H, w.L, w.d, w.seed, w.dtype, w.scale, w.valid_range,
+                       Lq=w.Lq, with_dout=w.backward)
