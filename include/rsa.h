@@ -1,0 +1,123 @@
+/*
+ * rsa.h -- C ABI of librsa.so, Ring Self-Attention (RSA) on AMD Instinct
+ * MI355X (gfx950).
+ *
+ * The operation (review page of "Sequence Parallelism: Making 4D Parallelism
+ * Possible", ABSTRACT and proposed-method section): the input sequence is
+ * split into N chunks, one per device; to produce the attention output each
+ * device's query chunk meets every key chunk and every value chunk, which
+ * travel around a ring of devices. The pages give no formula; the library
+ * computes plain scaled-dot-product attention,
+ *
+ *     O = softmax(Q K^T / sqrt(d) + M) V,
+ *
+ * where M is 0 for valid keys and -inf for padded keys, with the key and
+ * value chunks of rank n visited in ring order c = (n - t) mod N for ring
+ * step t = 0..N-1. On one GPU the ring is a rotation of chunk pointers inside
+ * the kernels; the result does not depend on N beyond rounding.
+ *
+ * Conventions shared by every entry point
+ *   Layout   q, k, v, out, dout, dq, dk, dv: [B, H, L, d] contiguous, row
+ *            major, d fastest (a one-rank share uses L/N rows for q and out).
+ *            key_mask: [B, L] uint8, nonzero = valid key, the same for every
+ *            head and query row; NULL = every key valid.
+ *            lse: [B, H, rows] fp32, natural-log sum of exp of the scaled
+ *            scores of each query row (-inf for a row with no valid key).
+ *   dtype    RSA_F32 (fp32 in, fp32 out) or RSA_BF16 (bf16 in, bf16 out;
+ *            products accumulate in fp32).
+ *   Sizes    B, H, L, d, N > 0; L % N == 0; d is 64 or 128.
+ *   Memory   every pointer except `stream` is device memory owned by the
+ *            caller; the library allocates nothing, keeps no pointer after
+ *            return and holds no state, so calls are thread-safe.
+ *   Stream   work is enqueued on `stream` (a hipStream_t; NULL = default
+ *            stream); no entry point synchronises. Device faults surface at
+ *            the caller's next synchronisation.
+ *   Errors   arguments are validated before any HIP call; a non-zero
+ *            rsa_status is returned and nothing is enqueued. RSA_ERR_HIP
+ *            reports a failed launch (hipGetLastError). Rows with no valid
+ *            key produce zeros (never NaN).
+ */
+#ifndef RSA_H
+#define RSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum rsa_status {
+    RSA_OK = 0,
+    RSA_ERR_NULL = 1,        /* a required pointer is NULL */
+    RSA_ERR_SHAPE = 2,       /* a size is <= 0, L % N != 0, or rank outside [0, N) */
+    RSA_ERR_UNSUPPORTED = 3, /* d not in {64, 128}, unknown dtype, or a size beyond the kernels' range */
+    RSA_ERR_ALIGN = 4,       /* a tensor pointer is not 16-byte aligned */
+    RSA_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than the query function returns */
+    RSA_ERR_HIP = 6          /* the HIP runtime reported an error at launch */
+} rsa_status;
+
+typedef enum rsa_dtype { RSA_F32 = 0, RSA_BF16 = 1 } rsa_dtype;
+
+/*
+ * Full RSA forward: all N ranks' shares at once. Rank n owns query rows
+ * [n*L/N, (n+1)*L/N) and visits key/value chunks (n - t) mod N for
+ * t = 0..N-1 (ABSTRACT: each chunk on its own device, attention output
+ * formed by circulating embeddings in a ring).
+ *   q, k, v  [B,H,L,d] of dtype (inputs)
+ *   key_mask [B,L] uint8 or NULL
+ *   out      [B,H,L,d] of dtype (output)
+ *   lse      [B,H,L] fp32 (output) or NULL
+ */
+int rsa_forward(const void* q, const void* k, const void* v, const uint8_t* key_mask,
+                int B, int H, int L, int d, int N, int dtype,
+                void* stream, void* out, float* lse);
+
+/*
+ * One rank's share, as one device of the ring computes it (ABSTRACT: no
+ * device holds the whole sequence's queries): q_local holds rank `rank`'s
+ * L/N query rows, k and v hold all L keys, visited in the ring order of that
+ * rank. The ring steps are split into groups processed in parallel; each
+ * group's unnormalised output and softmax statistics go to `workspace` and
+ * are merged exactly (log-sum-exp combination) into out_local.
+ *   q_local   [B,H,L/N,d] of dtype (input)
+ *   k, v      [B,H,L,d] of dtype (inputs)
+ *   workspace device buffer of at least rsa_forward_rank_workspace_bytes()
+ *   out_local [B,H,L/N,d] of dtype (output); lse_local [B,H,L/N] fp32 or NULL
+ */
+int rsa_forward_rank(const void* q_local, const void* k, const void* v, const uint8_t* key_mask,
+                     int B, int H, int L, int d, int N, int rank, int dtype,
+                     void* workspace, size_t workspace_bytes,
+                     void* stream, void* out_local, float* lse_local);
+
+/* Workspace bytes rsa_forward_rank needs for these sizes (0 if they are invalid). */
+size_t rsa_forward_rank_workspace_bytes(int B, int H, int L, int d, int N);
+
+/*
+ * Backward of the loss <O, dO> (proposed-method section: gradients also pass
+ * through the ring): dq, dk, dv for all ranks. `out` and `lse` are the
+ * forward's outputs for the same inputs. Rank n's query chunk meets every
+ * key chunk in ring order, and the dK/dV contributions of every query chunk
+ * are summed at the key chunk they belong to.
+ *   q, k, v, out, dout [B,H,L,d] of dtype (inputs); lse [B,H,L] fp32 (input)
+ *   workspace          at least rsa_backward_workspace_bytes()
+ *   dq, dk, dv         [B,H,L,d] of dtype (outputs)
+ * Only RSA_BF16 is supported (RSA_ERR_UNSUPPORTED for RSA_F32).
+ */
+int rsa_backward(const void* q, const void* k, const void* v, const void* out, const void* dout,
+                 const float* lse, const uint8_t* key_mask,
+                 int B, int H, int L, int d, int N, int dtype,
+                 void* workspace, size_t workspace_bytes,
+                 void* stream, void* dq, void* dk, void* dv);
+
+/* Workspace bytes rsa_backward needs for these sizes (0 if they are invalid). */
+size_t rsa_backward_workspace_bytes(int B, int H, int L, int d, int N, int dtype);
+
+/* A static, human-readable name for a status code. */
+const char* rsa_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RSA_H */

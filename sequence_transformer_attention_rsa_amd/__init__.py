@@ -1,0 +1,208 @@
+"""Ring Self-Attention (RSA) on AMD Instinct MI355X -- Python binding.
+
+A thin ctypes layer over ``librsa.so`` (C ABI in ``include/rsa.h``). It only
+marshals arguments: shapes and dtypes are checked, outputs are allocated with
+torch on the inputs' device, and the library is called on the current HIP
+stream. Every step of the computation runs in the library's HIP kernels; if
+the library is not built, every call raises.
+
+    out = rsa.forward(q, k, v, key_mask=None, N=4)
+    out, lse = rsa.forward(q, k, v, N=4, return_lse=True)
+    out_local = rsa.forward_rank(q_local, k, v, N=64, rank=3)
+    dq, dk, dv = rsa.backward(q, k, v, out, dout, lse, N=8)
+
+Shapes: q, k, v, out, dout: [B, H, L, d] contiguous (q_local and out_local:
+[B, H, L/N, d]); key_mask: [B, L] bool or uint8 (nonzero = valid key);
+lse: [B, H, rows] fp32. dtypes: torch.float32 or torch.bfloat16.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+__all__ = [
+    "RSAError", "lib_path", "load", "forward", "forward_rank", "backward",
+    "forward_rank_workspace_bytes", "backward_workspace_bytes", "status_string",
+    "RSA_F32", "RSA_BF16",
+]
+
+RSA_F32 = 0
+RSA_BF16 = 1
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "librsa.so")
+_lib = None
+
+_vp = ctypes.c_void_p
+_ci = ctypes.c_int
+_sz = ctypes.c_size_t
+
+# (name, restype, argtypes) for every symbol of include/rsa.h
+SIGNATURES = {
+    "rsa_forward": (_ci, [_vp, _vp, _vp, _vp, _ci, _ci, _ci, _ci, _ci, _ci, _vp, _vp, _vp]),
+    "rsa_forward_rank": (_ci, [_vp, _vp, _vp, _vp, _ci, _ci, _ci, _ci, _ci, _ci, _ci, _vp, _sz, _vp, _vp, _vp]),
+    "rsa_forward_rank_workspace_bytes": (_sz, [_ci, _ci, _ci, _ci, _ci]),
+    "rsa_backward": (_ci, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _ci, _ci, _ci, _ci, _ci, _ci,
+                           _vp, _sz, _vp, _vp, _vp, _vp]),
+    "rsa_backward_workspace_bytes": (_sz, [_ci, _ci, _ci, _ci, _ci, _ci]),
+    "rsa_status_string": (ctypes.c_char_p, [_ci]),
+}
+
+
+class RSAError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {status_string(status)} (status {status})")
+
+
+def lib_path() -> str:
+    return _LIB_PATH
+
+
+def load():
+    """Load librsa.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise RuntimeError(
+                f"{_LIB_PATH} is not built; run `python -m sequence_transformer_attention_rsa_amd.build`")
+        lib = ctypes.CDLL(_LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = lib
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return load().rsa_status_string(int(status)).decode()
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return RSA_F32
+    if t.dtype == torch.bfloat16:
+        return RSA_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}; use torch.float32 or torch.bfloat16")
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _need(t: torch.Tensor, name: str, shape, dtype, device):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _mask(key_mask, B, L, device):
+    if key_mask is None:
+        return None
+    if key_mask.dtype not in (torch.uint8, torch.bool):
+        raise TypeError("key_mask must be bool or uint8")
+    _need(key_mask, "key_mask", (B, L), key_mask.dtype, device)
+    return key_mask
+
+
+def forward(q, k, v, key_mask=None, N: int = 1, return_lse: bool = False, out=None, lse=None):
+    """RSA forward over all N ranks: softmax(q k^T / sqrt(d) + mask) v."""
+    B, H, L, d = q.shape
+    dev = q.device
+    _need(q, "q", (B, H, L, d), q.dtype, dev)
+    _need(k, "k", (B, H, L, d), q.dtype, dev)
+    _need(v, "v", (B, H, L, d), q.dtype, dev)
+    m = _mask(key_mask, B, L, dev)
+    code = _dtype_code(q)
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, "out", (B, H, L, d), q.dtype, dev)
+    if lse is None and return_lse:
+        lse = torch.empty((B, H, L), dtype=torch.float32, device=dev)
+    if lse is not None:
+        _need(lse, "lse", (B, H, L), torch.float32, dev)
+    st = load().rsa_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(m), B, H, L, d, int(N), code,
+                            _stream(dev), _ptr(out), _ptr(lse))
+    if st != 0:
+        raise RSAError(st, "rsa_forward")
+    return (out, lse) if (return_lse or lse is not None) else out
+
+
+def forward_rank_workspace_bytes(B: int, H: int, L: int, d: int, N: int) -> int:
+    return int(load().rsa_forward_rank_workspace_bytes(B, H, L, d, N))
+
+
+def forward_rank(q_local, k, v, key_mask=None, N: int = 1, rank: int = 0, return_lse: bool = False,
+                 out=None, lse=None, workspace=None):
+    """One rank's share: q_local [B,H,L/N,d] against all L keys in that rank's ring order."""
+    B, H, L, d = k.shape
+    dev = k.device
+    if N <= 0 or L % N != 0:
+        raise ValueError("N must divide L")
+    Lc = L // N
+    _need(q_local, "q_local", (B, H, Lc, d), k.dtype, dev)
+    _need(v, "v", (B, H, L, d), k.dtype, dev)
+    m = _mask(key_mask, B, L, dev)
+    code = _dtype_code(k)
+    if out is None:
+        out = torch.empty_like(q_local)
+    _need(out, "out", (B, H, Lc, d), k.dtype, dev)
+    if lse is None and return_lse:
+        lse = torch.empty((B, H, Lc), dtype=torch.float32, device=dev)
+    if lse is not None:
+        _need(lse, "lse", (B, H, Lc), torch.float32, dev)
+    need = forward_rank_workspace_bytes(B, H, L, d, N)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    st = load().rsa_forward_rank(_ptr(q_local), _ptr(k), _ptr(v), _ptr(m), B, H, L, d, int(N), int(rank),
+                                 code, _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                 _stream(dev), _ptr(out), _ptr(lse))
+    if st != 0:
+        raise RSAError(st, "rsa_forward_rank")
+    return (out, lse) if (return_lse or lse is not None) else out
+
+
+def backward_workspace_bytes(B: int, H: int, L: int, d: int, N: int, dtype: int = RSA_BF16) -> int:
+    return int(load().rsa_backward_workspace_bytes(B, H, L, d, N, dtype))
+
+
+def backward(q, k, v, out, dout, lse, key_mask=None, N: int = 1, dq=None, dk=None, dv=None, workspace=None):
+    """Gradients (dq, dk, dv) of <out, dout>; out and lse come from forward()."""
+    B, H, L, d = q.shape
+    dev = q.device
+    for name, t in (("q", q), ("k", k), ("v", v), ("out", out), ("dout", dout)):
+        _need(t, name, (B, H, L, d), q.dtype, dev)
+    _need(lse, "lse", (B, H, L), torch.float32, dev)
+    m = _mask(key_mask, B, L, dev)
+    code = _dtype_code(q)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(q) if dk is None else dk
+    dv = torch.empty_like(q) if dv is None else dv
+    for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+        _need(t, name, (B, H, L, d), q.dtype, dev)
+    need = backward_workspace_bytes(B, H, L, d, N, code)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    st = load().rsa_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(lse), _ptr(m),
+                             B, H, L, d, int(N), code, _ptr(workspace),
+                             workspace.numel() * workspace.element_size(), _stream(dev),
+                             _ptr(dq), _ptr(dk), _ptr(dv))
+    if st != 0:
+        raise RSAError(st, "rsa_backward")
+    return dq, dk, dv

@@ -1,0 +1,89 @@
+// rsa_device.h -- device-side building blocks shared by the RSA kernels
+// (gfx950 / CDNA4: 64-lane wavefronts, MFMA matrix cores, LDS).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace rsa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+constexpr int kXcds = 8;          // MI355X: 8 accelerator complex dies, one L2 each
+constexpr float kLn2 = 0.69314718055994530942f;
+
+// ---------------------------------------------------------------- MFMA ---
+// 32x32 accumulator layout (all 32x32 MFMA shapes): lane l holds column
+// n = l % 32; register r holds row m = 8*(r/4) + 4*(l/32) + (r%4).
+// Operand layout: A lane l holds row m = l % 32, B lane l holds column
+// n = l % 32; the contraction index is spread over (l / 32, register) in the
+// same way for A and B, so any data placed consistently in both contracts
+// correctly.
+__device__ __forceinline__ f32x16 mfma_32x32x16_bf16(u32x4 a, u32x4 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x16 mfma_32x32x2_f32(float a, float b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+}
+
+// Row index held by accumulator register r of a lane in half h = lane / 32.
+__device__ __forceinline__ constexpr int acc_row(int r, int h) { return 8 * (r >> 2) + 4 * h + (r & 3); }
+
+// ----------------------------------------------------------- bf16 packs ---
+// Two fp32 values to one dword of two bf16 (round to nearest even).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    bf16x2 v;
+    v[0] = (__bf16)lo;
+    v[1] = (__bf16)hi;
+    return __builtin_bit_cast(uint32_t, v);
+}
+
+// acc + lo + hi of a dword of two bf16, in fp32 (one dot2 instruction).
+__device__ __forceinline__ float add_bf16x2(uint32_t w, float acc) {
+    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), ones, acc, false);
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// ------------------------------------------------------------ ring math ---
+// Sequence position of the v-th key that rank n visits: ring step t = v / Lc
+// brings chunk c = (n - t) mod N, whose keys are visited in ascending order.
+__device__ __forceinline__ int ring_pos(int v, int n, int N, int Lc) {
+    const int t = v / Lc;
+    int c = n - t;
+    c += (c < 0) ? N : 0;
+    return c * Lc + (v - t * Lc);
+}
+
+// ------------------------------------------------------------- dispatch ---
+// Workgroups are dealt to the XCDs round-robin by id. Renumber them so that
+// each XCD receives a contiguous range of logical work items: neighbouring
+// items (query tiles of one head) then share that XCD's L2.
+__device__ __forceinline__ int xcd_remap(int id, int n) {
+    const int xcd = id % kXcds, local = id / kXcds;
+    const int per = n / kXcds, rem = n % kXcds;
+    return (xcd < rem) ? xcd * (per + 1) + local : rem * (per + 1) + (xcd - rem) * per + local;
+}
+
+__device__ __forceinline__ bool wave_any(bool p) { return __any(p); }
+
+__device__ __forceinline__ float shfl_xor32(float x) { return __shfl_xor(x, 32); }
+
+// True if some byte of w is zero.
+__device__ __forceinline__ bool has_zero_byte(uint32_t w) {
+    return ((w - 0x01010101u) & ~w & 0x80808080u) != 0;
+}
+
+}  // namespace rsa

@@ -1,0 +1,58 @@
+// rsa_internal.h -- host-side launch interface between the C ABI and the
+// kernels. Not installed; the public interface is include/rsa.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace rsa {
+
+// Keys per tile of the forward kernels, and the most tiles one workgroup's
+// key range may hold (the tile-occupancy table lives in LDS).
+constexpr int kFwdKeyTile = 64;
+constexpr int kFwdMaxTiles = 4096;
+
+struct ForwardCall {
+    const void* q;          // [B,H,Lq,d]
+    const void* k;          // [B,H,L,d]
+    const void* v;          // [B,H,L,d]
+    const uint8_t* mask;    // [B,L] or nullptr
+    void* out;              // [B,H,Lq,d]
+    float* lse;             // [B,H,Lq] or nullptr
+    float* part;            // split partials (groups > 1), see forward_workspace_bytes
+    int B, H, L, d, N;
+    int Lq;                 // query rows per head held by q / out
+    int q_pos0;             // sequence position of q's row 0
+    int groups;             // ring-step groups computed in parallel (1 = no split)
+    bool bf16;
+};
+
+// Bytes of split partials for `groups` ring-step groups.
+size_t forward_partial_bytes(int B, int H, int Lq, int d, int groups);
+
+// Ring-step groups the one-rank-share path uses for these sizes.
+int forward_rank_groups(int B, int H, int L, int d, int N);
+
+hipError_t launch_forward(const ForwardCall& c, hipStream_t stream);
+
+struct BackwardCall {
+    const void* q;
+    const void* k;
+    const void* v;
+    const void* out;
+    const void* dout;
+    const float* lse;
+    const uint8_t* mask;
+    float* delta;           // workspace [B,H,L] fp32
+    void* dq;
+    void* dk;
+    void* dv;
+    int B, H, L, d, N;
+};
+
+size_t backward_workspace_bytes(int B, int H, int L, int d);
+
+hipError_t launch_backward(const BackwardCall& c, hipStream_t stream);
+
+}  // namespace rsa

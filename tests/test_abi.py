@@ -1,0 +1,104 @@
+"""The C ABI without a GPU: librsa.so loads, exports every function that
+include/rsa.h declares, and rejects bad arguments before any HIP call.
+
+Pointers passed here are fake device addresses: validation only inspects
+their values, so no test below reaches a HIP call.
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import sequence_transformer_attention_rsa_amd as rsa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "rsa.h")
+
+OK, ENULL, ESHAPE, EUNSUP, EALIGN, EWS = 0, 1, 2, 3, 4, 5
+F32, BF16 = 0, 1
+P = 0x10000   # a 16-byte aligned fake address
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(rsa_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(rsa.lib_path()):
+        pytest.skip("librsa.so not built (run __graft_entry__.build())")
+    return rsa.load()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert names == sorted(rsa.SIGNATURES), names
+    for name in names:
+        assert hasattr(lib, name), name
+
+
+def test_status_strings(lib):
+    for code in range(7):
+        assert rsa.status_string(code).startswith("RSA_")
+    assert "unknown" in rsa.status_string(99)
+
+
+def fwd(lib, q=P, k=P, v=P, mask=None, B=1, H=2, L=256, d=64, N=4, dtype=BF16, out=P, lse=None):
+    return lib.rsa_forward(q, k, v, mask, B, H, L, d, N, dtype, None, out, lse)
+
+
+def test_forward_validation(lib):
+    assert fwd(lib, q=None) == ENULL
+    assert fwd(lib, out=None) == ENULL
+    assert fwd(lib, B=0) == ESHAPE
+    assert fwd(lib, H=-1) == ESHAPE
+    assert fwd(lib, L=255) == ESHAPE            # L % N != 0
+    assert fwd(lib, N=0) == ESHAPE
+    assert fwd(lib, d=32) == EUNSUP
+    assert fwd(lib, d=96) == EUNSUP
+    assert fwd(lib, dtype=7) == EUNSUP
+    assert fwd(lib, L=64 * 4096 * 2, N=1) == EUNSUP   # longer than one launch's tile table
+    assert fwd(lib, q=P + 8) == EALIGN
+    assert fwd(lib, out=P + 4) == EALIGN
+    assert fwd(lib, mask=P + 1) == EALIGN
+    assert fwd(lib, lse=P + 2) == EALIGN
+
+
+def test_forward_rank_validation(lib):
+    ws = lib.rsa_forward_rank_workspace_bytes(1, 16, 32768, 128, 64)
+    assert ws >= 8 * 16 * 512 * 130 * 4   # 8 ring-step groups of fp32 partials
+    assert lib.rsa_forward_rank_workspace_bytes(1, 16, 32767, 128, 64) == 0
+
+    def call(rank=0, ws_ptr=P, ws_bytes=ws, N=64, q=P, dtype=BF16):
+        return lib.rsa_forward_rank(q, P, P, None, 1, 16, 32768, 128, N, rank, dtype,
+                                    ws_ptr, ws_bytes, None, P, None)
+
+    assert call(q=None) == ENULL
+    assert call(rank=-1) == ESHAPE
+    assert call(rank=64) == ESHAPE
+    assert call(N=3) == ESHAPE
+    assert call(ws_ptr=None) == EWS
+    assert call(ws_bytes=ws - 1) == EWS
+    assert call(ws_ptr=P + 8) == EALIGN
+
+
+def test_backward_validation(lib):
+    B, H, L, d, N = 4, 12, 4096, 64, 8
+    ws = lib.rsa_backward_workspace_bytes(B, H, L, d, N, BF16)
+    assert ws >= B * H * L * 4
+
+    def call(dtype=BF16, ws_ptr=P, ws_bytes=ws, lse=P, dq=P, L_=L):
+        return lib.rsa_backward(P, P, P, P, P, lse, None, B, H, L_, d, N, dtype,
+                                ws_ptr, ws_bytes, None, dq, P, P)
+
+    assert call(lse=None) == ENULL
+    assert call(dq=None) == ENULL
+    assert call(L_=4095) == ESHAPE
+    assert call(dtype=F32) == EUNSUP
+    assert call(ws_ptr=None) == EWS
+    assert call(ws_bytes=ws - 4) == EWS
+    assert call(dq=P + 2) == EALIGN

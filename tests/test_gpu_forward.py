@@ -1,0 +1,221 @@
+"""GPU parity of the RSA forward (full sequence and one rank's share)
+against the fp64 oracle, through the C ABI.
+
+Small cases compare every element and span several tiles plus a ragged tail;
+the full-size workloads run in the launch configuration the bench times and
+are checked on sampled query rows, which the oracle computes one by one
+(rows are independent given all keys)."""
+
+import numpy as np
+import pytest
+import torch
+
+import rsa_inputs
+import sequence_transformer_attention_rsa_amd as rsa
+from gates import MAX_ABS, assert_parity
+from gpu_util import device, from_dev, inputs, mask_dev, sample_rows, say, to_dev
+
+pytestmark = pytest.mark.gpu
+
+LSE_TOL = {"f32": 1e-5, "bf16": 2e-3}
+
+
+def divisors(n):
+    return [x for x in range(1, n + 1) if n % x == 0]
+
+
+def gpu_forward(x, dtype, N, dev, return_lse=True):
+    q, k, v = (to_dev(x[n], dtype, dev) for n in ("q", "k", "v"))
+    out, lse = rsa.forward(q, k, v, mask_dev(x["mask"], dev), N=N, return_lse=True)
+    torch.cuda.synchronize()
+    return from_dev(out), lse.cpu().numpy().astype(np.float64)
+
+
+def check_lse(got, want, dtype, what):
+    fin = np.isfinite(want)
+    assert np.array_equal(np.isfinite(got), fin), f"{what}: lse finiteness differs"
+    if fin.any():
+        err = np.abs(got[fin] - want[fin]).max()
+        assert err <= LSE_TOL[dtype], f"{what}: lse max-abs {err:.3e}"
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("L,N,valid", [
+    (256, 4, None),          # four chunks of one 64-key tile each
+    (200, 5, (150, 200)),    # chunks of 40 keys: tiles straddle chunks, ragged tail
+    (320, 8, (1, 320)),      # very short valid lengths possible
+    (130, 13, None),         # chunks of 10 keys, 130 = 2 query tiles + 2 rows
+    (64, 64, None),          # one key per chunk
+])
+def test_forward_small_parity(oracle_lib, dtype, d, L, N, valid):
+    dev = device()
+    x = inputs(2, 3, L, d, seed=L + d + N, dtype=dtype, valid_range=valid)
+    say("forward", dtype, d, L, N, valid)
+    out, lse = gpu_forward(x, dtype, N, dev)
+    want, want_lse = oracle_lib.forward(x["q"], x["k"], x["v"], x["mask"], N=N)
+    assert_parity(out, want, dtype, f"out {dtype} d={d} L={L} N={N}")
+    check_lse(lse, want_lse, dtype, f"lse {dtype} d={d} L={L} N={N}")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_forward_every_ring_size(oracle_lib, dtype):
+    """The result does not depend on N: every divisor of L = 256."""
+    dev = device()
+    L, d = 256, 64
+    x = inputs(1, 2, L, d, seed=77, dtype=dtype, valid_range=(190, 190))
+    want, _ = oracle_lib.forward(x["q"], x["k"], x["v"], x["mask"], N=1)
+    outs = []
+    for N in divisors(L):
+        say("forward ring size", dtype, N)
+        out, _ = gpu_forward(x, dtype, N, dev)
+        assert_parity(out, want, dtype, f"N={N}")
+        outs.append(out)
+    spread = max(np.abs(o - outs[0]).max() for o in outs)
+    assert spread <= MAX_ABS[dtype] / 4
+
+
+def test_fully_masked_rows_give_zeros(oracle_lib):
+    dev = device()
+    L, d = 192, 64
+    x = inputs(2, 2, L, d, seed=5, dtype="bf16")
+    mask = np.ones((2, L), np.uint8)
+    mask[1] = 0
+    x["mask"] = mask
+    say("fully masked batch row")
+    out, lse = gpu_forward(x, "bf16", 3, dev)
+    assert np.all(out[1] == 0.0) and np.all(np.isneginf(lse[1]))
+    want, _ = oracle_lib.forward(x["q"], x["k"], x["v"], mask, N=3)
+    assert_parity(out, want, "bf16", "fully masked")
+
+
+def test_masked_garbage_is_ignored_bitwise():
+    dev = device()
+    L, d = 384, 128
+    x = inputs(2, 2, L, d, seed=6, dtype="bf16", valid_range=(100, 300))
+    say("masked garbage")
+    ref, ref_lse = gpu_forward(x, "bf16", 6, dev)
+    for b, vl in enumerate(x["valid_len"]):
+        x["k"][b, :, vl:] = 1.0e4
+        x["v"][b, :, vl:] = -1.0e4
+    out, lse = gpu_forward(x, "bf16", 6, dev)
+    assert np.array_equal(out, ref) and np.array_equal(lse, ref_lse)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_unit_values_give_unit_output(dtype):
+    """V = 1: each output entry is the sum of the weights actually used.
+    fp32: the MFMA sum and the row sum round differently, at most about
+    2 * 448 * 2^-24 = 5e-5 apart; bf16 adds the output rounding (2^-9)."""
+    dev = device()
+    L, d = 448, 64
+    x = inputs(1, 2, L, d, seed=8, dtype=dtype, scale=2.0, valid_range=(300, 448))
+    x["v"] = np.ones_like(x["v"])
+    say("unit values", dtype)
+    out, _ = gpu_forward(x, dtype, 7, dev)
+    assert np.abs(out - 1.0).max() <= (2e-5 if dtype == "f32" else 4e-3)
+
+
+def test_constant_keys_give_mean_of_values():
+    dev = device()
+    L, d = 320, 64
+    x = inputs(2, 2, L, d, seed=9, dtype="bf16", valid_range=(200, 320))
+    x["k"] = np.broadcast_to(x["k"][:, :, :1, :], x["k"].shape).copy()
+    say("constant keys")
+    out, _ = gpu_forward(x, "bf16", 4, dev)
+    for b, vl in enumerate(x["valid_len"]):
+        mean = x["v"][b, :, :vl].astype(np.float64).mean(axis=1)
+        assert np.abs(out[b] - mean[:, None, :]).max() <= 2e-3
+
+
+def test_large_scores_stress(oracle_lib):
+    """Q scaled by 8: scores span about +-60, stressing the running max."""
+    dev = device()
+    L, d = 512, 64
+    x = inputs(1, 2, L, d, seed=10, dtype="bf16")
+    x["q"] = rsa_inputs.bf16_round(x["q"] * 8.0)
+    say("large scores")
+    out, lse = gpu_forward(x, "bf16", 8, dev)
+    want, want_lse = oracle_lib.forward(x["q"], x["k"], x["v"], None, N=8)
+    assert_parity(out, want, "bf16", "large scores")
+    assert np.abs(lse - want_lse).max() <= 2e-2
+
+
+def test_forward_is_deterministic():
+    dev = device()
+    x = inputs(2, 4, 1024, 64, seed=11, dtype="bf16", valid_range=(700, 1024))
+    say("determinism")
+    a, la = gpu_forward(x, "bf16", 4, dev)
+    b, lb = gpu_forward(x, "bf16", 4, dev)
+    assert np.array_equal(a, b) and np.array_equal(la, lb)
+
+
+# --------------------------------------------------------- named workloads ---
+
+@pytest.mark.parametrize("name", ["fp32_small", "bert_base"])
+def test_workload_full_parity(oracle_lib, name):
+    w = rsa_inputs.WORKLOADS[name]
+    dev = device()
+    x = rsa_inputs.workload_inputs(w)
+    say("workload", name)
+    out, lse = gpu_forward(x, w.dtype, w.N, dev)
+    want, want_lse = oracle_lib.forward(x["q"], x["k"], x["v"], x["mask"], N=w.N)
+    assert_parity(out, want, w.dtype, name)
+    check_lse(lse, want_lse, w.dtype, name)
+
+
+def test_long_sequence_sampled_rows(oracle_lib):
+    """B=2, H=12, L=8192, d=64, N=16: the full launch, checked on 2 heads x
+    ~200 sampled rows (every rank represented)."""
+    w = rsa_inputs.WORKLOADS["long_seq"]
+    dev = device()
+    x = rsa_inputs.workload_inputs(w)
+    say("workload long_seq")
+    out, lse = gpu_forward(x, w.dtype, w.N, dev)
+    for b, h in ((0, 0), (1, 11)):
+        rows = sample_rows(w.L, 192, seed=b * 100 + h)
+        want, want_lse = oracle_lib.forward(x["q"][b:b + 1, h:h + 1, rows], x["k"][b:b + 1, h:h + 1],
+                                            x["v"][b:b + 1, h:h + 1], None, N=w.N, qpos=rows)
+        assert_parity(out[b, h, rows], want[0, 0], "bf16", f"long_seq b={b} h={h}")
+        check_lse(lse[b, h, rows], want_lse[0, 0], "bf16", "long_seq")
+
+
+@pytest.mark.parametrize("rank", [0, 31, 63])
+def test_rank_share_sampled_rows(oracle_lib, rank):
+    """One rank's 512 rows against 32768 keys (H=16, d=128, N=64, key
+    padding): split over ring-step groups and merged; rank 63 starts its ring
+    on a chunk that can be all padding."""
+    w = rsa_inputs.WORKLOADS["rank_share"]
+    dev = device()
+    x = rsa_inputs.make_inputs(w.B, w.H, w.L, w.d, w.seed, w.dtype, w.scale, w.valid_range, Lq=w.Lc)
+    q, k, v = (to_dev(x[n], "bf16", dev) for n in ("q", "k", "v"))
+    say("rank share", rank, "valid", x["valid_len"])
+    out, lse = rsa.forward_rank(q, k, v, mask_dev(x["mask"], dev), N=w.N, rank=rank, return_lse=True)
+    torch.cuda.synchronize()
+    out, lse = from_dev(out), lse.cpu().numpy()
+    base = rank * w.Lc
+    for h in (0, 9):
+        rows = sample_rows(w.Lc, 96, seed=rank * 16 + h)
+        want, want_lse = oracle_lib.forward(x["q"][:, h:h + 1, rows], x["k"][:, h:h + 1],
+                                            x["v"][:, h:h + 1], x["mask"], N=w.N, qpos=base + rows)
+        assert_parity(out[0, h, rows], want[0, 0], "bf16", f"rank {rank} h={h}")
+        check_lse(lse[0, h, rows], want_lse[0, 0], "bf16", f"rank {rank}")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("L,N,d", [(256, 4, 64), (1024, 32, 128), (600, 6, 64), (96, 96, 128)])
+def test_rank_share_matches_oracle_small(oracle_lib, dtype, L, N, d):
+    dev = device()
+    x = inputs(2, 2, L, d, seed=L + N, dtype=dtype, valid_range=(L // 3, L))
+    Lc = L // N
+    k, v = to_dev(x["k"], dtype, dev), to_dev(x["v"], dtype, dev)
+    m = mask_dev(x["mask"], dev)
+    for rank in sorted({0, N // 2, N - 1}):
+        rows = np.arange(rank * Lc, (rank + 1) * Lc)
+        ql = to_dev(x["q"][:, :, rows], dtype, dev)
+        say("rank share small", dtype, L, N, d, rank)
+        out, lse = rsa.forward_rank(ql, k, v, m, N=N, rank=rank, return_lse=True)
+        torch.cuda.synchronize()
+        want, want_lse = oracle_lib.forward(x["q"][:, :, rows], x["k"], x["v"], x["mask"], N=N, qpos=rows)
+        assert_parity(from_dev(out), want, dtype, f"rank {rank}")
+        check_lse(lse.cpu().numpy().astype(np.float64), want_lse, dtype, f"rank {rank}")
