@@ -113,6 +113,29 @@ int rsa_backward(const void* q, const void* k, const void* v, const void* out, c
 /* Workspace bytes rsa_backward needs for these sizes (0 if they are invalid). */
 size_t rsa_backward_workspace_bytes(int B, int H, int L, int d, int N, int dtype);
 
+/*
+ * The three stages rsa_backward runs, for callers that schedule them
+ * separately (on several devices dQ stays with its rank while the dK/dV
+ * contributions travel the ring back to the key chunk's owner; proposed-
+ * method section). Same conventions and validation as rsa_backward.
+ *
+ * Stage 1: delta[b,h,i] = sum_x dout[b,h,i,x] * out[b,h,i,x] (fp32 [B,H,L]).
+ */
+int rsa_backward_preprocess(const void* out, const void* dout, int B, int H, int L, int d, int dtype,
+                            void* stream, float* delta);
+
+/* Stage 2: dq from q, k, v, dout, lse and stage 1's delta (rank n's query
+ * chunk meets the key chunks in ring order). */
+int rsa_backward_dq(const void* q, const void* k, const void* v, const void* dout, const float* lse,
+                    const float* delta, const uint8_t* key_mask, int B, int H, int L, int d, int N, int dtype,
+                    void* stream, void* dq);
+
+/* Stage 3: dk and dv (key chunk c meets query chunk (c + t) mod N at ring
+ * step t; its contributions are summed in that order). */
+int rsa_backward_dkdv(const void* q, const void* k, const void* v, const void* dout, const float* lse,
+                      const float* delta, const uint8_t* key_mask, int B, int H, int L, int d, int N, int dtype,
+                      void* stream, void* dk, void* dv);
+
 /* A static, human-readable name for a status code. */
 const char* rsa_status_string(int status);
 

@@ -25,6 +25,32 @@ int check_sizes(int B, int H, int L, int d, int N, int dtype) {
 
 int launch_status(hipError_t e) { return e == hipSuccess ? RSA_OK : RSA_ERR_HIP; }
 
+int check_backward(int B, int H, int L, int d, int N, int dtype) {
+    int st = check_sizes(B, H, L, d, N, dtype);
+    if (st != RSA_OK) return st;
+    if (dtype != RSA_BF16) return RSA_ERR_UNSUPPORTED;
+    if (L > kMaxL) return RSA_ERR_UNSUPPORTED;
+    return RSA_OK;
+}
+
+rsa::BackwardCall backward_call(const void* q, const void* k, const void* v, const void* out, const void* dout,
+                                const float* lse, const uint8_t* mask, int B, int H, int L, int d, int N) {
+    rsa::BackwardCall c{};
+    c.q = q;
+    c.k = k;
+    c.v = v;
+    c.out = out;
+    c.dout = dout;
+    c.lse = lse;
+    c.mask = mask;
+    c.B = B;
+    c.H = H;
+    c.L = L;
+    c.d = d;
+    c.N = N;
+    return c;
+}
+
 }  // namespace
 
 extern "C" {
@@ -113,33 +139,61 @@ int rsa_backward(const void* q, const void* k, const void* v, const void* out, c
                  void* workspace, size_t workspace_bytes,
                  void* stream, void* dq, void* dk, void* dv) {
     if (!q || !k || !v || !out || !dout || !lse || !dq || !dk || !dv) return RSA_ERR_NULL;
-    int st = check_sizes(B, H, L, d, N, dtype);
+    int st = check_backward(B, H, L, d, N, dtype);
     if (st != RSA_OK) return st;
-    if (dtype != RSA_BF16) return RSA_ERR_UNSUPPORTED;
-    if (L > kMaxL) return RSA_ERR_UNSUPPORTED;
     if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) || !aligned(dout, 16) ||
         !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) || !aligned(key_mask, 16) ||
         !aligned(lse, 4) || !aligned(workspace, 16))
         return RSA_ERR_ALIGN;
     if (!workspace || workspace_bytes < rsa::backward_workspace_bytes(B, H, L, d)) return RSA_ERR_WORKSPACE;
-    rsa::BackwardCall c{};
-    c.q = q;
-    c.k = k;
-    c.v = v;
-    c.out = out;
-    c.dout = dout;
-    c.lse = lse;
-    c.mask = key_mask;
+    rsa::BackwardCall c = backward_call(q, k, v, out, dout, lse, key_mask, B, H, L, d, N);
     c.delta = static_cast<float*>(workspace);
     c.dq = dq;
     c.dk = dk;
     c.dv = dv;
-    c.B = B;
-    c.H = H;
-    c.L = L;
-    c.d = d;
-    c.N = N;
-    return launch_status(rsa::launch_backward(c, static_cast<hipStream_t>(stream)));
+    return launch_status(rsa::launch_backward(c, rsa::kBwdStageAll, static_cast<hipStream_t>(stream)));
+}
+
+int rsa_backward_preprocess(const void* out, const void* dout, int B, int H, int L, int d, int dtype,
+                            void* stream, float* delta) {
+    if (!out || !dout || !delta) return RSA_ERR_NULL;
+    int st = check_backward(B, H, L, d, 1, dtype);
+    if (st != RSA_OK) return st;
+    if (!aligned(out, 16) || !aligned(dout, 16) || !aligned(delta, 4)) return RSA_ERR_ALIGN;
+    rsa::BackwardCall c = backward_call(nullptr, nullptr, nullptr, out, dout, nullptr, nullptr, B, H, L, d, 1);
+    c.delta = delta;
+    return launch_status(rsa::launch_backward(c, rsa::kBwdStagePre, static_cast<hipStream_t>(stream)));
+}
+
+int rsa_backward_dq(const void* q, const void* k, const void* v, const void* dout, const float* lse,
+                    const float* delta, const uint8_t* key_mask, int B, int H, int L, int d, int N, int dtype,
+                    void* stream, void* dq) {
+    if (!q || !k || !v || !dout || !lse || !delta || !dq) return RSA_ERR_NULL;
+    int st = check_backward(B, H, L, d, N, dtype);
+    if (st != RSA_OK) return st;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(dout, 16) || !aligned(dq, 16) ||
+        !aligned(key_mask, 16) || !aligned(lse, 4) || !aligned(delta, 4))
+        return RSA_ERR_ALIGN;
+    rsa::BackwardCall c = backward_call(q, k, v, nullptr, dout, lse, key_mask, B, H, L, d, N);
+    c.delta = const_cast<float*>(delta);
+    c.dq = dq;
+    return launch_status(rsa::launch_backward(c, rsa::kBwdStageDq, static_cast<hipStream_t>(stream)));
+}
+
+int rsa_backward_dkdv(const void* q, const void* k, const void* v, const void* dout, const float* lse,
+                      const float* delta, const uint8_t* key_mask, int B, int H, int L, int d, int N, int dtype,
+                      void* stream, void* dk, void* dv) {
+    if (!q || !k || !v || !dout || !lse || !delta || !dk || !dv) return RSA_ERR_NULL;
+    int st = check_backward(B, H, L, d, N, dtype);
+    if (st != RSA_OK) return st;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(dout, 16) || !aligned(dk, 16) ||
+        !aligned(dv, 16) || !aligned(key_mask, 16) || !aligned(lse, 4) || !aligned(delta, 4))
+        return RSA_ERR_ALIGN;
+    rsa::BackwardCall c = backward_call(q, k, v, nullptr, dout, lse, key_mask, B, H, L, d, N);
+    c.delta = const_cast<float*>(delta);
+    c.dk = dk;
+    c.dv = dv;
+    return launch_status(rsa::launch_backward(c, rsa::kBwdStageDkDv, static_cast<hipStream_t>(stream)));
 }
 
 const char* rsa_status_string(int status) {

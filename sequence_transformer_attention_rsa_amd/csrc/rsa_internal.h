@@ -53,6 +53,12 @@ struct BackwardCall {
 
 size_t backward_workspace_bytes(int B, int H, int L, int d);
 
-hipError_t launch_backward(const BackwardCall& c, hipStream_t stream);
+// Backward stages (bit mask): delta = rowsum(dout o out); dq; dk and dv.
+constexpr int kBwdStagePre = 1;
+constexpr int kBwdStageDq = 2;
+constexpr int kBwdStageDkDv = 4;
+constexpr int kBwdStageAll = kBwdStagePre | kBwdStageDq | kBwdStageDkDv;
+
+hipError_t launch_backward(const BackwardCall& c, int stages, hipStream_t stream);
 
 }  // namespace rsa

@@ -1,0 +1,122 @@
+"""GPU parity of the RSA backward (dQ, dK, dV) against the fp64 oracle,
+through the C ABI. The GPU backward receives the GPU forward's output and
+lse, as a training step would."""
+
+import numpy as np
+import pytest
+import torch
+
+import rsa_inputs
+import sequence_transformer_attention_rsa_amd as rsa
+from gates import assert_parity
+from gpu_util import device, from_dev, inputs, mask_dev, say, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def gpu_fwd_bwd(x, N, dev):
+    q, k, v, g = (to_dev(x[n], "bf16", dev) for n in ("q", "k", "v", "dout"))
+    m = mask_dev(x["mask"], dev)
+    out, lse = rsa.forward(q, k, v, m, N=N, return_lse=True)
+    dq, dk, dv = rsa.backward(q, k, v, out, g, lse, m, N=N)
+    torch.cuda.synchronize()
+    return from_dev(dq), from_dev(dk), from_dev(dv)
+
+
+def check_grads(got, want, what):
+    for name, a, b in zip(("dq", "dk", "dv"), got, want):
+        assert_parity(a, b, "bf16", f"{what} {name}", grad=True)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("L,N,valid", [
+    (256, 4, None),
+    (256, 4, (150, 256)),
+    (200, 5, (120, 200)),    # chunks of 40: tiles straddle chunks, ragged tails
+    (130, 13, (60, 130)),    # chunks of 10, 130 = one 128-row tile + 2 rows
+    (64, 64, None),          # one token per chunk
+    (32, 8, (24, 32)),       # the finite-difference slice's shape
+])
+def test_backward_small_parity(oracle_lib, d, L, N, valid):
+    dev = device()
+    x = inputs(2, 2, L, d, seed=L * 7 + N + d, dtype="bf16", valid_range=valid, with_dout=True)
+    say("backward", d, L, N, valid)
+    got = gpu_fwd_bwd(x, N, dev)
+    want = oracle_lib.backward(x["q"], x["k"], x["v"], x["dout"], x["mask"], N=N)
+    check_grads(got, want, f"d={d} L={L} N={N}")
+    if x["mask"] is not None:
+        for b, vl in enumerate(x["valid_len"]):
+            assert np.all(got[1][b, :, vl:] == 0) and np.all(got[2][b, :, vl:] == 0)
+
+
+def test_backward_every_ring_size(oracle_lib):
+    dev = device()
+    L, d = 256, 64
+    x = inputs(1, 2, L, d, seed=21, dtype="bf16", valid_range=(180, 180), with_dout=True)
+    want = oracle_lib.backward(x["q"], x["k"], x["v"], x["dout"], x["mask"], N=1)
+    for N in (1, 2, 4, 8, 16, 32, 64, 128, 256):
+        say("backward ring size", N)
+        check_grads(gpu_fwd_bwd(x, N, dev), want, f"N={N}")
+
+
+def test_backward_fully_masked_row():
+    dev = device()
+    L, d = 192, 64
+    x = inputs(2, 2, L, d, seed=22, dtype="bf16", with_dout=True)
+    mask = np.ones((2, L), np.uint8)
+    mask[0] = 0
+    x["mask"] = mask
+    say("backward fully masked row")
+    dq, dk, dv = gpu_fwd_bwd(x, 3, dev)
+    assert np.all(dq[0] == 0) and np.all(dk[0] == 0) and np.all(dv[0] == 0)
+    assert np.all(np.isfinite(dq)) and np.all(np.isfinite(dk)) and np.all(np.isfinite(dv))
+
+
+def test_backward_stages_match_and_are_deterministic():
+    dev = device()
+    L, d, N = 512, 64, 8
+    x = inputs(2, 3, L, d, seed=23, dtype="bf16", valid_range=(300, 512), with_dout=True)
+    q, k, v, g = (to_dev(x[n], "bf16", dev) for n in ("q", "k", "v", "dout"))
+    m = mask_dev(x["mask"], dev)
+    say("backward stages")
+    out, lse = rsa.forward(q, k, v, m, N=N, return_lse=True)
+    full = rsa.backward(q, k, v, out, g, lse, m, N=N)
+    again = rsa.backward(q, k, v, out, g, lse, m, N=N)
+    delta = rsa.backward_preprocess(out, g)
+    dq = rsa.backward_dq(q, k, v, g, lse, delta, m, N=N)
+    dk, dv = rsa.backward_dkdv(q, k, v, g, lse, delta, m, N=N)
+    torch.cuda.synchronize()
+    for a, b in zip(full, again):
+        assert torch.equal(a, b)
+    for a, b in zip(full, (dq, dk, dv)):
+        assert torch.equal(a, b)
+    want_delta = (out.float() * g.float()).sum(-1)
+    assert torch.allclose(delta, want_delta, rtol=1e-5, atol=1e-5)
+
+
+def test_backward_invariants():
+    """Key gradients sum to zero over keys; value gradients sum to the sum of dO."""
+    dev = device()
+    L, d = 512, 64
+    x = inputs(1, 2, L, d, seed=24, dtype="bf16", with_dout=True)
+    say("backward invariants")
+    dq, dk, dv = gpu_fwd_bwd(x, 4, dev)
+    scale_k = np.abs(dk).sum(axis=2)
+    assert np.all(np.abs(dk.sum(axis=2)) <= 2e-2 * scale_k + 1e-3)
+    gsum = x["dout"].astype(np.float64).sum(axis=2)
+    assert np.abs(dv.sum(axis=2) - gsum).max() <= 2e-2 * np.abs(gsum).max() + 0.05
+
+
+def test_backward_workload_sampled_heads(oracle_lib):
+    """B=4, H=12, L=4096, d=64, N=8, key padding: the full launch, checked
+    element by element on two heads (the oracle computes each head alone)."""
+    w = rsa_inputs.WORKLOADS["backward"]
+    dev = device()
+    x = rsa_inputs.workload_inputs(w)
+    say("workload backward")
+    dq, dk, dv = gpu_fwd_bwd(x, w.N, dev)
+    for b, h in ((0, 0), (3, 7)):
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        want = oracle_lib.backward(x["q"][sl], x["k"][sl], x["v"][sl], x["dout"][sl],
+                                   x["mask"][b:b + 1], N=w.N)
+        check_grads((dq[sl], dk[sl], dv[sl]), want, f"backward b={b} h={h}")
