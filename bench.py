@@ -1,0 +1,267 @@
+"""Benchmark of the Ring Self-Attention hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload long_seq]
+
+One step is one pass of the whole path over one batch of seeded synthetic
+input already resident in HBM: the forward over all N ranks (rsa_forward,
+writing O and lse) and the backward (rsa_backward_preprocess, rsa_backward_dq,
+rsa_backward_dkdv). Each call launches exactly one kernel, so HIP events
+recorded between the calls on the library's stream (torch's current stream)
+time every kernel separately. Rank-share workloads (--workload rank_share)
+time rsa_forward_rank (split kernel + merge) and have no backward.
+
+Algorithmic work (only what the method must compute, recomputation not
+credited): forward 4*B*H*Lq*Lk*d flops, backward 8*B*H*Lq*Lk*d (the dV, dP,
+dQ and dK contractions), so a step counts 12*B*H*Lq*Lk*d; with a key mask the
+valid-key count replaces Lk. Per kernel: forward 4 (S and PV), dQ kernel 4
+(dP and dQ), dK/dV kernel 4 (dV and dK) times B*H*Lq*Lk*d.
+
+Prints one JSON line. `value` is whole-step TFLOP/s; `roofline` describes
+the kernel with the longest average duration against MI355X's dense bf16
+MFMA peak (2516.6 TFLOP/s); `cpu_baseline` times the fp64 CPU oracle on a
+bounded sample of the same workload (rank 0 only, N=1 only).
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import rsa_inputs  # noqa: E402
+
+METRIC = "RSA attention TFLOP/s (fwd, fwd+bwd) and % of MI355X bf16 MFMA peak"
+PEAK_BF16_TFLOPS = 2516.6     # 256 CUs x 4096 flop/clk/CU x 2.4 GHz, dense
+PEAK_F32_MATRIX_TFLOPS = 157.3
+PEAK_HBM_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="long_seq", choices=sorted(rsa_inputs.WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
+    ap.add_argument("--forward-only", action="store_true", help="time the forward alone")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="also run one plain device copy of this many MiB (counter calibration)")
+    return ap.parse_args()
+
+
+def valid_key_count(w, x):
+    """Sum over (b) of valid keys, times H: the Lk actually attended."""
+    if x["mask"] is None:
+        return w.B * w.L
+    return int(x["valid_len"].sum())
+
+
+def cpu_baseline(w, x, threads):
+    """fp64 oracle, forward (+ backward) on `threads` heads of batch row 0
+    (full sequence length), timed once."""
+    import oracle
+
+    heads = max(1, min(threads, w.H))
+    sl = (slice(0, 1), slice(0, heads))
+    m = None if x["mask"] is None else x["mask"][0:1]
+    q, k, v = x["q"][sl], x["k"][sl], x["v"][sl]
+    vl = w.L if x["mask"] is None else int(x["valid_len"][0])
+    t0 = time.perf_counter()
+    if w.rank is not None:
+        pos = np.arange(w.rank * w.Lc, (w.rank + 1) * w.Lc)
+        oracle.forward(q, k, v, m, N=w.N, qpos=pos)
+        flops = 4.0 * heads * w.Lc * vl * w.d
+        what = "forward"
+    else:
+        oracle.forward(q, k, v, m, N=w.N)
+        flops = 4.0 * heads * w.L * vl * w.d
+        what = "forward"
+        if x.get("dout") is not None:
+            g = x["dout"][sl]
+            oracle.backward(q, k, v, g, m, N=w.N)
+            flops += 8.0 * heads * w.L * vl * w.d
+            what = "forward+backward"
+    dt = time.perf_counter() - t0
+    return {
+        "value": flops / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": oracle.num_threads(),
+        "kind": "oracle",
+        "sample": f"fp64 oracle {what} of {heads} head(s) of batch row 0 at full length "
+                  f"({w.name}: L={w.L}, d={w.d}, N={w.N}); {dt:.1f} s wall",
+        "seconds": dt,
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(this build has no multi-GPU path)", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import sequence_transformer_attention_rsa_amd as rsa
+
+    w = rsa_inputs.WORKLOADS[args.workload]
+    if w.dtype not in ("bf16", "f32"):
+        print(f"workload {w.name} is CPU-only", file=sys.stderr)
+        return 2
+    dev = torch.device("cuda:0")
+    with_dout = w.rank is None
+    x = rsa_inputs.make_inputs(w.B, w.H, w.L, w.d, w.seed, w.dtype, w.scale, w.valid_range,
+                               Lq=w.Lq, with_dout=with_dout)
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+
+    def up(a):
+        return torch.from_numpy(a).to(tdt).to(dev).contiguous()
+
+    q, k, v = up(x["q"]), up(x["k"]), up(x["v"])
+    g = up(x["dout"]) if with_dout else None
+    mask = None if x["mask"] is None else torch.from_numpy(x["mask"]).to(dev)
+    do_bwd = with_dout and w.dtype == "bf16" and not args.forward_only
+
+    out = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+    delta = torch.empty_like(lse)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    ws = None
+    if w.rank is not None:
+        ws = torch.empty(rsa.forward_rank_workspace_bytes(w.B, w.H, w.L, w.d, w.N), dtype=torch.uint8, device=dev)
+
+    names = ["forward"] + (["bwd_preprocess", "bwd_dq", "bwd_dkdv"] if do_bwd else [])
+
+    def step(ev=None):
+        def mark(i):
+            if ev is not None:
+                ev[i].record()
+        mark(0)
+        if w.rank is not None:
+            rsa.forward_rank(q, k, v, mask, N=w.N, rank=w.rank, out=out, lse=lse, workspace=ws)
+        else:
+            rsa.forward(q, k, v, mask, N=w.N, out=out, lse=lse)
+        mark(1)
+        if do_bwd:
+            rsa.backward_preprocess(out, g, delta=delta)
+            mark(2)
+            rsa.backward_dq(q, k, v, g, lse, delta, mask, N=w.N, dq=dq)
+            mark(3)
+            rsa.backward_dkdv(q, k, v, g, lse, delta, mask, N=w.N, dk=dk, dv=dv)
+            mark(4)
+
+    if args.copy_calibration_mib > 0:
+        n = args.copy_calibration_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    nev = len(names) + 1
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(args.steps)]
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    start.record()
+    for s in range(args.steps):
+        step(events[s])
+    stop.record()
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    ms_total = start.elapsed_time(stop)
+    ms_per_step = ms_total / args.steps
+    per_kernel = {}
+    for i, name in enumerate(names):
+        durs = [events[s][i].elapsed_time(events[s][i + 1]) for s in range(args.steps)]
+        per_kernel[name] = {"avg_ms": float(np.mean(durs)), "median_ms": float(np.median(durs)),
+                            "p10_ms": float(np.percentile(durs, 10)), "p90_ms": float(np.percentile(durs, 90))}
+
+    # algorithmic work
+    lk_valid = valid_key_count(w, x)         # sum over batch rows of valid keys
+    unit = w.H * w.Lq * w.d                  # per (batch row, valid key)
+    fwd_flops = 4.0 * unit * lk_valid
+    fwd_flops_nominal = 4.0 * w.B * unit * w.L
+    bwd_flops = 8.0 * unit * lk_valid if do_bwd else 0.0
+    step_flops = fwd_flops + bwd_flops
+    value = step_flops / (ms_per_step * 1e-3) / 1e12
+    peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_MATRIX_TFLOPS
+
+    credited = {"forward": fwd_flops, "bwd_dq": 4.0 * unit * lk_valid, "bwd_dkdv": 4.0 * unit * lk_valid}
+    executed = {"forward": fwd_flops, "bwd_dq": 6.0 * unit * lk_valid, "bwd_dkdv": 8.0 * unit * lk_valid}
+    for name in names:
+        avg_s = per_kernel[name]["avg_ms"] * 1e-3
+        if name in credited:
+            per_kernel[name]["tflops_algorithmic"] = credited[name] / avg_s / 1e12
+            per_kernel[name]["tflops_mfma_executed"] = executed[name] / avg_s / 1e12
+        else:  # preprocess: reads O and dO, writes delta
+            nbytes = 2 * q.numel() * q.element_size() + delta.numel() * 4
+            per_kernel[name]["gbs"] = nbytes / avg_s / 1e9
+    dominant = max((n for n in names if n in credited), key=lambda n: per_kernel[n]["avg_ms"])
+    dom_s = per_kernel[dominant]["avg_ms"] * 1e-3
+    achieved = credited[dominant] / dom_s / 1e12
+    roofline = {
+        "kernel": {"forward": "rsa_fwd_kernel" if w.rank is None else "rsa_fwd_kernel + rsa_merge_kernel",
+                   "bwd_dq": "rsa_bwd_dq", "bwd_dkdv": "rsa_bwd_dkdv"}[dominant],
+        "bound": "mfma",
+        "achieved": achieved,
+        "peak": peak,
+        "unit": "TFLOP/s",
+        "frac": achieved / peak,
+        "traffic": None,
+        "avg_ms": per_kernel[dominant]["avg_ms"],
+        "flops_per_launch": credited[dominant],
+    }
+
+    fwd_s = per_kernel["forward"]["avg_ms"] * 1e-3
+    line = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "L": w.L, "d": w.d, "N": w.N,
+                   "rank": w.rank, "key_mask": w.valid_range is not None,
+                   "pass": "fwd+bwd" if do_bwd else "fwd", "description": w.description},
+        "fwd_tflops": fwd_flops / fwd_s / 1e12,
+        "fwd_tflops_nominal_keys": fwd_flops_nominal / fwd_s / 1e12,
+        "fwd_frac_peak": fwd_flops / fwd_s / 1e12 / peak,
+        "bwd_tflops": (bwd_flops / (sum(per_kernel[n]["avg_ms"] for n in names[1:]) * 1e-3) / 1e12
+                       if do_bwd else None),
+        "step_frac_peak": value / peak,
+        "kernels": per_kernel,
+        "roofline": roofline,
+        "wall_s_timed_region": t_wall,
+        "gpu": torch.cuda.get_device_name(dev),
+    }
+    if not args.no_cpu_baseline:
+        threads = len(os.sched_getaffinity(0))
+        os.environ.setdefault("OMP_NUM_THREADS", str(min(threads, 16)))
+        line["cpu_baseline"] = cpu_baseline(w, x, int(os.environ["OMP_NUM_THREADS"]))
+    else:
+        line["cpu_baseline"] = None
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
