@@ -9,14 +9,18 @@
 // an online softmax, so a rank's share needs O(rows * d) working memory
 // instead of O(rows * L).
 //
-// Kernel shape (one workgroup = 4 waves = 128 query rows of one head):
+// Kernel shape (bf16; one workgroup = 4 waves = 128 query rows of one head):
 //   * each wave owns 32 query rows; its Q fragment stays in registers;
-//   * keys stream through LDS in tiles of 64, double-buffered: K row-major,
-//     V transposed (bf16) so both contractions read 16-byte fragments;
-//   * S^T = K Q^T on the 32x32x16 bf16 MFMA (fp32 inputs: 32x32x2 fp32).
-//     In the 32x32 accumulator layout a lane owns one query column, so the
-//     row max and row sum are in-lane plus one exchange between wave halves,
-//     and the accumulator is the B operand of O^T = V^T P^T unchanged;
+//   * keys stream through LDS in tiles of 64, three buffers deep, copied
+//     straight from HBM by global_load_lds (no registers, no VALU) into an
+//     XOR-swizzled row-major layout; V^T fragments come from the transposing
+//     LDS read, so no transpose is ever stored;
+//   * S^T = K Q^T on the 32x32x16 bf16 MFMA. In the 32x32 accumulator layout
+//     a lane owns one query column, so the row max and row sum are in-lane
+//     plus one exchange between wave halves, and the accumulator is the B
+//     operand of O^T = V^T P^T unchanged;
+//   * software pipelining: the score MFMAs of tile t+1 run next to the
+//     softmax VALU work of tile t;
 //   * online softmax in base 2 (scale and log2(e) folded into one FMA), with
 //     a lazy rescale: the running base only moves when a tile's maximum
 //     exceeds it by more than 8 (weights stay <= 2^8), which is exact after
@@ -28,11 +32,14 @@
 //   * in split mode (one rank's share), each workgroup covers a contiguous
 //     group of ring steps and writes unnormalised partials that a merge
 //     kernel combines exactly.
+// fp32 inputs use a simpler kernel of the same structure on the 32x32x2
+// fp32 MFMA.
 
 #include <type_traits>
 
 #include "rsa_device.h"
 #include "rsa_internal.h"
+#include "rsa_tiles.h"
 
 namespace rsa {
 namespace {
@@ -56,170 +63,24 @@ struct FwdParams {
     int contiguous;   // Lc % kKT == 0: a tile never straddles two chunks
 };
 
-template <bool BF16, int D>
-struct Cfg {
-    using E = typename std::conditional<BF16, uint16_t, float>::type;
-    // LDS: K row-major [kKT][KP]; V transposed [D][VP] (bf16) or row-major [kKT][D] (fp32)
-    static constexpr int KP = BF16 ? D + 8 : D + 1;
-    static constexpr int VP = BF16 ? kKT + 8 : D;
+// fp32 forward (fp32 inputs and output): the same ring-ordered online
+// softmax on the 32x32x2 fp32 MFMA. K is staged row-major with pitch d+1
+// (a lane reads one element of its own key row: conflict-free), V row-major
+// (a lane reads one element of its own d column).
+template <int D>
+struct F32Cfg {
+    static constexpr int KP = D + 1;
     static constexpr int K_ELEMS = kKT * KP;
-    static constexpr int V_ELEMS = BF16 ? D * VP : kKT * D;
+    static constexpr int V_ELEMS = kKT * D;
     static constexpr int BUF = K_ELEMS + V_ELEMS;
-    // staging per thread: 16-byte K chunks; V units (bf16: one d pair x 8 keys)
-    static constexpr int K_CHUNKS = BF16 ? (kKT * D / 8) / kThreads : (kKT * D / 4) / kThreads;
-    static constexpr int V_UNITS = BF16 ? (D / 2 * (kKT / 8)) / kThreads : K_CHUNKS;
-    static constexpr int QF = BF16 ? D / 16 : D / 2;   // Q fragments per lane (k-steps of S^T)
-    static constexpr int DB = D / 32;                  // 32-row blocks of O^T
-    static_assert(K_CHUNKS * kThreads * (BF16 ? 8 : 4) == kKT * D, "K staging");
-    static_assert(!BF16 || V_UNITS * kThreads * 16 == kKT * D, "V staging");
+    static constexpr int CH = (kKT * D / 4) / kThreads;   // 16-byte chunks per thread and tensor
+    static_assert(CH * kThreads * 4 == kKT * D, "fp32 staging");
 };
 
-template <bool BF16, int D>
-struct Stage {
-    u32x4 k[Cfg<BF16, D>::K_CHUNKS];
-    uint32_t vb[BF16 ? Cfg<BF16, D>::V_UNITS : 1][8];      // bf16: 8 keys x (2 d) per unit
-    u32x4 vf[BF16 ? 1 : Cfg<BF16, D>::K_CHUNKS];           // fp32: 16-byte chunks
-};
-
-// Global -> registers for the tile starting at virtual key v0.
-template <bool BF16, int D>
-__device__ __forceinline__ void load_tile(const FwdParams& p, const typename Cfg<BF16, D>::E* kh,
-                                          const typename Cfg<BF16, D>::E* vh, int n, int v0, int vend,
-                                          Stage<BF16, D>& st) {
-    using C = Cfg<BF16, D>;
-    const int tid = threadIdx.x;
-    const int pos0 = p.contiguous ? ring_pos(v0, n, p.N, p.Lc) : 0;
-    constexpr int EPC = BF16 ? 8 : 4;   // elements per 16-byte chunk
-#pragma unroll
-    for (int i = 0; i < C::K_CHUNKS; ++i) {
-        const int c = tid + i * kThreads;
-        const int row = c / (D / EPC), col = c % (D / EPC);
-        const int vk = v0 + row;
-        u32x4 x = {0u, 0u, 0u, 0u};
-        if (vk < vend) {
-            const int pos = p.contiguous ? pos0 + row : ring_pos(vk, n, p.N, p.Lc);
-            x = *reinterpret_cast<const u32x4*>(kh + (size_t)pos * D + col * EPC);
-        }
-        st.k[i] = x;
-    }
-    if constexpr (BF16) {
-#pragma unroll
-        for (int i = 0; i < C::V_UNITS; ++i) {
-            const int u = tid + i * kThreads;
-            const int dp = u % (D / 2), kg = u / (D / 2);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int vk = v0 + kg * 8 + e;
-                uint32_t x = 0u;
-                if (vk < vend) {
-                    const int pos = p.contiguous ? pos0 + kg * 8 + e : ring_pos(vk, n, p.N, p.Lc);
-                    x = *reinterpret_cast<const uint32_t*>(vh + (size_t)pos * D + 2 * dp);
-                }
-                st.vb[i][e] = x;
-            }
-        }
-    } else {
-#pragma unroll
-        for (int i = 0; i < C::K_CHUNKS; ++i) {
-            const int c = tid + i * kThreads;
-            const int row = c / (D / 4), col = c % (D / 4);
-            const int vk = v0 + row;
-            u32x4 x = {0u, 0u, 0u, 0u};
-            if (vk < vend) {
-                const int pos = p.contiguous ? pos0 + row : ring_pos(vk, n, p.N, p.Lc);
-                x = *reinterpret_cast<const u32x4*>(vh + (size_t)pos * D + col * 4);
-            }
-            st.vf[i] = x;
-        }
-    }
-}
-
-// Position of key x (0..15) of a 16-key group inside the transposed V tile.
-// The S^T accumulator gives lane half h the keys 4h+{0..3} and 8+4h+{0..3}
-// of each 16-key MFMA step; storing them adjacently lets one 16-byte LDS
-// read fetch a lane's whole V^T fragment.
-__device__ __forceinline__ constexpr int vt_slot(int x) { return 8 * ((x >> 2) & 1) + (x & 3) + 4 * (x >> 3); }
-
-// Registers -> LDS buffer.
-template <bool BF16, int D>
-__device__ __forceinline__ void store_tile(typename Cfg<BF16, D>::E* buf, const Stage<BF16, D>& st) {
-    using C = Cfg<BF16, D>;
-    const int tid = threadIdx.x;
-    auto* ks = buf;
-    auto* vs = buf + C::K_ELEMS;
-    if constexpr (BF16) {
-#pragma unroll
-        for (int i = 0; i < C::K_CHUNKS; ++i) {
-            const int c = tid + i * kThreads;
-            const int row = c / (D / 8), col = c % (D / 8);
-            *reinterpret_cast<u32x4*>(ks + row * C::KP + col * 8) = st.k[i];
-        }
-#pragma unroll
-        for (int i = 0; i < C::V_UNITS; ++i) {
-            const int u = tid + i * kThreads;
-            const int dp = u % (D / 2), kg = u / (D / 2);
-            const uint32_t* w = st.vb[i];
-            const int base = 16 * (kg >> 1) + vt_slot(8 * (kg & 1));   // keys kg*8 + 0..3
-            const int base2 = 16 * (kg >> 1) + vt_slot(8 * (kg & 1) + 4);  // keys kg*8 + 4..7
-            const u32x2 lo0 = {(w[0] & 0xffffu) | (w[1] << 16), (w[2] & 0xffffu) | (w[3] << 16)};
-            const u32x2 lo1 = {(w[4] & 0xffffu) | (w[5] << 16), (w[6] & 0xffffu) | (w[7] << 16)};
-            const u32x2 hi0 = {(w[0] >> 16) | (w[1] & 0xffff0000u), (w[2] >> 16) | (w[3] & 0xffff0000u)};
-            const u32x2 hi1 = {(w[4] >> 16) | (w[5] & 0xffff0000u), (w[6] >> 16) | (w[7] & 0xffff0000u)};
-            uint16_t* r0 = vs + (2 * dp) * C::VP;
-            uint16_t* r1 = r0 + C::VP;
-            *reinterpret_cast<u32x2*>(r0 + base) = lo0;
-            *reinterpret_cast<u32x2*>(r0 + base2) = lo1;
-            *reinterpret_cast<u32x2*>(r1 + base) = hi0;
-            *reinterpret_cast<u32x2*>(r1 + base2) = hi1;
-        }
-    } else {
-#pragma unroll
-        for (int i = 0; i < C::K_CHUNKS; ++i) {
-            const int c = tid + i * kThreads;
-            const int row = c / (D / 4), col = c % (D / 4);
-            float* dst = ks + row * C::KP + col * 4;
-            dst[0] = __uint_as_float(st.k[i][0]);
-            dst[1] = __uint_as_float(st.k[i][1]);
-            dst[2] = __uint_as_float(st.k[i][2]);
-            dst[3] = __uint_as_float(st.k[i][3]);
-            *reinterpret_cast<u32x4*>(vs + row * D + col * 4) = st.vf[i];
-        }
-    }
-}
-
-// Occupancy of tile t of the workgroup's key range: bit 0 = some key valid,
-// bit 1 = all kKT keys exist and are valid.
-__device__ __forceinline__ uint8_t tile_flags(const FwdParams& p, const uint8_t* mrow, int n, int v0, int vend) {
-    const int cnt = min(kKT, vend - v0);
-    if (mrow == nullptr) return cnt == kKT ? 3 : 1;
-    bool any = false, all = (cnt == kKT);
-    if (p.contiguous) {
-        const int pos0 = ring_pos(v0, n, p.N, p.Lc);
-        const u32x4* m4 = reinterpret_cast<const u32x4*>(mrow + pos0);
-#pragma unroll
-        for (int i = 0; i < kKT / 16; ++i) {
-            const u32x4 w = m4[i];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                any |= (w[e] != 0u);
-                all &= !has_zero_byte(w[e]);
-            }
-        }
-    } else {
-        for (int i = 0; i < cnt; ++i) {
-            const bool ok = mrow[ring_pos(v0 + i, n, p.N, p.Lc)] != 0;
-            any |= ok;
-            all &= ok;
-        }
-    }
-    return (any ? 1 : 0) | (all ? 2 : 0);
-}
-
-template <bool BF16, int D>
-__global__ __launch_bounds__(kThreads) void rsa_fwd_kernel(FwdParams p) {
-    using C = Cfg<BF16, D>;
-    using E = typename C::E;
-    __shared__ __attribute__((aligned(16))) E smem[2 * C::BUF];
+template <int D>
+__global__ __launch_bounds__(kThreads) void rsa_fwd_f32(FwdParams p) {
+    using C = F32Cfg<D>;
+    __shared__ __attribute__((aligned(16))) float smem[2 * C::BUF];
     __shared__ uint8_t tflag[kFwdMaxTiles];
 
     const int total = p.nqt * p.BH * p.groups;
@@ -242,34 +103,24 @@ __global__ __launch_bounds__(kThreads) void rsa_fwd_kernel(FwdParams p) {
     const int vbeg = step0 * p.Lc, vend = step1 * p.Lc;
     const int ntile = (vend - vbeg + kKT - 1) / kKT;
 
-    const E* qh = static_cast<const E*>(p.q) + (size_t)bh * p.Lq * D;
-    const E* kh = static_cast<const E*>(p.k) + (size_t)bh * p.L * D;
-    const E* vh = static_cast<const E*>(p.v) + (size_t)bh * p.L * D;
+    const float* qh = static_cast<const float*>(p.q) + (size_t)bh * p.Lq * D;
+    const float* kh = static_cast<const float*>(p.k) + (size_t)bh * p.L * D;
+    const float* vh = static_cast<const float*>(p.v) + (size_t)bh * p.L * D;
     const uint8_t* mrow = p.mask ? p.mask + (size_t)b * p.L : nullptr;
     if (ntile > kFwdMaxTiles) return;   // the host never launches such a range
+    const bool contig = p.contiguous != 0;
 
     for (int t = threadIdx.x; t < ntile; t += kThreads)
-        tflag[t] = tile_flags(p, mrow, n, vbeg + t * kKT, vend);
+        tflag[t] = key_tile_flags(mrow, n, p.N, p.Lc, contig, vbeg + t * kKT, vend);
 
-    // Q^T fragments (B operand of S^T = K Q^T): lane (j, h) holds row `row`,
-    // contraction elements 16*ks + 8*h .. +8 (bf16) or 2*ks + h (fp32).
-    u32x4 qf_b[BF16 ? C::QF : 1];
-    float qf_f[BF16 ? 1 : C::QF];
-    if constexpr (BF16) {
+    // Q^T fragments (B operand of S^T = K Q^T): lane (j, h) holds Q[row][2 ks + h]
+    float qf[D / 2];
 #pragma unroll
-        for (int ks = 0; ks < C::QF; ++ks) {
-            u32x4 x = {0u, 0u, 0u, 0u};
-            if (row_ok) x = *reinterpret_cast<const u32x4*>(qh + (size_t)row * D + 16 * ks + 8 * h);
-            qf_b[ks] = x;
-        }
-    } else {
-#pragma unroll
-        for (int ks = 0; ks < C::QF; ++ks) qf_f[ks] = row_ok ? qh[(size_t)row * D + 2 * ks + h] : 0.0f;
-    }
+    for (int ks = 0; ks < D / 2; ++ks) qf[ks] = row_ok ? qh[(size_t)row * D + 2 * ks + h] : 0.0f;
 
-    f32x16 o[C::DB];
+    f32x16 o[D / 32];
 #pragma unroll
-    for (int db = 0; db < C::DB; ++db)
+    for (int db = 0; db < D / 32; ++db)
 #pragma unroll
         for (int r = 0; r < 16; ++r) o[db][r] = 0.0f;
     float m_b = -INFINITY;   // running base, raw score units
@@ -277,60 +128,72 @@ __global__ __launch_bounds__(kThreads) void rsa_fwd_kernel(FwdParams p) {
 
     __syncthreads();   // tile flags visible
 
+    u32x4 kst[C::CH], vst[C::CH];
+    auto load = [&](int t) {
+        const int v0 = vbeg + t * kKT;
+        const int pos0 = contig ? ring_pos(v0, n, p.N, p.Lc) : 0;
+#pragma unroll
+        for (int i = 0; i < C::CH; ++i) {
+            const int c = threadIdx.x + i * kThreads;
+            const int r = c / (D / 4), col = c % (D / 4);
+            const int vk = v0 + r;
+            u32x4 xk = {0u, 0u, 0u, 0u}, xv = {0u, 0u, 0u, 0u};
+            if (vk < vend) {
+                const size_t pos = contig ? pos0 + r : ring_pos(vk, n, p.N, p.Lc);
+                xk = *reinterpret_cast<const u32x4*>(kh + pos * D + 4 * col);
+                xv = *reinterpret_cast<const u32x4*>(vh + pos * D + 4 * col);
+            }
+            kst[i] = xk;
+            vst[i] = xv;
+        }
+    };
+    auto store = [&](float* buf) {
+#pragma unroll
+        for (int i = 0; i < C::CH; ++i) {
+            const int c = threadIdx.x + i * kThreads;
+            const int r = c / (D / 4), col = c % (D / 4);
+            float* dst = buf + r * C::KP + 4 * col;
+            dst[0] = __uint_as_float(kst[i][0]);
+            dst[1] = __uint_as_float(kst[i][1]);
+            dst[2] = __uint_as_float(kst[i][2]);
+            dst[3] = __uint_as_float(kst[i][3]);
+            *reinterpret_cast<u32x4*>(buf + C::K_ELEMS + r * D + 4 * col) = vst[i];
+        }
+    };
+
     int t = 0;
     while (t < ntile && !(tflag[t] & 1)) ++t;
-    Stage<BF16, D> st;
     int buf = 0;
     if (t < ntile) {
-        load_tile<BF16, D>(p, kh, vh, n, vbeg + t * kKT, vend, st);
-        store_tile<BF16, D>(smem, st);
+        load(t);
+        store(smem);
     }
-
     while (t < ntile) {
         int tn = t + 1;
         while (tn < ntile && !(tflag[tn] & 1)) ++tn;
-        if (tn < ntile) load_tile<BF16, D>(p, kh, vh, n, vbeg + tn * kKT, vend, st);
+        if (tn < ntile) load(tn);
         __syncthreads();   // buffer `buf` complete; the other one is free
 
-        const E* ks_ = smem + buf * C::BUF;
-        const E* vs_ = ks_ + C::K_ELEMS;
+        const float* ks_ = smem + buf * C::BUF;
+        const float* vs_ = ks_ + C::K_ELEMS;
         const int v0 = vbeg + t * kKT;
 
-        // ---- scores S^T = K Q^T for 64 keys (two 32-key blocks)
         f32x16 s[2];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) s[kb][r] = 0.0f;
-            if constexpr (BF16) {
 #pragma unroll
-                for (int kq = 0; kq < C::QF; ++kq) {
-                    const u32x4 a = *reinterpret_cast<const u32x4*>(ks_ + (32 * kb + j) * C::KP + 16 * kq + 8 * h);
-                    s[kb] = mfma_32x32x16_bf16(a, qf_b[kq], s[kb]);
-                }
-            } else {
-#pragma unroll
-                for (int kq = 0; kq < C::QF; ++kq) {
-                    const float a = ks_[(32 * kb + j) * C::KP + 2 * kq + h];
-                    s[kb] = mfma_32x32x2_f32(a, qf_f[kq], s[kb]);
-                }
-            }
+            for (int kq = 0; kq < D / 2; ++kq) s[kb] = mfma_32x32x2_f32(ks_[(32 * kb + j) * C::KP + 2 * kq + h], qf[kq], s[kb]);
         }
-
-        // ---- key mask and range tail (only tiles that are not fully valid)
         if (!(tflag[t] & 2)) {
-            const int vk = v0 + lane;
-            bool ok = vk < vend;
-            if (ok && mrow) ok = mrow[p.contiguous ? ring_pos(v0, n, p.N, p.Lc) + lane : ring_pos(vk, n, p.N, p.Lc)] != 0;
-            const uint64_t bits = __ballot(ok);
+            const uint64_t bits = key_tile_bits(mrow, n, p.N, p.Lc, contig, v0, vend);
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
                 for (int r = 0; r < 16; ++r)
                     if (!((bits >> (32 * kb + acc_row(r, h))) & 1ull)) s[kb][r] = -INFINITY;
         }
-
-        // ---- online softmax (base 2, lazy rescale)
         float mx = s[0][0];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
@@ -343,83 +206,49 @@ __global__ __launch_bounds__(kThreads) void rsa_fwd_kernel(FwdParams p) {
             m_b = m_new;
             l *= alpha;
 #pragma unroll
-            for (int db = 0; db < C::DB; ++db)
+            for (int db = 0; db < D / 32; ++db)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
         }
         const float nb = -m_b * p.sl2;
-
-        if constexpr (BF16) {
-            uint32_t pk[2][8];   // P^T as bf16 pairs, same register order as s
+        // O^T += V^T P^T: one MFMA per accumulator register; step r contracts
+        // key acc_row(r, h) of lane half h
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    const float p0 = fast_exp2(fmaf(s[kb][2 * i], p.sl2, nb));
-                    const float p1 = fast_exp2(fmaf(s[kb][2 * i + 1], p.sl2, nb));
-                    pk[kb][i] = pack_bf16x2(p0, p1);
-                    l = add_bf16x2(pk[kb][i], l);
-                }
-            // ---- O^T += V^T P^T, four 16-key steps
+            for (int r = 0; r < 16; ++r) {
+                const float pr = fast_exp2(fmaf(s[kb][r], p.sl2, nb));
+                l += pr;
+                const int key = 32 * kb + acc_row(r, h);
 #pragma unroll
-            for (int stp = 0; stp < 4; ++stp) {
-                const int kb = stp >> 1, half = stp & 1;
-                const u32x4 bfrag = {pk[kb][4 * half], pk[kb][4 * half + 1], pk[kb][4 * half + 2], pk[kb][4 * half + 3]};
-#pragma unroll
-                for (int db = 0; db < C::DB; ++db) {
-                    const u32x4 a = *reinterpret_cast<const u32x4*>(vs_ + (32 * db + j) * C::VP + 16 * stp + 8 * h);
-                    o[db] = mfma_32x32x16_bf16(a, bfrag, o[db]);
-                }
+                for (int db = 0; db < D / 32; ++db) o[db] = mfma_32x32x2_f32(vs_[key * D + 32 * db + j], pr, o[db]);
             }
-        } else {
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const float pr = fast_exp2(fmaf(s[kb][r], p.sl2, nb));
-                    l += pr;
-                    const int key = 32 * kb + acc_row(r, h);
-#pragma unroll
-                    for (int db = 0; db < C::DB; ++db)
-                        o[db] = mfma_32x32x2_f32(vs_[key * D + 32 * db + j], pr, o[db]);
-                }
-        }
 
-        if (tn < ntile) store_tile<BF16, D>(smem + (buf ^ 1) * C::BUF, st);
+        if (tn < ntile) store(smem + (buf ^ 1) * C::BUF);
         buf ^= 1;
         t = tn;
     }
 
-    // ---- epilogue
     const float l_row = l + shfl_xor32(l);
+    if (!row_ok) return;
     if (p.groups == 1) {
         const float inv = l_row > 0.0f ? 1.0f / l_row : 0.0f;
-        if (row_ok) {
-            E* orow = static_cast<E*>(p.out) + ((size_t)bh * p.Lq + row) * D;
+        float* orow = static_cast<float*>(p.out) + ((size_t)bh * p.Lq + row) * D;
 #pragma unroll
-            for (int db = 0; db < C::DB; ++db)
+        for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-                for (int r4 = 0; r4 < 4; ++r4) {
-                    const int dcol = 32 * db + 8 * r4 + 4 * h;
-                    const float a0 = o[db][4 * r4] * inv, a1 = o[db][4 * r4 + 1] * inv;
-                    const float a2 = o[db][4 * r4 + 2] * inv, a3 = o[db][4 * r4 + 3] * inv;
-                    if constexpr (BF16) {
-                        const u32x2 w = {pack_bf16x2(a0, a1), pack_bf16x2(a2, a3)};
-                        *reinterpret_cast<u32x2*>(orow + dcol) = w;
-                    } else {
-                        const f32x4 w = {a0, a1, a2, a3};
-                        *reinterpret_cast<f32x4*>(orow + dcol) = w;
-                    }
-                }
-            if (p.lse && h == 0)
-                p.lse[(size_t)bh * p.Lq + row] =
-                    l_row > 0.0f ? (m_b * p.sl2 + __log2f(l_row)) * kLn2 : -INFINITY;
-        }
-    } else if (row_ok) {
+            for (int r4 = 0; r4 < 4; ++r4) {
+                const f32x4 w = {o[db][4 * r4] * inv, o[db][4 * r4 + 1] * inv, o[db][4 * r4 + 2] * inv,
+                                 o[db][4 * r4 + 3] * inv};
+                *reinterpret_cast<f32x4*>(orow + 32 * db + 8 * r4 + 4 * h) = w;
+            }
+        if (p.lse && h == 0)
+            p.lse[(size_t)bh * p.Lq + row] = l_row > 0.0f ? (m_b * p.sl2 + __log2f(l_row)) * kLn2 : -INFINITY;
+    } else {
         const size_t prow = ((size_t)g * p.BH + bh) * p.Lq + row;
         float* po = p.part_o + prow * D;
 #pragma unroll
-        for (int db = 0; db < C::DB; ++db)
+        for (int db = 0; db < D / 32; ++db)
 #pragma unroll
             for (int r4 = 0; r4 < 4; ++r4) {
                 const f32x4 w = {o[db][4 * r4], o[db][4 * r4 + 1], o[db][4 * r4 + 2], o[db][4 * r4 + 3]};
@@ -432,6 +261,315 @@ __global__ __launch_bounds__(kThreads) void rsa_fwd_kernel(FwdParams p) {
     }
 }
 
+#ifndef RSA_FWD_MIN_WAVES
+#define RSA_FWD_MIN_WAVES 2
+#endif
+
+// bf16 forward. QB 32-row query blocks per wave (4 waves per workgroup).
+// CONTIG: chunks are whole 64-key tiles (Lc % 64 == 0), so every tile is
+// one aligned, complete run of keys and needs no per-row bounds or ring
+// arithmetic.
+//
+// Tiles reach LDS by direct copies from HBM (no registers, no VALU), three
+// buffers deep: while tile t is consumed, tile t+1 is resident and tile t+2
+// is in flight. Each iteration first reads all of its LDS fragments (K of
+// tile t+1, V^T of tile t through the transposing LDS read), then issues the
+// copy of tile t+2, then runs the softmax of tile t on the VALU next to the
+// score MFMAs of tile t+1 (one branch-free block, so they interleave), then
+// the PV MFMAs of tile t. One barrier per tile.
+template <int D, bool CONTIG, int QB>
+__global__ __launch_bounds__(kThreads, (QB == 1 && D == 64) ? RSA_FWD_MIN_WAVES : 1) void rsa_fwd_bf16(FwdParams p) {
+    using KTile = DirectTile<D, 0>;
+    using VTile = DirectTile<D, 1>;
+    constexpr int NBUF = 3;
+    constexpr int BUF = KTile::BYTES + VTile::BYTES;
+    constexpr int ROWS = 4 * 32 * QB;   // query rows per workgroup
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[NBUF * BUF];
+    __shared__ uint8_t tflag[kFwdMaxTiles];
+
+    const int total = p.nqt * p.BH * p.groups;
+    const int lid = xcd_remap(blockIdx.x, total);
+    const int qt = lid % p.nqt;
+    const int rest = lid / p.nqt;
+    const int g = rest % p.groups;
+    const int bh = rest / p.groups;
+    const int b = bh / p.H;
+
+    const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+    const int j = lane & 31, h = lane >> 5;
+    const int row0 = qt * ROWS;
+    const int wrow0 = row0 + wave * 32 * QB;   // first row of this wave
+    const int n = (p.q_pos0 + row0) / p.Lc;   // ring rank of the tile's first row
+
+    const int step0 = g * p.spg;
+    const int step1 = min(p.N, step0 + p.spg);
+    const int vbeg = step0 * p.Lc, vend = step1 * p.Lc;
+    const int ntile = (vend - vbeg + kKT - 1) / kKT;
+
+    const uint16_t* qh = static_cast<const uint16_t*>(p.q) + (size_t)bh * p.Lq * D;
+    const uint16_t* kh = static_cast<const uint16_t*>(p.k) + (size_t)bh * p.L * D;
+    const uint16_t* vh = static_cast<const uint16_t*>(p.v) + (size_t)bh * p.L * D;
+    const uint8_t* mrow = p.mask ? p.mask + (size_t)b * p.L : nullptr;
+    if (ntile > kFwdMaxTiles) return;   // the host never launches such a range
+
+    for (int t = threadIdx.x; t < ntile; t += kThreads)
+        tflag[t] = key_tile_flags(mrow, n, p.N, p.Lc, CONTIG, vbeg + t * kKT, vend);
+
+    // Q^T fragments (B operand of S^T = K Q^T): lane (j, h) of block qb holds
+    // row wrow0 + 32*qb + j, elements 16*ks + 8*h .. +8.
+    u32x4 qf[QB][D / 16];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+        const int row = wrow0 + 32 * qb + j;
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks) {
+            u32x4 x = {0u, 0u, 0u, 0u};
+            if (row < p.Lq) x = *reinterpret_cast<const u32x4*>(qh + (size_t)row * D + 16 * ks + 8 * h);
+            qf[qb][ks] = x;
+        }
+    }
+
+    f32x16 o[QB][D / 32];
+    float m_b[QB], l0[QB], l1[QB];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) o[qb][db][r] = 0.0f;
+        m_b[qb] = -INFINITY;
+        l0[qb] = 0.0f;
+        l1[qb] = 0.0f;
+    }
+
+    __syncthreads();   // tile flags visible
+
+    // Copy tile t into buffer bi. Rows outside the key range read the head's
+    // first row instead (finite data; those keys are masked to weight 0).
+    auto load = [&](int t, int bi) {
+        const int v0 = vbeg + t * kKT;
+        uint8_t* kbuf = smem + bi * BUF;
+        uint8_t* vbuf = kbuf + KTile::BYTES;
+        if constexpr (CONTIG) {
+            const int pos0 = ring_pos(v0, n, p.N, p.Lc);
+            const uint16_t* kb0 = kh + (size_t)pos0 * D;
+            const uint16_t* vb0 = vh + (size_t)pos0 * D;
+            KTile::load(kbuf, [&](int r) { return kb0 + r * D; });
+            VTile::load(vbuf, [&](int r) { return vb0 + r * D; });
+        } else {
+            auto row = [&](int r) -> size_t {
+                const int vk = v0 + r;
+                return vk < vend ? (size_t)ring_pos(vk, n, p.N, p.Lc) * D : 0;
+            };
+            KTile::load(kbuf, [&](int r) { return kh + row(r); });
+            VTile::load(vbuf, [&](int r) { return vh + row(r); });
+        }
+    };
+    auto next_tile = [&](int t) {
+        ++t;
+        while (t < ntile && !(tflag[t] & 1)) ++t;
+        return t;
+    };
+    // K fragments (A operand of S^T) of the tile in buffer bi
+    auto kfrags = [&](int bi, u32x4 (&kf)[2][D / 16]) {
+        const uint8_t* kbuf = smem + bi * BUF;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int kq = 0; kq < D / 16; ++kq) kf[kb][kq] = KTile::chunk(kbuf, 32 * kb + j, 2 * kq + h);
+    };
+    // S^T = K Q^T for the 64 keys of a tile
+    auto scores = [&](const u32x4 (&kf)[2][D / 16], f32x16 (&s)[QB][2]) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) s[qb][kb][r] = 0.0f;
+#pragma unroll
+            for (int kq = 0; kq < D / 16; ++kq)
+#pragma unroll
+                for (int qb = 0; qb < QB; ++qb) s[qb][kb] = mfma_32x32x16_bf16(kf[kb][kq], qf[qb][kq], s[qb][kb]);
+        }
+    };
+
+    // One pipelined step on tile t (buffer CB), tile tn (buffer CB+1) and the
+    // copy of tile tnn (into buffer CB+2). Buffer indices are compile-time
+    // constants and the two score arrays swap roles between calls, so the
+    // six-fold unrolled loop below needs no register copies and every LDS
+    // address is a per-lane base plus an immediate.
+    int t = next_tile(-1);
+    int tn = ntile;
+    auto body = [&](auto cb_c, f32x16 (&s_cur)[QB][2], f32x16 (&s_nxt)[QB][2]) -> bool {
+        constexpr int CB = decltype(cb_c)::value;
+        constexpr int NB = (CB + 1) % NBUF, FB = (CB + 2) % NBUF;
+        // ---- every LDS fragment of the iteration, read up front
+        u32x4 kf[2][D / 16];
+        kfrags(NB, kf);
+        u32x4 vf[4][D / 32];
+        {
+            const uint8_t* vbuf = smem + CB * BUF + KTile::BYTES;
+#pragma unroll
+            for (int stp = 0; stp < 4; ++stp)
+#pragma unroll
+                for (int db = 0; db < D / 32; ++db) vf[stp][db] = VTile::tfrag(vbuf, 16 * stp, 32 * db);
+        }
+        // ---- copy of tile t+2 into the free buffer, in flight meanwhile
+        const int tnn = tn < ntile ? next_tile(tn) : ntile;
+        if (tnn < ntile) load(tnn, FB);
+
+        // ---- key mask and range tail of tile t (tiles not fully valid)
+        if (!(tflag[t] & 2)) {
+            const uint64_t bits = key_tile_bits(mrow, n, p.N, p.Lc, CONTIG, vbeg + t * kKT, vend);
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    if (!((bits >> (32 * kb + acc_row(r, h))) & 1ull)) {
+#pragma unroll
+                        for (int qb = 0; qb < QB; ++qb) s_cur[qb][kb][r] = -INFINITY;
+                    }
+        }
+
+        // ---- online softmax of tile t (base 2, lazy rescale)
+        float mx[QB];
+        bool need = false;
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+            float a = fmaxf(s_cur[qb][0][0], s_cur[qb][0][1]);
+#pragma unroll
+            for (int r = 2; r < 16; r += 2)
+                a = __builtin_fmaxf(a, __builtin_fmaxf(s_cur[qb][0][r], s_cur[qb][0][r + 1]));
+#pragma unroll
+            for (int r = 0; r < 16; r += 2)
+                a = __builtin_fmaxf(a, __builtin_fmaxf(s_cur[qb][1][r], s_cur[qb][1][r + 1]));
+            mx[qb] = fmaxf(a, shfl_xor32(a));
+            need |= mx[qb] > m_b[qb] + p.tau_raw;
+        }
+        if (wave_any(need)) {
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb) {
+                const float m_new = fmaxf(m_b[qb], mx[qb]);
+                const float alpha = fast_exp2((m_b[qb] - m_new) * p.sl2);
+                m_b[qb] = m_new;
+                l0[qb] *= alpha;
+                l1[qb] *= alpha;
+#pragma unroll
+                for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) o[qb][db][r] *= alpha;
+            }
+        }
+
+        // ---- scores of tile t+1 (MFMA) next to the exponentials of tile t
+        // (VALU), one branch-free block so the two interleave. After the last
+        // tile the buffer holds stale data and s_nxt is discarded.
+        scores(kf, s_nxt);
+
+        uint32_t pk[QB][2][8];   // P^T as bf16 pairs, same register order as s
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+            const float nbase = -m_b[qb] * p.sl2;
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const float p0 = fast_exp2(fmaf(s_cur[qb][kb][2 * i], p.sl2, nbase));
+                    const float p1 = fast_exp2(fmaf(s_cur[qb][kb][2 * i + 1], p.sl2, nbase));
+                    pk[qb][kb][i] = pack_bf16x2(p0, p1);
+                }
+#pragma unroll
+            for (int i = 0; i < 8; i += 2) {
+                l0[qb] = add_bf16x2(pk[qb][0][i], l0[qb]);
+                l1[qb] = add_bf16x2(pk[qb][0][i + 1], l1[qb]);
+                l0[qb] = add_bf16x2(pk[qb][1][i], l0[qb]);
+                l1[qb] = add_bf16x2(pk[qb][1][i + 1], l1[qb]);
+            }
+        }
+
+        // ---- O^T += V^T P^T for tile t, four 16-key steps
+#pragma unroll
+        for (int stp = 0; stp < 4; ++stp)
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+                for (int qb = 0; qb < QB; ++qb)
+                    o[qb][db] = mfma_32x32x16_bf16(vf[stp][db], acc_frag(pk[qb], stp), o[qb][db]);
+
+        if (tn >= ntile) return true;
+        __builtin_amdgcn_s_waitcnt(0);   // this wave's copies of tile t+2 landed
+        __syncthreads();                 // ... and every wave's
+        t = tn;
+        tn = tnn;
+        return false;
+    };
+
+    if (t < ntile) {
+        tn = next_tile(t);
+        load(t, 0);
+        if (tn < ntile) load(tn, 1);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        f32x16 sA[QB][2], sB[QB][2];
+        {
+            u32x4 kf0[2][D / 16];
+            kfrags(0, kf0);
+            scores(kf0, sA);
+        }
+        using C0 = std::integral_constant<int, 0>;
+        using C1 = std::integral_constant<int, 1>;
+        using C2 = std::integral_constant<int, 2>;
+        while (true) {
+            if (body(C0{}, sA, sB)) break;
+            if (body(C1{}, sB, sA)) break;
+            if (body(C2{}, sA, sB)) break;
+            if (body(C0{}, sB, sA)) break;
+            if (body(C1{}, sA, sB)) break;
+            if (body(C2{}, sB, sA)) break;
+        }
+    }
+
+    // ---- epilogue
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+        const int row = wrow0 + 32 * qb + j;
+        const float lsum = l0[qb] + l1[qb];
+        const float l_row = lsum + shfl_xor32(lsum);
+        if (row >= p.Lq) continue;
+        if (p.groups == 1) {
+            const float inv = l_row > 0.0f ? 1.0f / l_row : 0.0f;
+            uint16_t* orow = static_cast<uint16_t*>(p.out) + ((size_t)bh * p.Lq + row) * D;
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+                for (int r4 = 0; r4 < 4; ++r4) {
+                    const f32x16& a = o[qb][db];
+                    const u32x2 w = {pack_bf16x2(a[4 * r4] * inv, a[4 * r4 + 1] * inv),
+                                     pack_bf16x2(a[4 * r4 + 2] * inv, a[4 * r4 + 3] * inv)};
+                    *reinterpret_cast<u32x2*>(orow + 32 * db + 8 * r4 + 4 * h) = w;
+                }
+            if (p.lse && h == 0)
+                p.lse[(size_t)bh * p.Lq + row] =
+                    l_row > 0.0f ? (m_b[qb] * p.sl2 + __log2f(l_row)) * kLn2 : -INFINITY;
+        } else {
+            const size_t prow = ((size_t)g * p.BH + bh) * p.Lq + row;
+            float* po = p.part_o + prow * D;
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+                for (int r4 = 0; r4 < 4; ++r4) {
+                    const f32x16& a = o[qb][db];
+                    const f32x4 w = {a[4 * r4], a[4 * r4 + 1], a[4 * r4 + 2], a[4 * r4 + 3]};
+                    *reinterpret_cast<f32x4*>(po + 32 * db + 8 * r4 + 4 * h) = w;
+                }
+            if (h == 0) {
+                p.part_ml[2 * prow] = l_row > 0.0f ? m_b[qb] * p.sl2 : -INFINITY;
+                p.part_ml[2 * prow + 1] = l_row;
+            }
+        }
+    }
+}
+
 // Exact merge of ring-step-group partials: with base m_g (log2 units) and
 // row sum l_g per group, M = max_g m_g, w_g = 2^(m_g - M),
 // O = sum_g w_g O_g / sum_g w_g l_g.
@@ -439,7 +577,7 @@ template <bool BF16, int D>
 __global__ __launch_bounds__(kThreads) void rsa_merge_kernel(const float* __restrict__ part_o,
                                                              const float* __restrict__ part_ml, int groups,
                                                              int rows, void* out, float* lse) {
-    using E = typename Cfg<BF16, D>::E;
+    using E = typename std::conditional<BF16, uint16_t, float>::type;
     constexpr int TPR = D / 4;   // threads per row, 4 columns each
     const int tid = blockIdx.x * kThreads + threadIdx.x;
     const int rrow = tid / TPR, c4 = tid % TPR;
@@ -473,8 +611,13 @@ __global__ __launch_bounds__(kThreads) void rsa_merge_kernel(const float* __rest
     if (lse && c4 == 0) lse[rrow] = lsum > 0.0f ? (M + __log2f(lsum)) * kLn2 : -INFINITY;
 }
 
+#ifndef RSA_FWD_QB
+#define RSA_FWD_QB 1
+#endif
+
 template <bool BF16, int D>
 hipError_t launch_t(const ForwardCall& c, hipStream_t stream) {
+    constexpr int QB = BF16 ? RSA_FWD_QB : 1;   // 32-row query blocks per wave
     FwdParams p{};
     p.q = c.q;
     p.k = c.k;
@@ -491,7 +634,7 @@ hipError_t launch_t(const ForwardCall& c, hipStream_t stream) {
     p.BH = c.B * c.H;
     p.groups = c.groups;
     p.spg = (c.N + c.groups - 1) / c.groups;
-    p.nqt = (c.Lq + 4 * kQW - 1) / (4 * kQW);
+    p.nqt = (c.Lq + 4 * kQW * QB - 1) / (4 * kQW * QB);
     const double sl2 = 1.4426950408889634 / __builtin_sqrt((double)D);
     p.sl2 = (float)sl2;
     p.tau_raw = (float)(8.0 / sl2);
@@ -502,7 +645,14 @@ hipError_t launch_t(const ForwardCall& c, hipStream_t stream) {
     }
     const long long total = (long long)p.nqt * p.BH * p.groups;
     if (total <= 0) return hipSuccess;
-    hipLaunchKernelGGL((rsa_fwd_kernel<BF16, D>), dim3((unsigned)total), dim3(kThreads), 0, stream, p);
+    if constexpr (BF16) {
+        if (p.contiguous)
+            hipLaunchKernelGGL((rsa_fwd_bf16<D, true, QB>), dim3((unsigned)total), dim3(kThreads), 0, stream, p);
+        else
+            hipLaunchKernelGGL((rsa_fwd_bf16<D, false, QB>), dim3((unsigned)total), dim3(kThreads), 0, stream, p);
+    } else {
+        hipLaunchKernelGGL((rsa_fwd_f32<D>), dim3((unsigned)total), dim3(kThreads), 0, stream, p);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || c.groups == 1) return e;
     const int rows = p.BH * c.Lq;

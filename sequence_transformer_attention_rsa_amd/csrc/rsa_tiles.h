@@ -155,3 +155,79 @@ __device__ __forceinline__ uint64_t key_tile_bits(const uint8_t* mrow, int n, in
 }
 
 }  // namespace rsa
+
+namespace rsa {
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// [64 rows][D] bf16 tile copied from HBM straight into LDS with
+// global_load_lds (16 bytes per lane, no registers, no VALU): each
+// wave-instruction fills one contiguous 1 KB block, so rows are unpadded and
+// the 16-byte chunk c of row r is stored at r * 2D + 16 * (c ^ swz(r)) bytes;
+// the XOR is chosen through each lane's source address. SW = 0 (K tiles):
+// swz(r) = r & 7, so eight rows read at the same chunk hit eight different
+// bank groups. SW = 1 (V tiles, read with the transposing ds_read_b64_tr_b16):
+// swz(r) = 2(r & 3) + ((r >> 2) & 1), so four consecutive rows read at a pair
+// of chunks hit eight different bank groups.
+template <int D, int SW>
+struct DirectTile {
+    static constexpr int ROW_BYTES = 2 * D;
+    static constexpr int BYTES = kTileRows * ROW_BYTES;
+    static constexpr int CPR = D / 8;                  // 16-byte chunks per row
+    static constexpr int RPI = 1024 / ROW_BYTES;       // rows per wave-instruction
+    static constexpr int IPW = kTileRows / RPI / 4;    // instructions per wave (4 waves)
+
+    __device__ __forceinline__ static constexpr int swz(int r) {
+        return SW == 0 ? (r & 7) : (2 * (r & 3) + ((r >> 2) & 1));
+    }
+
+    // Issue the copies; rowptr(r) must return a readable row for every r
+    // (callers point rows outside the range at any valid row).
+    template <class RowPtr>
+    __device__ __forceinline__ static void load(uint8_t* lds, RowPtr rowptr) {
+        const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+#pragma unroll
+        for (int u = 0; u < IPW; ++u) {
+            const int blk = wave * IPW + u;
+            const int r = blk * RPI + lane / CPR;
+            const int c = (lane % CPR) ^ swz(r);
+            const uint16_t* src = rowptr(r) + 8 * c;
+            __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)src,
+                                             (__attribute__((address_space(3))) void*)(lds + blk * 1024), 16, 0, 0);
+        }
+    }
+
+    // 16-byte chunk c of row r (ds_read_b128).
+    __device__ __forceinline__ static u32x4 chunk(const uint8_t* lds, int r, int c) {
+        return *reinterpret_cast<const u32x4*>(lds + r * ROW_BYTES + 16 * (c ^ swz(r)));
+    }
+
+    // Transposed fragment: the A operand of a 32x32x16 MFMA that contracts
+    // over 16 tile rows starting at `row0`, for 32 columns starting at `col0`.
+    // Lane (column col0 + lane % 32, half h) receives rows
+    // row0 + 4h + {0..3} and row0 + 8 + 4h + {0..3} of its column -- the
+    // register order of a 32x32 accumulator used as the B operand.
+    // ds_read_b64_tr_b16: in each 16-lane group, lane 4*rho + c supplies
+    // elements 4c..4c+3 of row rho of a 4 x 16 block; lane i receives column i.
+    __device__ __forceinline__ static u32x4 tfrag(const uint8_t* lds, int row0, int col0) {
+        const int lane = threadIdx.x % kWave;
+        const int i = lane & 15, ig = (lane >> 4) & 1, h = lane >> 5;
+        const int rho = i >> 2, c4 = i & 3;
+        const int e = col0 + 16 * ig + 4 * c4;          // first element of this lane's 4
+        const int c = e >> 3, half = (e >> 2) & 1;
+        u32x4 f;
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            const int r = row0 + 8 * k + 4 * h + rho;
+            const uint8_t* addr = lds + r * ROW_BYTES + 16 * (c ^ swz(r)) + 8 * half;
+            const s16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)addr);
+            const u32x2 w = __builtin_bit_cast(u32x2, x);
+            f[2 * k] = w[0];
+            f[2 * k + 1] = w[1];
+        }
+        return f;
+    }
+};
+
+}  // namespace rsa
