@@ -132,7 +132,7 @@ def main():
 
     out = torch.empty_like(q)
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
-    delta = torch.empty_like(lse)
+    stats = torch.empty((2,) + tuple(lse.shape), dtype=torch.float32, device=dev)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
     ws = None
     if w.rank is not None:
@@ -151,11 +151,11 @@ def main():
             rsa.forward(q, k, v, mask, N=w.N, out=out, lse=lse)
         mark(1)
         if do_bwd:
-            rsa.backward_preprocess(out, g, delta=delta)
+            rsa.backward_preprocess(out, g, lse, rowstats=stats)
             mark(2)
-            rsa.backward_dq(q, k, v, g, lse, delta, mask, N=w.N, dq=dq)
+            rsa.backward_dq(q, k, v, g, stats, mask, N=w.N, dq=dq)
             mark(3)
-            rsa.backward_dkdv(q, k, v, g, lse, delta, mask, N=w.N, dk=dk, dv=dv)
+            rsa.backward_dkdv(q, k, v, g, stats, mask, N=w.N, dk=dk, dv=dv)
             mark(4)
 
     if args.copy_calibration_mib > 0:
@@ -206,8 +206,8 @@ def main():
         if name in credited:
             per_kernel[name]["tflops_algorithmic"] = credited[name] / avg_s / 1e12
             per_kernel[name]["tflops_mfma_executed"] = executed[name] / avg_s / 1e12
-        else:  # preprocess: reads O and dO, writes delta
-            nbytes = 2 * q.numel() * q.element_size() + delta.numel() * 4
+        else:  # preprocess: reads O, dO and lse, writes the row statistics
+            nbytes = 2 * q.numel() * q.element_size() + lse.numel() * 4 + stats.numel() * 4
             per_kernel[name]["gbs"] = nbytes / avg_s / 1e9
     dominant = max((n for n in names if n in credited), key=lambda n: per_kernel[n]["avg_ms"])
     dom_s = per_kernel[dominant]["avg_ms"] * 1e-3

@@ -100,7 +100,8 @@ size_t rsa_forward_rank_workspace_bytes(int B, int H, int L, int d, int N);
  * key chunk in ring order, and the dK/dV contributions of every query chunk
  * are summed at the key chunk they belong to.
  *   q, k, v, out, dout [B,H,L,d] of dtype (inputs); lse [B,H,L] fp32 (input)
- *   workspace          at least rsa_backward_workspace_bytes()
+ *   workspace          at least rsa_backward_workspace_bytes() (holds the
+ *                      row statistics of stage 1 below)
  *   dq, dk, dv         [B,H,L,d] of dtype (outputs)
  * Only RSA_BF16 is supported (RSA_ERR_UNSUPPORTED for RSA_F32).
  */
@@ -119,21 +120,23 @@ size_t rsa_backward_workspace_bytes(int B, int H, int L, int d, int N, int dtype
  * contributions travel the ring back to the key chunk's owner; proposed-
  * method section). Same conventions and validation as rsa_backward.
  *
- * Stage 1: delta[b,h,i] = sum_x dout[b,h,i,x] * out[b,h,i,x] (fp32 [B,H,L]).
+ * Stage 1: row statistics of the forward, rowstats fp32 [2][B,H,L]:
+ *   rowstats[0][b,h,i] = -sum_x dout[b,h,i,x] * out[b,h,i,x]
+ *   rowstats[1][b,h,i] = -lse[b,h,i] * log2(e)   (-inf where lse = -inf)
  */
-int rsa_backward_preprocess(const void* out, const void* dout, int B, int H, int L, int d, int dtype,
-                            void* stream, float* delta);
+int rsa_backward_preprocess(const void* out, const void* dout, const float* lse, int B, int H, int L, int d,
+                            int dtype, void* stream, float* rowstats);
 
-/* Stage 2: dq from q, k, v, dout, lse and stage 1's delta (rank n's query
+/* Stage 2: dq from q, k, v, dout and stage 1's rowstats (rank n's query
  * chunk meets the key chunks in ring order). */
-int rsa_backward_dq(const void* q, const void* k, const void* v, const void* dout, const float* lse,
-                    const float* delta, const uint8_t* key_mask, int B, int H, int L, int d, int N, int dtype,
+int rsa_backward_dq(const void* q, const void* k, const void* v, const void* dout, const float* rowstats,
+                    const uint8_t* key_mask, int B, int H, int L, int d, int N, int dtype,
                     void* stream, void* dq);
 
 /* Stage 3: dk and dv (key chunk c meets query chunk (c + t) mod N at ring
  * step t; its contributions are summed in that order). */
-int rsa_backward_dkdv(const void* q, const void* k, const void* v, const void* dout, const float* lse,
-                      const float* delta, const uint8_t* key_mask, int B, int H, int L, int d, int N, int dtype,
+int rsa_backward_dkdv(const void* q, const void* k, const void* v, const void* dout, const float* rowstats,
+                      const uint8_t* key_mask, int B, int H, int L, int d, int N, int dtype,
                       void* stream, void* dk, void* dv);
 
 /* A static, human-readable name for a status code. */

@@ -50,9 +50,9 @@ SIGNATURES = {
     "rsa_backward": (_ci, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _ci, _ci, _ci, _ci, _ci, _ci,
                            _vp, _sz, _vp, _vp, _vp, _vp]),
     "rsa_backward_workspace_bytes": (_sz, [_ci, _ci, _ci, _ci, _ci, _ci]),
-    "rsa_backward_preprocess": (_ci, [_vp, _vp, _ci, _ci, _ci, _ci, _ci, _vp, _vp]),
-    "rsa_backward_dq": (_ci, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _ci, _ci, _ci, _ci, _ci, _ci, _vp, _vp]),
-    "rsa_backward_dkdv": (_ci, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _ci, _ci, _ci, _ci, _ci, _ci, _vp, _vp, _vp]),
+    "rsa_backward_preprocess": (_ci, [_vp, _vp, _vp, _ci, _ci, _ci, _ci, _ci, _vp, _vp]),
+    "rsa_backward_dq": (_ci, [_vp, _vp, _vp, _vp, _vp, _vp, _ci, _ci, _ci, _ci, _ci, _ci, _vp, _vp]),
+    "rsa_backward_dkdv": (_ci, [_vp, _vp, _vp, _vp, _vp, _vp, _ci, _ci, _ci, _ci, _ci, _ci, _vp, _vp, _vp]),
     "rsa_status_string": (ctypes.c_char_p, [_ci]),
 }
 
@@ -186,52 +186,53 @@ def backward_workspace_bytes(B: int, H: int, L: int, d: int, N: int, dtype: int 
     return int(load().rsa_backward_workspace_bytes(B, H, L, d, N, dtype))
 
 
-def backward_preprocess(out, dout, delta=None):
-    """Stage 1 of the backward: delta = rowsum(dout * out), fp32 [B,H,L]."""
+def backward_preprocess(out, dout, lse, rowstats=None):
+    """Stage 1 of the backward: row statistics, fp32 [2, B, H, L]
+    (-rowsum(dout * out), -lse * log2(e))."""
     B, H, L, d = out.shape
     dev = out.device
     _need(out, "out", (B, H, L, d), out.dtype, dev)
     _need(dout, "dout", (B, H, L, d), out.dtype, dev)
-    if delta is None:
-        delta = torch.empty((B, H, L), dtype=torch.float32, device=dev)
-    _need(delta, "delta", (B, H, L), torch.float32, dev)
-    st = load().rsa_backward_preprocess(_ptr(out), _ptr(dout), B, H, L, d, _dtype_code(out), _stream(dev),
-                                        _ptr(delta))
+    _need(lse, "lse", (B, H, L), torch.float32, dev)
+    if rowstats is None:
+        rowstats = torch.empty((2, B, H, L), dtype=torch.float32, device=dev)
+    _need(rowstats, "rowstats", (2, B, H, L), torch.float32, dev)
+    st = load().rsa_backward_preprocess(_ptr(out), _ptr(dout), _ptr(lse), B, H, L, d, _dtype_code(out),
+                                        _stream(dev), _ptr(rowstats))
     if st != 0:
         raise RSAError(st, "rsa_backward_preprocess")
-    return delta
+    return rowstats
 
 
-def _stage_args(q, k, v, dout, lse, delta, key_mask):
+def _stage_args(q, k, v, dout, rowstats, key_mask):
     B, H, L, d = q.shape
     dev = q.device
     for name, t in (("q", q), ("k", k), ("v", v), ("dout", dout)):
         _need(t, name, (B, H, L, d), q.dtype, dev)
-    _need(lse, "lse", (B, H, L), torch.float32, dev)
-    _need(delta, "delta", (B, H, L), torch.float32, dev)
+    _need(rowstats, "rowstats", (2, B, H, L), torch.float32, dev)
     return B, H, L, d, dev, _mask(key_mask, B, L, dev)
 
 
-def backward_dq(q, k, v, dout, lse, delta, key_mask=None, N: int = 1, dq=None):
+def backward_dq(q, k, v, dout, rowstats, key_mask=None, N: int = 1, dq=None):
     """Stage 2 of the backward: dq."""
-    B, H, L, d, dev, m = _stage_args(q, k, v, dout, lse, delta, key_mask)
+    B, H, L, d, dev, m = _stage_args(q, k, v, dout, rowstats, key_mask)
     dq = torch.empty_like(q) if dq is None else dq
     _need(dq, "dq", (B, H, L, d), q.dtype, dev)
-    st = load().rsa_backward_dq(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(lse), _ptr(delta), _ptr(m),
+    st = load().rsa_backward_dq(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(rowstats), _ptr(m),
                                 B, H, L, d, int(N), _dtype_code(q), _stream(dev), _ptr(dq))
     if st != 0:
         raise RSAError(st, "rsa_backward_dq")
     return dq
 
 
-def backward_dkdv(q, k, v, dout, lse, delta, key_mask=None, N: int = 1, dk=None, dv=None):
+def backward_dkdv(q, k, v, dout, rowstats, key_mask=None, N: int = 1, dk=None, dv=None):
     """Stage 3 of the backward: dk and dv."""
-    B, H, L, d, dev, m = _stage_args(q, k, v, dout, lse, delta, key_mask)
+    B, H, L, d, dev, m = _stage_args(q, k, v, dout, rowstats, key_mask)
     dk = torch.empty_like(q) if dk is None else dk
     dv = torch.empty_like(q) if dv is None else dv
     _need(dk, "dk", (B, H, L, d), q.dtype, dev)
     _need(dv, "dv", (B, H, L, d), q.dtype, dev)
-    st = load().rsa_backward_dkdv(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(lse), _ptr(delta), _ptr(m),
+    st = load().rsa_backward_dkdv(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(rowstats), _ptr(m),
                                   B, H, L, d, int(N), _dtype_code(q), _stream(dev), _ptr(dk), _ptr(dv))
     if st != 0:
         raise RSAError(st, "rsa_backward_dkdv")

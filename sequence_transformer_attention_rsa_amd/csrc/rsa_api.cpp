@@ -147,50 +147,50 @@ int rsa_backward(const void* q, const void* k, const void* v, const void* out, c
         return RSA_ERR_ALIGN;
     if (!workspace || workspace_bytes < rsa::backward_workspace_bytes(B, H, L, d)) return RSA_ERR_WORKSPACE;
     rsa::BackwardCall c = backward_call(q, k, v, out, dout, lse, key_mask, B, H, L, d, N);
-    c.delta = static_cast<float*>(workspace);
+    c.stats = static_cast<float*>(workspace);
     c.dq = dq;
     c.dk = dk;
     c.dv = dv;
     return launch_status(rsa::launch_backward(c, rsa::kBwdStageAll, static_cast<hipStream_t>(stream)));
 }
 
-int rsa_backward_preprocess(const void* out, const void* dout, int B, int H, int L, int d, int dtype,
-                            void* stream, float* delta) {
-    if (!out || !dout || !delta) return RSA_ERR_NULL;
+int rsa_backward_preprocess(const void* out, const void* dout, const float* lse, int B, int H, int L, int d,
+                            int dtype, void* stream, float* rowstats) {
+    if (!out || !dout || !lse || !rowstats) return RSA_ERR_NULL;
     int st = check_backward(B, H, L, d, 1, dtype);
     if (st != RSA_OK) return st;
-    if (!aligned(out, 16) || !aligned(dout, 16) || !aligned(delta, 4)) return RSA_ERR_ALIGN;
-    rsa::BackwardCall c = backward_call(nullptr, nullptr, nullptr, out, dout, nullptr, nullptr, B, H, L, d, 1);
-    c.delta = delta;
+    if (!aligned(out, 16) || !aligned(dout, 16) || !aligned(lse, 4) || !aligned(rowstats, 4)) return RSA_ERR_ALIGN;
+    rsa::BackwardCall c = backward_call(nullptr, nullptr, nullptr, out, dout, lse, nullptr, B, H, L, d, 1);
+    c.stats = rowstats;
     return launch_status(rsa::launch_backward(c, rsa::kBwdStagePre, static_cast<hipStream_t>(stream)));
 }
 
-int rsa_backward_dq(const void* q, const void* k, const void* v, const void* dout, const float* lse,
-                    const float* delta, const uint8_t* key_mask, int B, int H, int L, int d, int N, int dtype,
+int rsa_backward_dq(const void* q, const void* k, const void* v, const void* dout, const float* rowstats,
+                    const uint8_t* key_mask, int B, int H, int L, int d, int N, int dtype,
                     void* stream, void* dq) {
-    if (!q || !k || !v || !dout || !lse || !delta || !dq) return RSA_ERR_NULL;
+    if (!q || !k || !v || !dout || !rowstats || !dq) return RSA_ERR_NULL;
     int st = check_backward(B, H, L, d, N, dtype);
     if (st != RSA_OK) return st;
     if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(dout, 16) || !aligned(dq, 16) ||
-        !aligned(key_mask, 16) || !aligned(lse, 4) || !aligned(delta, 4))
+        !aligned(key_mask, 16) || !aligned(rowstats, 4))
         return RSA_ERR_ALIGN;
-    rsa::BackwardCall c = backward_call(q, k, v, nullptr, dout, lse, key_mask, B, H, L, d, N);
-    c.delta = const_cast<float*>(delta);
+    rsa::BackwardCall c = backward_call(q, k, v, nullptr, dout, nullptr, key_mask, B, H, L, d, N);
+    c.stats = const_cast<float*>(rowstats);
     c.dq = dq;
     return launch_status(rsa::launch_backward(c, rsa::kBwdStageDq, static_cast<hipStream_t>(stream)));
 }
 
-int rsa_backward_dkdv(const void* q, const void* k, const void* v, const void* dout, const float* lse,
-                      const float* delta, const uint8_t* key_mask, int B, int H, int L, int d, int N, int dtype,
+int rsa_backward_dkdv(const void* q, const void* k, const void* v, const void* dout, const float* rowstats,
+                      const uint8_t* key_mask, int B, int H, int L, int d, int N, int dtype,
                       void* stream, void* dk, void* dv) {
-    if (!q || !k || !v || !dout || !lse || !delta || !dk || !dv) return RSA_ERR_NULL;
+    if (!q || !k || !v || !dout || !rowstats || !dk || !dv) return RSA_ERR_NULL;
     int st = check_backward(B, H, L, d, N, dtype);
     if (st != RSA_OK) return st;
     if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(dout, 16) || !aligned(dk, 16) ||
-        !aligned(dv, 16) || !aligned(key_mask, 16) || !aligned(lse, 4) || !aligned(delta, 4))
+        !aligned(dv, 16) || !aligned(key_mask, 16) || !aligned(rowstats, 4))
         return RSA_ERR_ALIGN;
-    rsa::BackwardCall c = backward_call(q, k, v, nullptr, dout, lse, key_mask, B, H, L, d, N);
-    c.delta = const_cast<float*>(delta);
+    rsa::BackwardCall c = backward_call(q, k, v, nullptr, dout, nullptr, key_mask, B, H, L, d, N);
+    c.stats = const_cast<float*>(rowstats);
     c.dk = dk;
     c.dv = dv;
     return launch_status(rsa::launch_backward(c, rsa::kBwdStageDkDv, static_cast<hipStream_t>(stream)));

@@ -9,18 +9,23 @@
 //   dQ = dS K / sqrt(d),  dK = dS^T Q / sqrt(d),  dV = P^T dO.
 //
 // Three kernels, all deterministic (no atomics):
-//   rsa_bwd_pre   D_i = rowsum(dO o O)                         (HBM-bound)
+//   rsa_bwd_pre   row statistics: -D_i and -lse_i * log2(e)       (HBM-bound)
 //   rsa_bwd_dq    query-stationary: a rank's query tile meets the key chunks
 //                 in ring order (as in the forward) and accumulates dQ;
-//                 recomputes S, P, dP from lse (3 contractions)
+//                 recomputes S, P and dP (3 contractions)
 //   rsa_bwd_dkdv  key-stationary: a key chunk meets every query chunk in the
 //                 order the ring delivers them (query chunk (c + t) mod N at
 //                 step t) and accumulates dK and dV -- the sum over query
 //                 chunks that the ring performs across devices (4
 //                 contractions)
-// Layout tricks as in the forward: every 32x32 accumulator is reused as the
-// B operand of the next contraction; operands contracted over tile rows are
-// staged transposed in LDS.
+//
+// As in the forward, tiles are copied from HBM straight into swizzled LDS
+// (global_load_lds), fragments contracted over tile rows come from the
+// transposing LDS read, every 32x32 accumulator is reused as the B operand of
+// the next contraction, P = exp2(s * log2(e)/sqrt(d) - lse * log2(e)) is one
+// FMA and one exp, and the dP accumulator starts at -D so dS = P * acc.
+
+#include <type_traits>
 
 #include "rsa_device.h"
 #include "rsa_internal.h"
@@ -30,6 +35,7 @@ namespace rsa {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kKT = kTileRows;   // rows per LDS tile
 constexpr float kLog2e = 1.4426950408889634f;
 
 struct BwdParams {
@@ -40,14 +46,13 @@ struct BwdParams {
     const uint16_t* dout;
     const float* lse;
     const uint8_t* mask;
-    float* delta;
+    float* stats;   // [2][B*H*L]: -D, then -lse * log2(e)
     uint16_t* dq;
     uint16_t* dk;
     uint16_t* dv;
     int H, L, N, Lc, BH, nt;   // nt: 128-row tiles per head
     float sl2;                 // log2(e) / sqrt(d)
     float scale;               // 1 / sqrt(d)
-    int contiguous;            // Lc % 64 == 0
 };
 
 // Sequence position of the u-th query row that key chunk c meets: ring step
@@ -59,13 +64,11 @@ __device__ __forceinline__ int ring_pos_rev(int u, int c, int N, int Lc) {
     return n * Lc + (u - t * Lc);
 }
 
-// log2-domain lse, +inf for rows without a valid key so that P = 0 there.
-__device__ __forceinline__ float lse_log2(float lse) { return lse == -INFINITY ? INFINITY : lse * kLog2e; }
-
-// ------------------------------------------------------------ D = rowsum ---
+// --------------------------------------------------------- row statistics ---
 template <int D>
 __global__ __launch_bounds__(kThreads) void rsa_bwd_pre(const uint16_t* __restrict__ o,
-                                                        const uint16_t* __restrict__ dout, float* __restrict__ delta,
+                                                        const uint16_t* __restrict__ dout,
+                                                        const float* __restrict__ lse, float* __restrict__ stats,
                                                         long long rows) {
     constexpr int TPR = D / 8;   // lanes per row, 8 elements each
     const long long t = (long long)blockIdx.x * kThreads + threadIdx.x;
@@ -80,22 +83,32 @@ __global__ __launch_bounds__(kThreads) void rsa_bwd_pre(const uint16_t* __restri
     }
 #pragma unroll
     for (int off = TPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
-    if (row < rows && c == 0) delta[row] = acc;
+    if (row < rows && c == 0) {
+        stats[row] = -acc;
+        const float l = lse[row];
+        stats[rows + row] = l == -INFINITY ? -INFINITY : -l * kLog2e;   // a row without keys gets P = 0
+    }
+}
+
+// Copy one fp32 per row for the 64 rows of a tile (rows r -> src + rowoff(r))
+// into LDS: one global_load_lds of 4 bytes per lane, issued by one wave.
+template <class RowOff>
+__device__ __forceinline__ void load_rowvec(uint8_t* lds, const float* src, RowOff rowoff) {
+    const int lane = threadIdx.x % kWave;
+    __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)(src + rowoff(lane)),
+                                     (__attribute__((address_space(3))) void*)lds, 4, 0, 0);
 }
 
 // ------------------------------------------------------------------ dQ ---
-template <int D>
-struct DqSmem {
-    static constexpr int K_OFF = 0;
-    static constexpr int V_OFF = K_OFF + RowTile<D>::ELEMS;
-    static constexpr int KT_OFF = V_OFF + RowTile<D>::ELEMS;
-    static constexpr int BUF = KT_OFF + TransTile<D>::ELEMS;
-};
-
-template <int D>
-__global__ __launch_bounds__(kThreads) void rsa_bwd_dq(BwdParams p) {
-    using S = DqSmem<D>;
-    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * S::BUF];
+// Query-stationary, mirror of the forward: 4 waves x 32 query rows; per key
+// tile S^T = K Q^T and dP^T = V dO^T (lane <-> query), then
+// dQ^T += K^T dS^T with K^T from the transposing read of the same K tile.
+template <int D, bool CONTIG>
+__global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void rsa_bwd_dq(BwdParams p) {
+    using T = DirectTile<D, 1>;
+    constexpr int NBUF = 3;
+    constexpr int BUF = 2 * T::BYTES;   // K, V
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[NBUF * BUF];
     __shared__ uint8_t tflag[kFwdMaxTiles];
 
     const int lid = xcd_remap(blockIdx.x, p.nt * p.BH);
@@ -106,17 +119,17 @@ __global__ __launch_bounds__(kThreads) void rsa_bwd_dq(BwdParams p) {
     const int row = row0 + wave * 32 + j;
     const bool row_ok = row < p.L;
     const int n = row0 / p.Lc;
-    const int ntile = (p.L + kTileRows - 1) / kTileRows;
+    const int ntile = (p.L + kKT - 1) / kKT;
     if (ntile > kFwdMaxTiles) return;   // the host never launches such a length
 
     const size_t hoff = (size_t)bh * p.L * D;
     const uint16_t* kh = p.k + hoff;
     const uint16_t* vh = p.v + hoff;
     const uint8_t* mrow = p.mask ? p.mask + (size_t)b * p.L : nullptr;
-    const bool contig = p.contiguous != 0;
+    const size_t rows_all = (size_t)p.BH * p.L;
 
     for (int t = threadIdx.x; t < ntile; t += kThreads)
-        tflag[t] = key_tile_flags(mrow, n, p.N, p.Lc, contig, t * kTileRows, p.L);
+        tflag[t] = key_tile_flags(mrow, n, p.N, p.Lc, CONTIG, t * kKT, p.L);
 
     u32x4 qf[D / 16], gf[D / 16];
 #pragma unroll
@@ -129,8 +142,12 @@ __global__ __launch_bounds__(kThreads) void rsa_bwd_dq(BwdParams p) {
         qf[ks] = a;
         gf[ks] = g;
     }
-    const float lse2 = row_ok ? lse_log2(p.lse[(size_t)bh * p.L + row]) : INFINITY;
-    const float Di = row_ok ? p.delta[(size_t)bh * p.L + row] : 0.0f;
+    // tail rows get P = 0 through nl2 = -inf
+    const float nD = row_ok ? p.stats[(size_t)bh * p.L + row] : 0.0f;
+    const float nl2 = row_ok ? p.stats[rows_all + (size_t)bh * p.L + row] : -INFINITY;
+    f32x16 nDv;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) nDv[r] = nD;
 
     f32x16 acc[D / 32];
 #pragma unroll
@@ -140,89 +157,107 @@ __global__ __launch_bounds__(kThreads) void rsa_bwd_dq(BwdParams p) {
 
     __syncthreads();
 
-    RowTile<D> kst, vst;
-    TransTile<D> ktst;
-    auto load = [&](int t) {
-        const int v0 = t * kTileRows;
-        const int pos0 = contig ? ring_pos(v0, n, p.N, p.Lc) : 0;
-        auto kptr = [&](int r) -> const uint16_t* {
-            const int vk = v0 + r;
-            if (vk >= p.L) return nullptr;
-            return kh + (size_t)(contig ? pos0 + r : ring_pos(vk, n, p.N, p.Lc)) * D;
-        };
-        auto vptr = [&](int r) -> const uint16_t* {
-            const int vk = v0 + r;
-            if (vk >= p.L) return nullptr;
-            return vh + (size_t)(contig ? pos0 + r : ring_pos(vk, n, p.N, p.Lc)) * D;
-        };
-        kst.load(kptr);
-        vst.load(vptr);
-        ktst.load(kptr);
-    };
-    auto store = [&](uint16_t* buf) {
-        kst.store(buf + S::K_OFF);
-        vst.store(buf + S::V_OFF);
-        ktst.store(buf + S::KT_OFF);
-    };
-
-    int t = 0;
-    while (t < ntile && !(tflag[t] & 1)) ++t;
-    int buf = 0;
-    if (t < ntile) {
-        load(t);
-        store(smem);
-    }
-    while (t < ntile) {
-        int tn = t + 1;
-        while (tn < ntile && !(tflag[tn] & 1)) ++tn;
-        if (tn < ntile) load(tn);
-        __syncthreads();
-        const uint16_t* base = smem + buf * S::BUF;
-        const uint16_t* ks_ = base + S::K_OFF;
-        const uint16_t* vs_ = base + S::V_OFF;
-        const uint16_t* kts = base + S::KT_OFF;
-
-        f32x16 s[2], dp[2];
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                s[kb][r] = 0.0f;
-                dp[kb][r] = 0.0f;
-            }
-#pragma unroll
-            for (int ks = 0; ks < D / 16; ++ks) {
-                s[kb] = mfma_32x32x16_bf16(RowTile<D>::frag(ks_, 32 * kb + j, 16 * ks + 8 * h), qf[ks], s[kb]);
-                dp[kb] = mfma_32x32x16_bf16(RowTile<D>::frag(vs_, 32 * kb + j, 16 * ks + 8 * h), gf[ks], dp[kb]);
-            }
+    auto load = [&](int t, int bi) {
+        const int v0 = t * kKT;
+        uint8_t* kb = smem + bi * BUF;
+        if constexpr (CONTIG) {
+            const size_t pos0 = (size_t)ring_pos(v0, n, p.N, p.Lc) * D;
+            T::load(kb, [&](int r) { return kh + pos0 + r * D; });
+            T::load(kb + T::BYTES, [&](int r) { return vh + pos0 + r * D; });
+        } else {
+            auto off = [&](int r) -> size_t {
+                const int vk = v0 + r;
+                return vk < p.L ? (size_t)ring_pos(vk, n, p.N, p.Lc) * D : 0;
+            };
+            T::load(kb, [&](int r) { return kh + off(r); });
+            T::load(kb + T::BYTES, [&](int r) { return vh + off(r); });
         }
-        if (!(tflag[t] & 2)) {
-            const uint64_t bits = key_tile_bits(mrow, n, p.N, p.Lc, contig, t * kTileRows, p.L);
+    };
+    auto next_tile = [&](int t) {
+        ++t;
+        while (t < ntile && !(tflag[t] & 1)) ++t;
+        return t;
+    };
+
+    int t = next_tile(-1);
+    int tn = ntile;
+    int tnn_ = ntile;
+    auto body = [&](auto cb_c) -> bool {
+        constexpr int CB = decltype(cb_c)::value;
+        constexpr int FB = (CB + 2) % NBUF;
+        const uint8_t* kb = smem + CB * BUF;
+        const uint8_t* vb = kb + T::BYTES;
+        const int tnn = tn < ntile ? next_tile(tn) : ntile;
+        if (tnn < ntile) load(tnn, FB);
+        tnn_ = tnn;
+        const uint64_t bits = (tflag[t] & 2) ? ~0ull : key_tile_bits(mrow, n, p.N, p.Lc, CONTIG, t * kKT, p.L);
+        // two 32-key halves in turn, to bound the live registers
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
+        for (int kb2 = 0; kb2 < 2; ++kb2) {
+            // ---- S^T = K Q^T and dP^T - D = V dO^T - D for keys 32 kb2 .. +32
+            f32x16 s, dp;
+            {
+                u32x4 kfr[D / 16], vfr[D / 16];
+#pragma unroll
+                for (int ks = 0; ks < D / 16; ++ks) {
+                    kfr[ks] = T::chunk(kb, 32 * kb2 + j, 2 * ks + h);
+                    vfr[ks] = T::chunk(vb, 32 * kb2 + j, 2 * ks + h);
+                }
+#pragma unroll
+                for (int r = 0; r < 16; ++r) s[r] = 0.0f;
+                dp = nDv;
+#pragma unroll
+                for (int ks = 0; ks < D / 16; ++ks) {
+                    s = mfma_32x32x16_bf16(kfr[ks], qf[ks], s);
+                    dp = mfma_32x32x16_bf16(vfr[ks], gf[ks], dp);
+                }
+            }
+            u32x4 ktf[2][D / 32];   // K^T fragments of this half for dQ^T
+#pragma unroll
+            for (int hs = 0; hs < 2; ++hs)
+#pragma unroll
+                for (int db = 0; db < D / 32; ++db) ktf[hs][db] = T::tfrag(kb, 32 * kb2 + 16 * hs, 32 * db);
+            if (bits != ~0ull) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r)
-                    if (!((bits >> (32 * kb + acc_row(r, h))) & 1ull)) s[kb][r] = -INFINITY;
-        }
-        uint32_t pk[2][8];
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+                    if (!((bits >> (32 * kb2 + acc_row(r, h))) & 1ull)) s[r] = -INFINITY;
+            }
+            uint32_t pk[8];
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
-                const float p0 = fast_exp2(fmaf(s[kb][2 * i], p.sl2, -lse2));
-                const float p1 = fast_exp2(fmaf(s[kb][2 * i + 1], p.sl2, -lse2));
-                pk[kb][i] = pack_bf16x2(p0 * (dp[kb][2 * i] - Di), p1 * (dp[kb][2 * i + 1] - Di));
+                const float p0 = fast_exp2(fmaf(s[2 * i], p.sl2, nl2));
+                const float p1 = fast_exp2(fmaf(s[2 * i + 1], p.sl2, nl2));
+                pk[i] = pack_bf16x2(p0 * dp[2 * i], p1 * dp[2 * i + 1]);
             }
 #pragma unroll
-        for (int stp = 0; stp < 4; ++stp) {
-            const u32x4 bfrag = acc_frag(pk, stp);
+            for (int hs = 0; hs < 2; ++hs) {
+                const u32x4 bfrag = {pk[4 * hs], pk[4 * hs + 1], pk[4 * hs + 2], pk[4 * hs + 3]};
 #pragma unroll
-            for (int db = 0; db < D / 32; ++db)
-                acc[db] = mfma_32x32x16_bf16(TransTile<D>::frag(kts, 32 * db + j, stp, h), bfrag, acc[db]);
+                for (int db = 0; db < D / 32; ++db) acc[db] = mfma_32x32x16_bf16(ktf[hs][db], bfrag, acc[db]);
+            }
         }
-        if (tn < ntile) store(smem + (buf ^ 1) * S::BUF);
-        buf ^= 1;
+        if (tn >= ntile) return true;
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
         t = tn;
+        tn = tnn_;
+        return false;
+    };
+
+    if (t < ntile) {
+        tn = next_tile(t);
+        load(t, 0);
+        if (tn < ntile) load(tn, 1);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        using C0 = std::integral_constant<int, 0>;
+        using C1 = std::integral_constant<int, 1>;
+        using C2 = std::integral_constant<int, 2>;
+        while (true) {
+            if (body(C0{})) break;
+            if (body(C1{})) break;
+            if (body(C2{})) break;
+        }
     }
 
     if (row_ok) {
@@ -239,20 +274,18 @@ __global__ __launch_bounds__(kThreads) void rsa_bwd_dq(BwdParams p) {
 }
 
 // ---------------------------------------------------------------- dK dV ---
-template <int D>
-struct DkvSmem {
-    static constexpr int Q_OFF = 0;
-    static constexpr int G_OFF = Q_OFF + RowTile<D>::ELEMS;
-    static constexpr int QT_OFF = G_OFF + RowTile<D>::ELEMS;
-    static constexpr int GT_OFF = QT_OFF + TransTile<D>::ELEMS;
-    static constexpr int ROWS_OFF = GT_OFF + TransTile<D>::ELEMS;   // lse2[64], D[64] as fp32
-    static constexpr int BUF = ROWS_OFF + 2 * kTileRows * 2;
-};
-
-template <int D>
-__global__ __launch_bounds__(kThreads) void rsa_bwd_dkdv(BwdParams p) {
-    using S = DkvSmem<D>;
-    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * S::BUF];
+// Key-stationary: 4 waves x 32 keys, K and V fragments in registers. Per
+// query tile (64 rows, in ring delivery order): S = Q K^T and dP - D =
+// dO V^T (lane <-> key, registers <-> query rows), P and dS elementwise, then
+// dV^T += dO^T P and dK^T += Q^T dS, with Q^T and dO^T from the transposing
+// read of the same Q and dO tiles.
+template <int D, bool CONTIG>
+__global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void rsa_bwd_dkdv(BwdParams p) {
+    using T = DirectTile<D, 1>;
+    constexpr int NBUF = 3;
+    constexpr int ROWV = 2 * kKT * 4;             // -D and -lse*log2(e) for 64 rows
+    constexpr int BUF = 2 * T::BYTES + ROWV;      // Q, dO, row statistics
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[NBUF * BUF];
 
     const int lid = xcd_remap(blockIdx.x, p.nt * p.BH);
     const int kt = lid % p.nt, bh = lid / p.nt, b = bh / p.H;
@@ -264,15 +297,16 @@ __global__ __launch_bounds__(kThreads) void rsa_bwd_dkdv(BwdParams p) {
     const bool key_ok = key_in && (p.mask == nullptr || p.mask[(size_t)b * p.L + key] != 0);
     const int c = key0 / p.Lc;   // key chunk of the tile's first key
     const size_t hoff = (size_t)bh * p.L * D;
-    const bool contig = p.contiguous != 0;
+    const size_t rows_all = (size_t)p.BH * p.L;
+    const float* nDh = p.stats + (size_t)bh * p.L;
+    const float* nLh = p.stats + rows_all + (size_t)bh * p.L;
 
     if (!__syncthreads_or(key_ok)) {
         // no valid key in this tile: its gradients are exactly zero
         if (key_in) {
             const u32x4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
-            for (int e = 0; e < D / 8; e += 1) {
-                if ((e & 1) != h) continue;
+            for (int e = h; e < D / 8; e += 2) {
                 *reinterpret_cast<u32x4*>(p.dk + hoff + (size_t)key * D + 8 * e) = z;
                 *reinterpret_cast<u32x4*>(p.dv + hoff + (size_t)key * D + 8 * e) = z;
             }
@@ -301,114 +335,138 @@ __global__ __launch_bounds__(kThreads) void rsa_bwd_dkdv(BwdParams p) {
             dv[db][r] = 0.0f;
         }
 
-    const int ntq = (p.L + kTileRows - 1) / kTileRows;
-    RowTile<D> qst, gst;
-    TransTile<D> qtst, gtst;
-    float rowval = 0.0f;   // threads 0..63: lse2 of row tid; 64..127: D of row tid - 64
-    auto load = [&](int t) {
-        const int u0 = t * kTileRows;
-        const int pos0 = contig ? ring_pos_rev(u0, c, p.N, p.Lc) : 0;
-        auto rpos = [&](int r) -> int {
-            const int u = u0 + r;
-            if (u >= p.L) return -1;
-            return contig ? pos0 + r : ring_pos_rev(u, c, p.N, p.Lc);
-        };
-        auto qptr = [&](int r) -> const uint16_t* {
-            const int pos = rpos(r);
-            return pos < 0 ? nullptr : p.q + hoff + (size_t)pos * D;
-        };
-        auto gptr = [&](int r) -> const uint16_t* {
-            const int pos = rpos(r);
-            return pos < 0 ? nullptr : p.dout + hoff + (size_t)pos * D;
-        };
-        qst.load(qptr);
-        gst.load(gptr);
-        qtst.load(qptr);
-        gtst.load(gptr);
-        if (threadIdx.x < 2 * kTileRows) {
-            const int r = threadIdx.x % kTileRows;
-            const int pos = rpos(r);
-            if (threadIdx.x < kTileRows)
-                rowval = pos < 0 ? INFINITY : lse_log2(p.lse[(size_t)bh * p.L + pos]);
-            else
-                rowval = pos < 0 ? 0.0f : p.delta[(size_t)bh * p.L + pos];
+    const int ntq = (p.L + kKT - 1) / kKT;
+    // Copy query tile t into buffer bi. Rows past the sequence read row 0
+    // (finite data) and get -lse*log2(e) = -inf, so their P is 0.
+    auto load = [&](int t, int bi) {
+        const int u0 = t * kKT;
+        uint8_t* qb = smem + bi * BUF;
+        uint8_t* gb = qb + T::BYTES;
+        uint8_t* rb = gb + T::BYTES;
+        if constexpr (CONTIG) {
+            const int pos0 = ring_pos_rev(u0, c, p.N, p.Lc);
+            T::load(qb, [&](int r) { return p.q + hoff + (size_t)(pos0 + r) * D; });
+            T::load(gb, [&](int r) { return p.dout + hoff + (size_t)(pos0 + r) * D; });
+            if (wave == 0) load_rowvec(rb, nDh, [&](int r) { return pos0 + r; });
+            if (wave == 1) load_rowvec(rb + kKT * 4, nLh, [&](int r) { return pos0 + r; });
+        } else {
+            auto pos = [&](int r) -> int {
+                const int u = u0 + r;
+                return u < p.L ? ring_pos_rev(u, c, p.N, p.Lc) : 0;
+            };
+            T::load(qb, [&](int r) { return p.q + hoff + (size_t)pos(r) * D; });
+            T::load(gb, [&](int r) { return p.dout + hoff + (size_t)pos(r) * D; });
+            if (wave == 0) load_rowvec(rb, nDh, pos);
+            if (wave == 1) load_rowvec(rb + kKT * 4, nLh, pos);
         }
     };
-    auto store = [&](uint16_t* buf) {
-        qst.store(buf + S::Q_OFF);
-        gst.store(buf + S::G_OFF);
-        qtst.store(buf + S::QT_OFF);
-        gtst.store(buf + S::GT_OFF);
-        if (threadIdx.x < 2 * kTileRows) reinterpret_cast<float*>(buf + S::ROWS_OFF)[threadIdx.x] = rowval;
+    // Rows past the sequence get P = 0. Run by wave 1, which issued the copy
+    // of these values, after its own s_waitcnt (so its write lands last).
+    auto fix_tail = [&](int t, int bi) {
+        if (CONTIG || t >= ntq || t * kKT + kKT <= p.L || wave != 1) return;
+        float* nl = reinterpret_cast<float*>(smem + bi * BUF + 2 * T::BYTES) + kKT;
+        if (t * kKT + lane >= p.L) nl[lane] = -INFINITY;
     };
 
-    load(0);
-    store(smem);
-    int buf = 0;
-    for (int t = 0; t < ntq; ++t) {
-        if (t + 1 < ntq) load(t + 1);
-        __syncthreads();
-        const uint16_t* base = smem + buf * S::BUF;
-        const uint16_t* qs = base + S::Q_OFF;
-        const uint16_t* gs = base + S::G_OFF;
-        const uint16_t* qts = base + S::QT_OFF;
-        const uint16_t* gts = base + S::GT_OFF;
-        const float* lse2s = reinterpret_cast<const float*>(base + S::ROWS_OFF);
-        const float* ds_ = lse2s + kTileRows;
-
-        // S = Q K^T and dP = dO V^T for 64 queries (two 32-row blocks):
-        // lane <-> key column, registers <-> query rows.
-        f32x16 s[2], dp[2];
+    auto body = [&](auto cb_c, int t) -> bool {
+        constexpr int CB = decltype(cb_c)::value;
+        constexpr int FB = (CB + 2) % NBUF;
+        const uint8_t* qb = smem + CB * BUF;
+        const uint8_t* gb = qb + T::BYTES;
+        const float* nDs = reinterpret_cast<const float*>(gb + T::BYTES);
+        const float* nLs = nDs + kKT;
+        if (t + 2 < ntq) load(t + 2, FB);
+        // two 32-query halves in turn, to bound the live registers
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
+        for (int qb2 = 0; qb2 < 2; ++qb2) {
+            // ---- S = Q K^T and dP - D = dO V^T - D for queries 32 qb2 .. +32
+            f32x16 s, dp;
+            {
+                u32x4 qfr[D / 16], gfr[D / 16];
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                s[qb][r] = 0.0f;
-                dp[qb][r] = 0.0f;
+                for (int ks = 0; ks < D / 16; ++ks) {
+                    qfr[ks] = T::chunk(qb, 32 * qb2 + j, 2 * ks + h);
+                    gfr[ks] = T::chunk(gb, 32 * qb2 + j, 2 * ks + h);
+                }
+#pragma unroll
+                for (int r4 = 0; r4 < 4; ++r4) {   // dP accumulators start at -D of their rows
+                    const f32x4 d4 = *reinterpret_cast<const f32x4*>(nDs + 32 * qb2 + 8 * r4 + 4 * h);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) dp[4 * r4 + e] = d4[e];
+                }
+#pragma unroll
+                for (int r = 0; r < 16; ++r) s[r] = 0.0f;
+#pragma unroll
+                for (int ks = 0; ks < D / 16; ++ks) {
+                    s = mfma_32x32x16_bf16(qfr[ks], kf[ks], s);
+                    dp = mfma_32x32x16_bf16(gfr[ks], vf[ks], dp);
+                }
             }
+            u32x4 qtf[2][D / 32], gtf[2][D / 32];
 #pragma unroll
-            for (int ks = 0; ks < D / 16; ++ks) {
-                s[qb] = mfma_32x32x16_bf16(RowTile<D>::frag(qs, 32 * qb + j, 16 * ks + 8 * h), kf[ks], s[qb]);
-                dp[qb] = mfma_32x32x16_bf16(RowTile<D>::frag(gs, 32 * qb + j, 16 * ks + 8 * h), vf[ks], dp[qb]);
-            }
-        }
-        uint32_t pp[2][8], pd[2][8];
+            for (int hs = 0; hs < 2; ++hs)
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb)
+                for (int db = 0; db < D / 32; ++db) {
+                    qtf[hs][db] = T::tfrag(qb, 32 * qb2 + 16 * hs, 32 * db);
+                    gtf[hs][db] = T::tfrag(gb, 32 * qb2 + 16 * hs, 32 * db);
+                }
+            uint32_t pp[8], pd[8];
 #pragma unroll
             for (int r4 = 0; r4 < 4; ++r4) {
-                const int qr = 32 * qb + 8 * r4 + 4 * h;   // query rows qr .. qr+3 of registers 4*r4 ..
-                const f32x4 l4 = *reinterpret_cast<const f32x4*>(lse2s + qr);
-                const f32x4 d4 = *reinterpret_cast<const f32x4*>(ds_ + qr);
+                const f32x4 l4 = *reinterpret_cast<const f32x4*>(nLs + 32 * qb2 + 8 * r4 + 4 * h);
                 float pv[4], dsv[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int r = 4 * r4 + e;
-                    const float pe = key_ok ? fast_exp2(fmaf(s[qb][r], p.sl2, -l4[e])) : 0.0f;
-                    pv[e] = pe;
-                    dsv[e] = pe * (dp[qb][r] - d4[e]);
+                    pv[e] = fast_exp2(fmaf(s[r], p.sl2, l4[e]));
+                    dsv[e] = pv[e] * dp[r];
                 }
-                pp[qb][2 * r4] = pack_bf16x2(pv[0], pv[1]);
-                pp[qb][2 * r4 + 1] = pack_bf16x2(pv[2], pv[3]);
-                pd[qb][2 * r4] = pack_bf16x2(dsv[0], dsv[1]);
-                pd[qb][2 * r4 + 1] = pack_bf16x2(dsv[2], dsv[3]);
+                pp[2 * r4] = pack_bf16x2(pv[0], pv[1]);
+                pp[2 * r4 + 1] = pack_bf16x2(pv[2], pv[3]);
+                pd[2 * r4] = pack_bf16x2(dsv[0], dsv[1]);
+                pd[2 * r4 + 1] = pack_bf16x2(dsv[2], dsv[3]);
             }
-        // dV^T += dO^T P and dK^T += Q^T dS, contracted over the 64 queries
+            // ---- dV^T += dO^T P and dK^T += Q^T dS over these 32 queries
 #pragma unroll
-        for (int stp = 0; stp < 4; ++stp) {
-            const u32x4 bp = acc_frag(pp, stp);
-            const u32x4 bd = acc_frag(pd, stp);
+            for (int hs = 0; hs < 2; ++hs) {
+                const u32x4 bp = {pp[4 * hs], pp[4 * hs + 1], pp[4 * hs + 2], pp[4 * hs + 3]};
+                const u32x4 bd = {pd[4 * hs], pd[4 * hs + 1], pd[4 * hs + 2], pd[4 * hs + 3]};
 #pragma unroll
-            for (int db = 0; db < D / 32; ++db) {
-                dv[db] = mfma_32x32x16_bf16(TransTile<D>::frag(gts, 32 * db + j, stp, h), bp, dv[db]);
-                dk[db] = mfma_32x32x16_bf16(TransTile<D>::frag(qts, 32 * db + j, stp, h), bd, dk[db]);
+                for (int db = 0; db < D / 32; ++db) {
+                    dv[db] = mfma_32x32x16_bf16(gtf[hs][db], bp, dv[db]);
+                    dk[db] = mfma_32x32x16_bf16(qtf[hs][db], bd, dk[db]);
+                }
             }
         }
-        if (t + 1 < ntq) store(smem + (buf ^ 1) * S::BUF);
-        buf ^= 1;
+        if (t + 1 >= ntq) return true;
+        __builtin_amdgcn_s_waitcnt(0);
+        fix_tail(t + 2, FB);
+        __syncthreads();
+        return false;
+    };
+
+    load(0, 0);
+    if (ntq > 1) load(1, 1);
+    __builtin_amdgcn_s_waitcnt(0);
+    fix_tail(0, 0);
+    fix_tail(1, 1);
+    __syncthreads();
+    {
+        using C0 = std::integral_constant<int, 0>;
+        using C1 = std::integral_constant<int, 1>;
+        using C2 = std::integral_constant<int, 2>;
+        int t = 0;
+        while (true) {
+            if (body(C0{}, t++)) break;
+            if (body(C1{}, t++)) break;
+            if (body(C2{}, t++)) break;
+        }
     }
 
     if (key_in) {
+        // a padded key's lane accumulated only into its own columns; it is 0
+        const float sk = key_ok ? p.scale : 0.0f;
+        const float sv = key_ok ? 1.0f : 0.0f;
         uint16_t* okk = p.dk + hoff + (size_t)key * D;
         uint16_t* ovv = p.dv + hoff + (size_t)key * D;
 #pragma unroll
@@ -416,10 +474,14 @@ __global__ __launch_bounds__(kThreads) void rsa_bwd_dkdv(BwdParams p) {
 #pragma unroll
             for (int r4 = 0; r4 < 4; ++r4) {
                 const int dcol = 32 * db + 8 * r4 + 4 * h;
-                const u32x2 wk = {pack_bf16x2(dk[db][4 * r4] * p.scale, dk[db][4 * r4 + 1] * p.scale),
-                                  pack_bf16x2(dk[db][4 * r4 + 2] * p.scale, dk[db][4 * r4 + 3] * p.scale)};
-                const u32x2 wv = {pack_bf16x2(dv[db][4 * r4], dv[db][4 * r4 + 1]),
-                                  pack_bf16x2(dv[db][4 * r4 + 2], dv[db][4 * r4 + 3])};
+                u32x2 wk = {pack_bf16x2(dk[db][4 * r4] * sk, dk[db][4 * r4 + 1] * sk),
+                            pack_bf16x2(dk[db][4 * r4 + 2] * sk, dk[db][4 * r4 + 3] * sk)};
+                u32x2 wv = {pack_bf16x2(dv[db][4 * r4] * sv, dv[db][4 * r4 + 1] * sv),
+                            pack_bf16x2(dv[db][4 * r4 + 2] * sv, dv[db][4 * r4 + 3] * sv)};
+                if (!key_ok) {   // inf * 0 would be NaN
+                    wk = u32x2{0u, 0u};
+                    wv = u32x2{0u, 0u};
+                }
                 *reinterpret_cast<u32x2*>(okk + dcol) = wk;
                 *reinterpret_cast<u32x2*>(ovv + dcol) = wv;
             }
@@ -435,7 +497,7 @@ BwdParams make_params(const BackwardCall& c) {
     p.dout = static_cast<const uint16_t*>(c.dout);
     p.lse = c.lse;
     p.mask = c.mask;
-    p.delta = c.delta;
+    p.stats = c.stats;
     p.dq = static_cast<uint16_t*>(c.dq);
     p.dk = static_cast<uint16_t*>(c.dk);
     p.dv = static_cast<uint16_t*>(c.dv);
@@ -447,7 +509,6 @@ BwdParams make_params(const BackwardCall& c) {
     p.nt = (c.L + 127) / 128;
     p.scale = (float)(1.0 / __builtin_sqrt((double)c.d));
     p.sl2 = (float)(1.4426950408889634 / __builtin_sqrt((double)c.d));
-    p.contiguous = (p.Lc % kTileRows) == 0;
     return p;
 }
 
@@ -455,21 +516,28 @@ template <int D>
 hipError_t launch_t(const BackwardCall& c, int stages, hipStream_t stream) {
     const BwdParams p = make_params(c);
     const long long rows = (long long)p.BH * c.L;
+    const bool contig = (p.Lc % kKT) == 0;
     if (stages & kBwdStagePre) {
         const long long threads = rows * (D / 8);
         hipLaunchKernelGGL((rsa_bwd_pre<D>), dim3((unsigned)((threads + kThreads - 1) / kThreads)), dim3(kThreads), 0,
-                           stream, p.o, p.dout, p.delta, rows);
+                           stream, p.o, p.dout, p.lse, p.stats, rows);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
     const unsigned blocks = (unsigned)((long long)p.nt * p.BH);
     if (stages & kBwdStageDq) {
-        hipLaunchKernelGGL((rsa_bwd_dq<D>), dim3(blocks), dim3(kThreads), 0, stream, p);
+        if (contig)
+            hipLaunchKernelGGL((rsa_bwd_dq<D, true>), dim3(blocks), dim3(kThreads), 0, stream, p);
+        else
+            hipLaunchKernelGGL((rsa_bwd_dq<D, false>), dim3(blocks), dim3(kThreads), 0, stream, p);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
     if (stages & kBwdStageDkDv) {
-        hipLaunchKernelGGL((rsa_bwd_dkdv<D>), dim3(blocks), dim3(kThreads), 0, stream, p);
+        if (contig)
+            hipLaunchKernelGGL((rsa_bwd_dkdv<D, true>), dim3(blocks), dim3(kThreads), 0, stream, p);
+        else
+            hipLaunchKernelGGL((rsa_bwd_dkdv<D, false>), dim3(blocks), dim3(kThreads), 0, stream, p);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
@@ -480,7 +548,7 @@ hipError_t launch_t(const BackwardCall& c, int stages, hipStream_t stream) {
 
 size_t backward_workspace_bytes(int B, int H, int L, int d) {
     (void)d;
-    return (size_t)B * H * L * sizeof(float);
+    return 2 * (size_t)B * H * L * sizeof(float);
 }
 
 hipError_t launch_backward(const BackwardCall& c, int stages, hipStream_t stream) {

@@ -44,7 +44,7 @@ struct BackwardCall {
     const void* dout;
     const float* lse;
     const uint8_t* mask;
-    float* delta;           // workspace [B,H,L] fp32
+    float* stats;           // row statistics [2][B,H,L] fp32: -D, -lse*log2(e)
     void* dq;
     void* dk;
     void* dv;
@@ -53,7 +53,7 @@ struct BackwardCall {
 
 size_t backward_workspace_bytes(int B, int H, int L, int d);
 
-// Backward stages (bit mask): delta = rowsum(dout o out); dq; dk and dv.
+// Backward stages (bit mask): row statistics; dq; dk and dv.
 constexpr int kBwdStagePre = 1;
 constexpr int kBwdStageDq = 2;
 constexpr int kBwdStageDkDv = 4;

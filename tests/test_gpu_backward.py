@@ -82,16 +82,17 @@ def test_backward_stages_match_and_are_deterministic():
     out, lse = rsa.forward(q, k, v, m, N=N, return_lse=True)
     full = rsa.backward(q, k, v, out, g, lse, m, N=N)
     again = rsa.backward(q, k, v, out, g, lse, m, N=N)
-    delta = rsa.backward_preprocess(out, g)
-    dq = rsa.backward_dq(q, k, v, g, lse, delta, m, N=N)
-    dk, dv = rsa.backward_dkdv(q, k, v, g, lse, delta, m, N=N)
+    stats = rsa.backward_preprocess(out, g, lse)
+    dq = rsa.backward_dq(q, k, v, g, stats, m, N=N)
+    dk, dv = rsa.backward_dkdv(q, k, v, g, stats, m, N=N)
     torch.cuda.synchronize()
     for a, b in zip(full, again):
         assert torch.equal(a, b)
     for a, b in zip(full, (dq, dk, dv)):
         assert torch.equal(a, b)
     want_delta = (out.float() * g.float()).sum(-1)
-    assert torch.allclose(delta, want_delta, rtol=1e-5, atol=1e-5)
+    assert torch.allclose(-stats[0], want_delta, rtol=1e-5, atol=1e-5)
+    assert torch.allclose(-stats[1], lse * 1.4426950408889634, rtol=1e-6, atol=1e-6)
 
 
 def test_backward_invariants():
