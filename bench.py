@@ -57,6 +57,36 @@ def parse():
     return ap.parse_args()
 
 
+KERNEL_SOURCES = {
+    "forward": ("rsa_fwd.hip", "rsa_tiles.h", "rsa_device.h"),
+    "bwd_dq": ("rsa_bwd.hip", "rsa_tiles.h", "rsa_device.h"),
+    "bwd_dkdv": ("rsa_bwd.hip", "rsa_tiles.h", "rsa_device.h"),
+}
+
+
+def recorded_traffic(workload: str, kernel: str):
+    """HBM bytes per launch from the calibrated FETCH_SIZE/WRITE_SIZE counters
+    summarised in profiles/<workload>_<kernel>_traffic.md, or None when there
+    is no such summary or the kernel's sources changed since it was taken."""
+    import hashlib
+
+    path = os.path.join(ROOT, "profiles", f"{workload}_{kernel}_traffic.md")
+    if kernel not in KERNEL_SOURCES or not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        if ":" in line and not line.startswith(("|", "#", " ")):
+            key, _, val = line.partition(":")
+            fields[key.strip()] = val.strip()
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(ROOT, "sequence_transformer_attention_rsa_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    if fields.get("source-sha256") != h.hexdigest() or "traffic_bytes" not in fields:
+        return None
+    return float(fields["traffic_bytes"])
+
+
 def valid_key_count(w, x):
     """Sum over (b) of valid keys, times H: the Lk actually attended."""
     if x["mask"] is None:
@@ -220,7 +250,8 @@ def main():
         "peak": peak,
         "unit": "TFLOP/s",
         "frac": achieved / peak,
-        "traffic": None,
+        "traffic": recorded_traffic(w.name, dominant),
+        "traffic_unit": "bytes per launch (calibrated FETCH_SIZE + WRITE_SIZE)",
         "avg_ms": per_kernel[dominant]["avg_ms"],
         "flops_per_launch": credited[dominant],
     }
