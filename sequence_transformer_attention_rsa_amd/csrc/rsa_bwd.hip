@@ -105,7 +105,7 @@ __device__ __forceinline__ void load_rowvec(uint8_t* lds, const float* src, RowO
 // dQ^T += K^T dS^T with K^T from the transposing read of the same K tile.
 template <int D, bool CONTIG>
 __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void rsa_bwd_dq(BwdParams p) {
-    using T = DirectTile<D, 1>;
+    using T = DirectTile<D>;
     constexpr int NBUF = 3;
     constexpr int BUF = 2 * T::BYTES;   // K, V
     __shared__ __attribute__((aligned(1024))) uint8_t smem[NBUF * BUF];
@@ -280,8 +280,8 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void rsa_bwd_dq(BwdParam
 // dV^T += dO^T P and dK^T += Q^T dS, with Q^T and dO^T from the transposing
 // read of the same Q and dO tiles.
 template <int D, bool CONTIG>
-__global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void rsa_bwd_dkdv(BwdParams p) {
-    using T = DirectTile<D, 1>;
+__global__ __launch_bounds__(kThreads, D == 64 ? 3 : 1) void rsa_bwd_dkdv(BwdParams p) {
+    using T = DirectTile<D>;
     constexpr int NBUF = 3;
     constexpr int ROWV = 2 * kKT * 4;             // -D and -lse*log2(e) for 64 rows
     constexpr int BUF = 2 * T::BYTES + ROWV;      // Q, dO, row statistics

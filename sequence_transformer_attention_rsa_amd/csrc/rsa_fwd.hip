@@ -11,7 +11,7 @@
 //
 // Kernel shape (bf16; one workgroup = 4 waves = 128 query rows of one head):
 //   * each wave owns 32 query rows; its Q fragment stays in registers;
-//   * keys stream through LDS in tiles of 64, three buffers deep, copied
+//   * keys stream through LDS in tiles of 64, double-buffered, copied
 //     straight from HBM by global_load_lds (no registers, no VALU) into an
 //     XOR-swizzled row-major layout; V^T fragments come from the transposing
 //     LDS read, so no transpose is ever stored;
@@ -19,8 +19,6 @@
 //     a lane owns one query column, so the row max and row sum are in-lane
 //     plus one exchange between wave halves, and the accumulator is the B
 //     operand of O^T = V^T P^T unchanged;
-//   * software pipelining: the score MFMAs of tile t+1 run next to the
-//     softmax VALU work of tile t;
 //   * online softmax in base 2 (scale and log2(e) folded into one FMA), with
 //     a lazy rescale: the running base only moves when a tile's maximum
 //     exceeds it by more than 8 (weights stay <= 2^8), which is exact after
@@ -261,30 +259,21 @@ __global__ __launch_bounds__(kThreads) void rsa_fwd_f32(FwdParams p) {
     }
 }
 
-#ifndef RSA_FWD_MIN_WAVES
-#define RSA_FWD_MIN_WAVES 2
-#endif
-
-// bf16 forward. QB 32-row query blocks per wave (4 waves per workgroup).
-// CONTIG: chunks are whole 64-key tiles (Lc % 64 == 0), so every tile is
-// one aligned, complete run of keys and needs no per-row bounds or ring
-// arithmetic.
-//
-// Tiles reach LDS by direct copies from HBM (no registers, no VALU), three
-// buffers deep: while tile t is consumed, tile t+1 is resident and tile t+2
-// is in flight. Each iteration first reads all of its LDS fragments (K of
-// tile t+1, V^T of tile t through the transposing LDS read), then issues the
-// copy of tile t+2, then runs the softmax of tile t on the VALU next to the
-// score MFMAs of tile t+1 (one branch-free block, so they interleave), then
-// the PV MFMAs of tile t. One barrier per tile.
-template <int D, bool CONTIG, int QB>
-__global__ __launch_bounds__(kThreads, (QB == 1 && D == 64) ? RSA_FWD_MIN_WAVES : 1) void rsa_fwd_bf16(FwdParams p) {
-    using KTile = DirectTile<D, 0>;
-    using VTile = DirectTile<D, 1>;
-    constexpr int NBUF = 3;
+// bf16 forward. Two LDS buffers: the copy of tile t+1 is issued right after
+// the barrier that opens tile t (its buffer held tile t-1, which every wave
+// has finished) and lands while tile t is computed; one barrier per tile.
+// Register use is kept low enough for three waves per SIMD at d = 64 (two at
+// d = 128): with several workgroups per CU, one wave's MFMAs run while
+// another's softmax occupies the vector ALU. (A variant that overlapped the
+// next tile's score MFMAs with this tile's softmax inside one wave needed
+// more registers, ran at fewer waves per SIMD and was slower.)
+template <int D, bool CONTIG>
+__global__ __launch_bounds__(kThreads, D == 64 ? 3 : 2) void rsa_fwd_bf16(FwdParams p) {
+    using KTile = DirectTile<D>;
+    using VTile = DirectTile<D>;
     constexpr int BUF = KTile::BYTES + VTile::BYTES;
-    constexpr int ROWS = 4 * 32 * QB;   // query rows per workgroup
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[NBUF * BUF];
+    constexpr int ROWS = 4 * 32;
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * BUF];
     __shared__ uint8_t tflag[kFwdMaxTiles];
 
     const int total = p.nqt * p.BH * p.groups;
@@ -298,8 +287,8 @@ __global__ __launch_bounds__(kThreads, (QB == 1 && D == 64) ? RSA_FWD_MIN_WAVES 
     const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
     const int j = lane & 31, h = lane >> 5;
     const int row0 = qt * ROWS;
-    const int wrow0 = row0 + wave * 32 * QB;   // first row of this wave
-    const int n = (p.q_pos0 + row0) / p.Lc;   // ring rank of the tile's first row
+    const int row = row0 + wave * 32 + j;
+    const int n = (p.q_pos0 + row0) / p.Lc;
 
     const int step0 = g * p.spg;
     const int step1 = min(p.N, step0 + p.spg);
@@ -315,37 +304,22 @@ __global__ __launch_bounds__(kThreads, (QB == 1 && D == 64) ? RSA_FWD_MIN_WAVES 
     for (int t = threadIdx.x; t < ntile; t += kThreads)
         tflag[t] = key_tile_flags(mrow, n, p.N, p.Lc, CONTIG, vbeg + t * kKT, vend);
 
-    // Q^T fragments (B operand of S^T = K Q^T): lane (j, h) of block qb holds
-    // row wrow0 + 32*qb + j, elements 16*ks + 8*h .. +8.
-    u32x4 qf[QB][D / 16];
+    u32x4 qf[D / 16];
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-        const int row = wrow0 + 32 * qb + j;
-#pragma unroll
-        for (int ks = 0; ks < D / 16; ++ks) {
-            u32x4 x = {0u, 0u, 0u, 0u};
-            if (row < p.Lq) x = *reinterpret_cast<const u32x4*>(qh + (size_t)row * D + 16 * ks + 8 * h);
-            qf[qb][ks] = x;
-        }
+    for (int ks = 0; ks < D / 16; ++ks) {
+        u32x4 x = {0u, 0u, 0u, 0u};
+        if (row < p.Lq) x = *reinterpret_cast<const u32x4*>(qh + (size_t)row * D + 16 * ks + 8 * h);
+        qf[ks] = x;
     }
-
-    f32x16 o[QB][D / 32];
-    float m_b[QB], l0[QB], l1[QB];
+    f32x16 o[D / 32];
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
+    for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-        for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) o[qb][db][r] = 0.0f;
-        m_b[qb] = -INFINITY;
-        l0[qb] = 0.0f;
-        l1[qb] = 0.0f;
-    }
+        for (int r = 0; r < 16; ++r) o[db][r] = 0.0f;
+    float m_b = -INFINITY, l0 = 0.0f, l1 = 0.0f;
 
     __syncthreads();   // tile flags visible
 
-    // Copy tile t into buffer bi. Rows outside the key range read the head's
-    // first row instead (finite data; those keys are masked to weight 0).
     auto load = [&](int t, int bi) {
         const int v0 = vbeg + t * kKT;
         uint8_t* kbuf = smem + bi * BUF;
@@ -357,12 +331,12 @@ __global__ __launch_bounds__(kThreads, (QB == 1 && D == 64) ? RSA_FWD_MIN_WAVES 
             KTile::load(kbuf, [&](int r) { return kb0 + r * D; });
             VTile::load(vbuf, [&](int r) { return vb0 + r * D; });
         } else {
-            auto row = [&](int r) -> size_t {
+            auto rowoff = [&](int r) -> size_t {
                 const int vk = v0 + r;
                 return vk < vend ? (size_t)ring_pos(vk, n, p.N, p.Lc) * D : 0;
             };
-            KTile::load(kbuf, [&](int r) { return kh + row(r); });
-            VTile::load(vbuf, [&](int r) { return vh + row(r); });
+            KTile::load(kbuf, [&](int r) { return kh + rowoff(r); });
+            VTile::load(vbuf, [&](int r) { return vh + rowoff(r); });
         }
     };
     auto next_tile = [&](int t) {
@@ -370,202 +344,121 @@ __global__ __launch_bounds__(kThreads, (QB == 1 && D == 64) ? RSA_FWD_MIN_WAVES 
         while (t < ntile && !(tflag[t] & 1)) ++t;
         return t;
     };
-    // K fragments (A operand of S^T) of the tile in buffer bi
-    auto kfrags = [&](int bi, u32x4 (&kf)[2][D / 16]) {
-        const uint8_t* kbuf = smem + bi * BUF;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int kq = 0; kq < D / 16; ++kq) kf[kb][kq] = KTile::chunk(kbuf, 32 * kb + j, 2 * kq + h);
-    };
-    // S^T = K Q^T for the 64 keys of a tile
-    auto scores = [&](const u32x4 (&kf)[2][D / 16], f32x16 (&s)[QB][2]) {
+
+    int t = next_tile(-1);
+    auto body = [&](auto cb_c) -> bool {
+        constexpr int CB = decltype(cb_c)::value;
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();   // tile t landed; buffer CB ^ 1 is free
+        const int tn = next_tile(t);
+        if (tn < ntile) load(tn, CB ^ 1);
+        const uint8_t* kbuf = smem + CB * BUF;
+        const uint8_t* vbuf = kbuf + KTile::BYTES;
+
+        f32x16 s[2];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
+            u32x4 kf[D / 16];
 #pragma unroll
-            for (int qb = 0; qb < QB; ++qb)
+            for (int kq = 0; kq < D / 16; ++kq) kf[kq] = KTile::chunk(kbuf, 32 * kb + j, 2 * kq + h);
 #pragma unroll
-                for (int r = 0; r < 16; ++r) s[qb][kb][r] = 0.0f;
+            for (int r = 0; r < 16; ++r) s[kb][r] = 0.0f;
 #pragma unroll
-            for (int kq = 0; kq < D / 16; ++kq)
-#pragma unroll
-                for (int qb = 0; qb < QB; ++qb) s[qb][kb] = mfma_32x32x16_bf16(kf[kb][kq], qf[qb][kq], s[qb][kb]);
+            for (int kq = 0; kq < D / 16; ++kq) s[kb] = mfma_32x32x16_bf16(kf[kq], qf[kq], s[kb]);
         }
-    };
-
-    // One pipelined step on tile t (buffer CB), tile tn (buffer CB+1) and the
-    // copy of tile tnn (into buffer CB+2). Buffer indices are compile-time
-    // constants and the two score arrays swap roles between calls, so the
-    // six-fold unrolled loop below needs no register copies and every LDS
-    // address is a per-lane base plus an immediate.
-    int t = next_tile(-1);
-    int tn = ntile;
-    auto body = [&](auto cb_c, f32x16 (&s_cur)[QB][2], f32x16 (&s_nxt)[QB][2]) -> bool {
-        constexpr int CB = decltype(cb_c)::value;
-        constexpr int NB = (CB + 1) % NBUF, FB = (CB + 2) % NBUF;
-        // ---- every LDS fragment of the iteration, read up front
-        u32x4 kf[2][D / 16];
-        kfrags(NB, kf);
-        u32x4 vf[4][D / 32];
-        {
-            const uint8_t* vbuf = smem + CB * BUF + KTile::BYTES;
-#pragma unroll
-            for (int stp = 0; stp < 4; ++stp)
-#pragma unroll
-                for (int db = 0; db < D / 32; ++db) vf[stp][db] = VTile::tfrag(vbuf, 16 * stp, 32 * db);
-        }
-        // ---- copy of tile t+2 into the free buffer, in flight meanwhile
-        const int tnn = tn < ntile ? next_tile(tn) : ntile;
-        if (tnn < ntile) load(tnn, FB);
-
-        // ---- key mask and range tail of tile t (tiles not fully valid)
         if (!(tflag[t] & 2)) {
             const uint64_t bits = key_tile_bits(mrow, n, p.N, p.Lc, CONTIG, vbeg + t * kKT, vend);
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
                 for (int r = 0; r < 16; ++r)
-                    if (!((bits >> (32 * kb + acc_row(r, h))) & 1ull)) {
-#pragma unroll
-                        for (int qb = 0; qb < QB; ++qb) s_cur[qb][kb][r] = -INFINITY;
-                    }
+                    if (!((bits >> (32 * kb + acc_row(r, h))) & 1ull)) s[kb][r] = -INFINITY;
         }
-
-        // ---- online softmax of tile t (base 2, lazy rescale)
-        float mx[QB];
-        bool need = false;
+        float a = fmaxf(s[0][0], s[0][1]);
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-            float a = fmaxf(s_cur[qb][0][0], s_cur[qb][0][1]);
+        for (int r = 2; r < 16; r += 2) a = __builtin_fmaxf(a, __builtin_fmaxf(s[0][r], s[0][r + 1]));
 #pragma unroll
-            for (int r = 2; r < 16; r += 2)
-                a = __builtin_fmaxf(a, __builtin_fmaxf(s_cur[qb][0][r], s_cur[qb][0][r + 1]));
-#pragma unroll
-            for (int r = 0; r < 16; r += 2)
-                a = __builtin_fmaxf(a, __builtin_fmaxf(s_cur[qb][1][r], s_cur[qb][1][r + 1]));
-            mx[qb] = fmaxf(a, shfl_xor32(a));
-            need |= mx[qb] > m_b[qb] + p.tau_raw;
-        }
-        if (wave_any(need)) {
-#pragma unroll
-            for (int qb = 0; qb < QB; ++qb) {
-                const float m_new = fmaxf(m_b[qb], mx[qb]);
-                const float alpha = fast_exp2((m_b[qb] - m_new) * p.sl2);
-                m_b[qb] = m_new;
-                l0[qb] *= alpha;
-                l1[qb] *= alpha;
-#pragma unroll
-                for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) o[qb][db][r] *= alpha;
-            }
-        }
-
-        // ---- scores of tile t+1 (MFMA) next to the exponentials of tile t
-        // (VALU), one branch-free block so the two interleave. After the last
-        // tile the buffer holds stale data and s_nxt is discarded.
-        scores(kf, s_nxt);
-
-        uint32_t pk[QB][2][8];   // P^T as bf16 pairs, same register order as s
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-            const float nbase = -m_b[qb] * p.sl2;
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    const float p0 = fast_exp2(fmaf(s_cur[qb][kb][2 * i], p.sl2, nbase));
-                    const float p1 = fast_exp2(fmaf(s_cur[qb][kb][2 * i + 1], p.sl2, nbase));
-                    pk[qb][kb][i] = pack_bf16x2(p0, p1);
-                }
-#pragma unroll
-            for (int i = 0; i < 8; i += 2) {
-                l0[qb] = add_bf16x2(pk[qb][0][i], l0[qb]);
-                l1[qb] = add_bf16x2(pk[qb][0][i + 1], l1[qb]);
-                l0[qb] = add_bf16x2(pk[qb][1][i], l0[qb]);
-                l1[qb] = add_bf16x2(pk[qb][1][i + 1], l1[qb]);
-            }
-        }
-
-        // ---- O^T += V^T P^T for tile t, four 16-key steps
-#pragma unroll
-        for (int stp = 0; stp < 4; ++stp)
+        for (int r = 0; r < 16; r += 2) a = __builtin_fmaxf(a, __builtin_fmaxf(s[1][r], s[1][r + 1]));
+        const float mx = fmaxf(a, shfl_xor32(a));
+        if (wave_any(mx > m_b + p.tau_raw)) {
+            const float m_new = fmaxf(m_b, mx);
+            const float alpha = fast_exp2((m_b - m_new) * p.sl2);
+            m_b = m_new;
+            l0 *= alpha;
+            l1 *= alpha;
 #pragma unroll
             for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-                for (int qb = 0; qb < QB; ++qb)
-                    o[qb][db] = mfma_32x32x16_bf16(vf[stp][db], acc_frag(pk[qb], stp), o[qb][db]);
-
-        if (tn >= ntile) return true;
-        __builtin_amdgcn_s_waitcnt(0);   // this wave's copies of tile t+2 landed
-        __syncthreads();                 // ... and every wave's
-        t = tn;
-        tn = tnn;
-        return false;
-    };
-
-    if (t < ntile) {
-        tn = next_tile(t);
-        load(t, 0);
-        if (tn < ntile) load(tn, 1);
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
-        f32x16 sA[QB][2], sB[QB][2];
-        {
-            u32x4 kf0[2][D / 16];
-            kfrags(0, kf0);
-            scores(kf0, sA);
+                for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
         }
+        const float nbase = -m_b * p.sl2;
+        uint32_t pk[2][8];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const float p0 = fast_exp2(fmaf(s[kb][2 * i], p.sl2, nbase));
+                const float p1 = fast_exp2(fmaf(s[kb][2 * i + 1], p.sl2, nbase));
+                pk[kb][i] = pack_bf16x2(p0, p1);
+            }
+#pragma unroll
+        for (int i = 0; i < 8; i += 2) {
+            l0 = add_bf16x2(pk[0][i], l0);
+            l1 = add_bf16x2(pk[0][i + 1], l1);
+            l0 = add_bf16x2(pk[1][i], l0);
+            l1 = add_bf16x2(pk[1][i + 1], l1);
+        }
+#pragma unroll
+        for (int stp = 0; stp < 4; ++stp) {
+            u32x4 vf[D / 32];
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db) vf[db] = VTile::tfrag(vbuf, 16 * stp, 32 * db);
+            const u32x4 bfrag = acc_frag(pk, stp);
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db) o[db] = mfma_32x32x16_bf16(vf[db], bfrag, o[db]);
+        }
+        t = tn;
+        return t >= ntile;
+    };
+    if (t < ntile) {
+        load(t, 0);
         using C0 = std::integral_constant<int, 0>;
         using C1 = std::integral_constant<int, 1>;
-        using C2 = std::integral_constant<int, 2>;
         while (true) {
-            if (body(C0{}, sA, sB)) break;
-            if (body(C1{}, sB, sA)) break;
-            if (body(C2{}, sA, sB)) break;
-            if (body(C0{}, sB, sA)) break;
-            if (body(C1{}, sA, sB)) break;
-            if (body(C2{}, sB, sA)) break;
+            if (body(C0{})) break;
+            if (body(C1{})) break;
         }
     }
 
-    // ---- epilogue
+    const float lsum = l0 + l1;
+    const float l_row = lsum + shfl_xor32(lsum);
+    if (row >= p.Lq) return;
+    if (p.groups == 1) {
+        const float inv = l_row > 0.0f ? 1.0f / l_row : 0.0f;
+        uint16_t* orow = static_cast<uint16_t*>(p.out) + ((size_t)bh * p.Lq + row) * D;
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-        const int row = wrow0 + 32 * qb + j;
-        const float lsum = l0[qb] + l1[qb];
-        const float l_row = lsum + shfl_xor32(lsum);
-        if (row >= p.Lq) continue;
-        if (p.groups == 1) {
-            const float inv = l_row > 0.0f ? 1.0f / l_row : 0.0f;
-            uint16_t* orow = static_cast<uint16_t*>(p.out) + ((size_t)bh * p.Lq + row) * D;
+        for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-            for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-                for (int r4 = 0; r4 < 4; ++r4) {
-                    const f32x16& a = o[qb][db];
-                    const u32x2 w = {pack_bf16x2(a[4 * r4] * inv, a[4 * r4 + 1] * inv),
-                                     pack_bf16x2(a[4 * r4 + 2] * inv, a[4 * r4 + 3] * inv)};
-                    *reinterpret_cast<u32x2*>(orow + 32 * db + 8 * r4 + 4 * h) = w;
-                }
-            if (p.lse && h == 0)
-                p.lse[(size_t)bh * p.Lq + row] =
-                    l_row > 0.0f ? (m_b[qb] * p.sl2 + __log2f(l_row)) * kLn2 : -INFINITY;
-        } else {
-            const size_t prow = ((size_t)g * p.BH + bh) * p.Lq + row;
-            float* po = p.part_o + prow * D;
-#pragma unroll
-            for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-                for (int r4 = 0; r4 < 4; ++r4) {
-                    const f32x16& a = o[qb][db];
-                    const f32x4 w = {a[4 * r4], a[4 * r4 + 1], a[4 * r4 + 2], a[4 * r4 + 3]};
-                    *reinterpret_cast<f32x4*>(po + 32 * db + 8 * r4 + 4 * h) = w;
-                }
-            if (h == 0) {
-                p.part_ml[2 * prow] = l_row > 0.0f ? m_b[qb] * p.sl2 : -INFINITY;
-                p.part_ml[2 * prow + 1] = l_row;
+            for (int r4 = 0; r4 < 4; ++r4) {
+                const u32x2 w = {pack_bf16x2(o[db][4 * r4] * inv, o[db][4 * r4 + 1] * inv),
+                                 pack_bf16x2(o[db][4 * r4 + 2] * inv, o[db][4 * r4 + 3] * inv)};
+                *reinterpret_cast<u32x2*>(orow + 32 * db + 8 * r4 + 4 * h) = w;
             }
+        if (p.lse && h == 0)
+            p.lse[(size_t)bh * p.Lq + row] = l_row > 0.0f ? (m_b * p.sl2 + __log2f(l_row)) * kLn2 : -INFINITY;
+    } else {
+        const size_t prow = ((size_t)g * p.BH + bh) * p.Lq + row;
+        float* po = p.part_o + prow * D;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4) {
+                const f32x4 w = {o[db][4 * r4], o[db][4 * r4 + 1], o[db][4 * r4 + 2], o[db][4 * r4 + 3]};
+                *reinterpret_cast<f32x4*>(po + 32 * db + 8 * r4 + 4 * h) = w;
+            }
+        if (h == 0) {
+            p.part_ml[2 * prow] = l_row > 0.0f ? m_b * p.sl2 : -INFINITY;
+            p.part_ml[2 * prow + 1] = l_row;
         }
     }
 }
@@ -611,13 +504,8 @@ __global__ __launch_bounds__(kThreads) void rsa_merge_kernel(const float* __rest
     if (lse && c4 == 0) lse[rrow] = lsum > 0.0f ? (M + __log2f(lsum)) * kLn2 : -INFINITY;
 }
 
-#ifndef RSA_FWD_QB
-#define RSA_FWD_QB 1
-#endif
-
 template <bool BF16, int D>
 hipError_t launch_t(const ForwardCall& c, hipStream_t stream) {
-    constexpr int QB = BF16 ? RSA_FWD_QB : 1;   // 32-row query blocks per wave
     FwdParams p{};
     p.q = c.q;
     p.k = c.k;
@@ -634,7 +522,7 @@ hipError_t launch_t(const ForwardCall& c, hipStream_t stream) {
     p.BH = c.B * c.H;
     p.groups = c.groups;
     p.spg = (c.N + c.groups - 1) / c.groups;
-    p.nqt = (c.Lq + 4 * kQW * QB - 1) / (4 * kQW * QB);
+    p.nqt = (c.Lq + 4 * kQW - 1) / (4 * kQW);
     const double sl2 = 1.4426950408889634 / __builtin_sqrt((double)D);
     p.sl2 = (float)sl2;
     p.tau_raw = (float)(8.0 / sl2);
@@ -647,9 +535,9 @@ hipError_t launch_t(const ForwardCall& c, hipStream_t stream) {
     if (total <= 0) return hipSuccess;
     if constexpr (BF16) {
         if (p.contiguous)
-            hipLaunchKernelGGL((rsa_fwd_bf16<D, true, QB>), dim3((unsigned)total), dim3(kThreads), 0, stream, p);
+            hipLaunchKernelGGL((rsa_fwd_bf16<D, true>), dim3((unsigned)total), dim3(kThreads), 0, stream, p);
         else
-            hipLaunchKernelGGL((rsa_fwd_bf16<D, false, QB>), dim3((unsigned)total), dim3(kThreads), 0, stream, p);
+            hipLaunchKernelGGL((rsa_fwd_bf16<D, false>), dim3((unsigned)total), dim3(kThreads), 0, stream, p);
     } else {
         hipLaunchKernelGGL((rsa_fwd_f32<D>), dim3((unsigned)total), dim3(kThreads), 0, stream, p);
     }
