@@ -106,9 +106,8 @@ __device__ __forceinline__ void load_rowvec(uint8_t* lds, const float* src, RowO
 template <int D, bool CONTIG>
 __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void rsa_bwd_dq(BwdParams p) {
     using T = DirectTile<D>;
-    constexpr int NBUF = 3;
     constexpr int BUF = 2 * T::BYTES;   // K, V
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[NBUF * BUF];
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * BUF];
     __shared__ uint8_t tflag[kFwdMaxTiles];
 
     const int lid = xcd_remap(blockIdx.x, p.nt * p.BH);
@@ -145,9 +144,6 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void rsa_bwd_dq(BwdParam
     // tail rows get P = 0 through nl2 = -inf
     const float nD = row_ok ? p.stats[(size_t)bh * p.L + row] : 0.0f;
     const float nl2 = row_ok ? p.stats[rows_all + (size_t)bh * p.L + row] : -INFINITY;
-    f32x16 nDv;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) nDv[r] = nD;
 
     f32x16 acc[D / 32];
 #pragma unroll
@@ -179,17 +175,17 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void rsa_bwd_dq(BwdParam
         return t;
     };
 
+    // Two LDS buffers: the copy of tile t+1 is issued right after the barrier
+    // that opens tile t and lands while tile t is computed.
     int t = next_tile(-1);
-    int tn = ntile;
-    int tnn_ = ntile;
     auto body = [&](auto cb_c) -> bool {
         constexpr int CB = decltype(cb_c)::value;
-        constexpr int FB = (CB + 2) % NBUF;
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();   // tile t landed; buffer CB ^ 1 is free
+        const int tn = next_tile(t);
+        if (tn < ntile) load(tn, CB ^ 1);
         const uint8_t* kb = smem + CB * BUF;
         const uint8_t* vb = kb + T::BYTES;
-        const int tnn = tn < ntile ? next_tile(tn) : ntile;
-        if (tnn < ntile) load(tnn, FB);
-        tnn_ = tnn;
         const uint64_t bits = (tflag[t] & 2) ? ~0ull : key_tile_bits(mrow, n, p.N, p.Lc, CONTIG, t * kKT, p.L);
         // two 32-key halves in turn, to bound the live registers
 #pragma unroll
@@ -204,19 +200,16 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void rsa_bwd_dq(BwdParam
                     vfr[ks] = T::chunk(vb, 32 * kb2 + j, 2 * ks + h);
                 }
 #pragma unroll
-                for (int r = 0; r < 16; ++r) s[r] = 0.0f;
-                dp = nDv;
+                for (int r = 0; r < 16; ++r) {
+                    s[r] = 0.0f;
+                    dp[r] = nD;
+                }
 #pragma unroll
                 for (int ks = 0; ks < D / 16; ++ks) {
                     s = mfma_32x32x16_bf16(kfr[ks], qf[ks], s);
                     dp = mfma_32x32x16_bf16(vfr[ks], gf[ks], dp);
                 }
             }
-            u32x4 ktf[2][D / 32];   // K^T fragments of this half for dQ^T
-#pragma unroll
-            for (int hs = 0; hs < 2; ++hs)
-#pragma unroll
-                for (int db = 0; db < D / 32; ++db) ktf[hs][db] = T::tfrag(kb, 32 * kb2 + 16 * hs, 32 * db);
             if (bits != ~0ull) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r)
@@ -229,34 +222,26 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void rsa_bwd_dq(BwdParam
                 const float p1 = fast_exp2(fmaf(s[2 * i + 1], p.sl2, nl2));
                 pk[i] = pack_bf16x2(p0 * dp[2 * i], p1 * dp[2 * i + 1]);
             }
+            // ---- dQ^T += K^T dS^T over these 32 keys (K^T: transposing read)
 #pragma unroll
             for (int hs = 0; hs < 2; ++hs) {
                 const u32x4 bfrag = {pk[4 * hs], pk[4 * hs + 1], pk[4 * hs + 2], pk[4 * hs + 3]};
 #pragma unroll
-                for (int db = 0; db < D / 32; ++db) acc[db] = mfma_32x32x16_bf16(ktf[hs][db], bfrag, acc[db]);
+                for (int db = 0; db < D / 32; ++db)
+                    acc[db] = mfma_32x32x16_bf16(T::tfrag(kb, 32 * kb2 + 16 * hs, 32 * db), bfrag, acc[db]);
             }
         }
-        if (tn >= ntile) return true;
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
         t = tn;
-        tn = tnn_;
-        return false;
+        return t >= ntile;
     };
 
     if (t < ntile) {
-        tn = next_tile(t);
         load(t, 0);
-        if (tn < ntile) load(tn, 1);
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
         using C0 = std::integral_constant<int, 0>;
         using C1 = std::integral_constant<int, 1>;
-        using C2 = std::integral_constant<int, 2>;
         while (true) {
             if (body(C0{})) break;
             if (body(C1{})) break;
-            if (body(C2{})) break;
         }
     }
 

@@ -267,10 +267,16 @@ __global__ __launch_bounds__(kThreads) void rsa_fwd_f32(FwdParams p) {
 // another's softmax occupies the vector ALU. (A variant that overlapped the
 // next tile's score MFMAs with this tile's softmax inside one wave needed
 // more registers, ran at fewer waves per SIMD and was slower.)
-template <int D, bool CONTIG>
-__global__ __launch_bounds__(kThreads, D == 64 ? 3 : 2) void rsa_fwd_bf16(FwdParams p) {
-    using KTile = DirectTile<D>;
-    using VTile = DirectTile<D>;
+template <int D, bool CONTIG, int QB>
+__global__ __launch_bounds__(256 / QB, (D == 64 && QB == 1) ? 3 : 2)
+void rsa_fwd_bf16(FwdParams p) {
+    // QB 32-row query blocks per wave; 128 query rows per workgroup either
+    // way (4 waves x 32 rows, or 2 waves x 64 rows: each K and V^T fragment
+    // read from LDS then feeds two MFMAs).
+    constexpr int WAVES = 4 / QB;
+    constexpr int NTH = WAVES * kWave;
+    using KTile = DirectTile<D, WAVES>;
+    using VTile = DirectTile<D, WAVES>;
     constexpr int BUF = KTile::BYTES + VTile::BYTES;
     constexpr int ROWS = 4 * 32;
     __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * BUF];
@@ -287,7 +293,7 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 3 : 2) void rsa_fwd_bf16(FwdPar
     const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
     const int j = lane & 31, h = lane >> 5;
     const int row0 = qt * ROWS;
-    const int row = row0 + wave * 32 + j;
+    const int wrow0 = row0 + wave * 32 * QB;
     const int n = (p.q_pos0 + row0) / p.Lc;
 
     const int step0 = g * p.spg;
@@ -301,22 +307,32 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 3 : 2) void rsa_fwd_bf16(FwdPar
     const uint8_t* mrow = p.mask ? p.mask + (size_t)b * p.L : nullptr;
     if (ntile > kFwdMaxTiles) return;   // the host never launches such a range
 
-    for (int t = threadIdx.x; t < ntile; t += kThreads)
+    for (int t = threadIdx.x; t < ntile; t += NTH)
         tflag[t] = key_tile_flags(mrow, n, p.N, p.Lc, CONTIG, vbeg + t * kKT, vend);
 
-    u32x4 qf[D / 16];
+    u32x4 qf[QB][D / 16];
 #pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) {
-        u32x4 x = {0u, 0u, 0u, 0u};
-        if (row < p.Lq) x = *reinterpret_cast<const u32x4*>(qh + (size_t)row * D + 16 * ks + 8 * h);
-        qf[ks] = x;
+    for (int qb = 0; qb < QB; ++qb) {
+        const int row = wrow0 + 32 * qb + j;
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks) {
+            u32x4 x = {0u, 0u, 0u, 0u};
+            if (row < p.Lq) x = *reinterpret_cast<const u32x4*>(qh + (size_t)row * D + 16 * ks + 8 * h);
+            qf[qb][ks] = x;
+        }
     }
-    f32x16 o[D / 32];
+    f32x16 o[QB][D / 32];
+    float m_b[QB], l0[QB], l1[QB];
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db)
+    for (int qb = 0; qb < QB; ++qb) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) o[db][r] = 0.0f;
-    float m_b = -INFINITY, l0 = 0.0f, l1 = 0.0f;
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) o[qb][db][r] = 0.0f;
+        m_b[qb] = -INFINITY;
+        l0[qb] = 0.0f;
+        l1[qb] = 0.0f;
+    }
 
     __syncthreads();   // tile flags visible
 
@@ -355,67 +371,97 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 3 : 2) void rsa_fwd_bf16(FwdPar
         const uint8_t* kbuf = smem + CB * BUF;
         const uint8_t* vbuf = kbuf + KTile::BYTES;
 
-        f32x16 s[2];
+        // ---- S^T = K Q^T for 64 keys (two 32-key blocks). All K fragments
+        // are requested before the first MFMA so their LDS latency overlaps.
+        f32x16 s[QB][2];
+        {
+            u32x4 kf[2][D / 16];
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-            u32x4 kf[D / 16];
+            for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-            for (int kq = 0; kq < D / 16; ++kq) kf[kq] = KTile::chunk(kbuf, 32 * kb + j, 2 * kq + h);
+                for (int kq = 0; kq < D / 16; ++kq) kf[kb][kq] = KTile::chunk(kbuf, 32 * kb + j, 2 * kq + h);
 #pragma unroll
-            for (int r = 0; r < 16; ++r) s[kb][r] = 0.0f;
+            for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-            for (int kq = 0; kq < D / 16; ++kq) s[kb] = mfma_32x32x16_bf16(kf[kq], qf[kq], s[kb]);
+                for (int qb = 0; qb < QB; ++qb) {
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) s[qb][kb][r] = 0.0f;
+#pragma unroll
+                    for (int kq = 0; kq < D / 16; ++kq)
+                        s[qb][kb] = mfma_32x32x16_bf16(kf[kb][kq], qf[qb][kq], s[qb][kb]);
+                }
         }
+        // ---- key mask and range tail (tiles not fully valid)
         if (!(tflag[t] & 2)) {
             const uint64_t bits = key_tile_bits(mrow, n, p.N, p.Lc, CONTIG, vbeg + t * kKT, vend);
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
                 for (int r = 0; r < 16; ++r)
-                    if (!((bits >> (32 * kb + acc_row(r, h))) & 1ull)) s[kb][r] = -INFINITY;
+                    if (!((bits >> (32 * kb + acc_row(r, h))) & 1ull)) {
+#pragma unroll
+                        for (int qb = 0; qb < QB; ++qb) s[qb][kb][r] = -INFINITY;
+                    }
         }
-        float a = fmaxf(s[0][0], s[0][1]);
+        // ---- online softmax (base 2, lazy rescale)
+        float mx[QB];
+        bool need = false;
 #pragma unroll
-        for (int r = 2; r < 16; r += 2) a = __builtin_fmaxf(a, __builtin_fmaxf(s[0][r], s[0][r + 1]));
+        for (int qb = 0; qb < QB; ++qb) {
+            float a = fmaxf(s[qb][0][0], s[qb][0][1]);
 #pragma unroll
-        for (int r = 0; r < 16; r += 2) a = __builtin_fmaxf(a, __builtin_fmaxf(s[1][r], s[1][r + 1]));
-        const float mx = fmaxf(a, shfl_xor32(a));
-        if (wave_any(mx > m_b + p.tau_raw)) {
-            const float m_new = fmaxf(m_b, mx);
-            const float alpha = fast_exp2((m_b - m_new) * p.sl2);
-            m_b = m_new;
-            l0 *= alpha;
-            l1 *= alpha;
+            for (int r = 2; r < 16; r += 2) a = __builtin_fmaxf(a, __builtin_fmaxf(s[qb][0][r], s[qb][0][r + 1]));
 #pragma unroll
-            for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+            for (int r = 0; r < 16; r += 2) a = __builtin_fmaxf(a, __builtin_fmaxf(s[qb][1][r], s[qb][1][r + 1]));
+            mx[qb] = fmaxf(a, shfl_xor32(a));
+            need |= mx[qb] > m_b[qb] + p.tau_raw;
         }
-        const float nbase = -m_b * p.sl2;
-        uint32_t pk[2][8];
+        if (wave_any(need)) {
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+            for (int qb = 0; qb < QB; ++qb) {
+                const float m_new = fmaxf(m_b[qb], mx[qb]);
+                const float alpha = fast_exp2((m_b[qb] - m_new) * p.sl2);
+                m_b[qb] = m_new;
+                l0[qb] *= alpha;
+                l1[qb] *= alpha;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const float p0 = fast_exp2(fmaf(s[kb][2 * i], p.sl2, nbase));
-                const float p1 = fast_exp2(fmaf(s[kb][2 * i + 1], p.sl2, nbase));
-                pk[kb][i] = pack_bf16x2(p0, p1);
+                for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) o[qb][db][r] *= alpha;
             }
-#pragma unroll
-        for (int i = 0; i < 8; i += 2) {
-            l0 = add_bf16x2(pk[0][i], l0);
-            l1 = add_bf16x2(pk[0][i + 1], l1);
-            l0 = add_bf16x2(pk[1][i], l0);
-            l1 = add_bf16x2(pk[1][i + 1], l1);
         }
+        uint32_t pk[QB][2][8];
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+            const float nbase = -m_b[qb] * p.sl2;
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const float p0 = fast_exp2(fmaf(s[qb][kb][2 * i], p.sl2, nbase));
+                    const float p1 = fast_exp2(fmaf(s[qb][kb][2 * i + 1], p.sl2, nbase));
+                    pk[qb][kb][i] = pack_bf16x2(p0, p1);
+                }
+#pragma unroll
+            for (int i = 0; i < 8; i += 2) {
+                l0[qb] = add_bf16x2(pk[qb][0][i], l0[qb]);
+                l1[qb] = add_bf16x2(pk[qb][0][i + 1], l1[qb]);
+                l0[qb] = add_bf16x2(pk[qb][1][i], l0[qb]);
+                l1[qb] = add_bf16x2(pk[qb][1][i + 1], l1[qb]);
+            }
+        }
+        // ---- O^T += V^T P^T, four 16-key steps
 #pragma unroll
         for (int stp = 0; stp < 4; ++stp) {
             u32x4 vf[D / 32];
 #pragma unroll
             for (int db = 0; db < D / 32; ++db) vf[db] = VTile::tfrag(vbuf, 16 * stp, 32 * db);
-            const u32x4 bfrag = acc_frag(pk, stp);
 #pragma unroll
-            for (int db = 0; db < D / 32; ++db) o[db] = mfma_32x32x16_bf16(vf[db], bfrag, o[db]);
+            for (int qb = 0; qb < QB; ++qb) {
+                const u32x4 bfrag = acc_frag(pk[qb], stp);
+#pragma unroll
+                for (int db = 0; db < D / 32; ++db) o[qb][db] = mfma_32x32x16_bf16(vf[db], bfrag, o[qb][db]);
+            }
         }
         t = tn;
         return t >= ntile;
@@ -430,35 +476,43 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 3 : 2) void rsa_fwd_bf16(FwdPar
         }
     }
 
-    const float lsum = l0 + l1;
-    const float l_row = lsum + shfl_xor32(lsum);
-    if (row >= p.Lq) return;
-    if (p.groups == 1) {
-        const float inv = l_row > 0.0f ? 1.0f / l_row : 0.0f;
-        uint16_t* orow = static_cast<uint16_t*>(p.out) + ((size_t)bh * p.Lq + row) * D;
+    // ---- epilogue
 #pragma unroll
-        for (int db = 0; db < D / 32; ++db)
+    for (int qb = 0; qb < QB; ++qb) {
+        const int row = wrow0 + 32 * qb + j;
+        const float lsum = l0[qb] + l1[qb];
+        const float l_row = lsum + shfl_xor32(lsum);
+        if (row >= p.Lq) continue;
+        if (p.groups == 1) {
+            const float inv = l_row > 0.0f ? 1.0f / l_row : 0.0f;
+            uint16_t* orow = static_cast<uint16_t*>(p.out) + ((size_t)bh * p.Lq + row) * D;
 #pragma unroll
-            for (int r4 = 0; r4 < 4; ++r4) {
-                const u32x2 w = {pack_bf16x2(o[db][4 * r4] * inv, o[db][4 * r4 + 1] * inv),
-                                 pack_bf16x2(o[db][4 * r4 + 2] * inv, o[db][4 * r4 + 3] * inv)};
-                *reinterpret_cast<u32x2*>(orow + 32 * db + 8 * r4 + 4 * h) = w;
+            for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+                for (int r4 = 0; r4 < 4; ++r4) {
+                    const f32x16& a = o[qb][db];
+                    const u32x2 w = {pack_bf16x2(a[4 * r4] * inv, a[4 * r4 + 1] * inv),
+                                     pack_bf16x2(a[4 * r4 + 2] * inv, a[4 * r4 + 3] * inv)};
+                    *reinterpret_cast<u32x2*>(orow + 32 * db + 8 * r4 + 4 * h) = w;
+                }
+            if (p.lse && h == 0)
+                p.lse[(size_t)bh * p.Lq + row] =
+                    l_row > 0.0f ? (m_b[qb] * p.sl2 + __log2f(l_row)) * kLn2 : -INFINITY;
+        } else {
+            const size_t prow = ((size_t)g * p.BH + bh) * p.Lq + row;
+            float* po = p.part_o + prow * D;
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+                for (int r4 = 0; r4 < 4; ++r4) {
+                    const f32x16& a = o[qb][db];
+                    const f32x4 w = {a[4 * r4], a[4 * r4 + 1], a[4 * r4 + 2], a[4 * r4 + 3]};
+                    *reinterpret_cast<f32x4*>(po + 32 * db + 8 * r4 + 4 * h) = w;
+                }
+            if (h == 0) {
+                p.part_ml[2 * prow] = l_row > 0.0f ? m_b[qb] * p.sl2 : -INFINITY;
+                p.part_ml[2 * prow + 1] = l_row;
             }
-        if (p.lse && h == 0)
-            p.lse[(size_t)bh * p.Lq + row] = l_row > 0.0f ? (m_b * p.sl2 + __log2f(l_row)) * kLn2 : -INFINITY;
-    } else {
-        const size_t prow = ((size_t)g * p.BH + bh) * p.Lq + row;
-        float* po = p.part_o + prow * D;
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-            for (int r4 = 0; r4 < 4; ++r4) {
-                const f32x4 w = {o[db][4 * r4], o[db][4 * r4 + 1], o[db][4 * r4 + 2], o[db][4 * r4 + 3]};
-                *reinterpret_cast<f32x4*>(po + 32 * db + 8 * r4 + 4 * h) = w;
-            }
-        if (h == 0) {
-            p.part_ml[2 * prow] = l_row > 0.0f ? m_b * p.sl2 : -INFINITY;
-            p.part_ml[2 * prow + 1] = l_row;
         }
     }
 }
@@ -534,10 +588,15 @@ hipError_t launch_t(const ForwardCall& c, hipStream_t stream) {
     const long long total = (long long)p.nqt * p.BH * p.groups;
     if (total <= 0) return hipSuccess;
     if constexpr (BF16) {
+        // 32 query rows per wave: 64 (QB = 2, two waves per workgroup) halves the
+        // LDS reads per MFMA but needs 256 VGPRs and two waves per SIMD, and
+        // measured 12% slower at d = 64.
+        constexpr int QB = 1;
+        const dim3 block(kWave * 4 / QB);
         if (p.contiguous)
-            hipLaunchKernelGGL((rsa_fwd_bf16<D, true>), dim3((unsigned)total), dim3(kThreads), 0, stream, p);
+            hipLaunchKernelGGL((rsa_fwd_bf16<D, true, QB>), dim3((unsigned)total), block, 0, stream, p);
         else
-            hipLaunchKernelGGL((rsa_fwd_bf16<D, false>), dim3((unsigned)total), dim3(kThreads), 0, stream, p);
+            hipLaunchKernelGGL((rsa_fwd_bf16<D, false, QB>), dim3((unsigned)total), block, 0, stream, p);
     } else {
         hipLaunchKernelGGL((rsa_fwd_f32<D>), dim3((unsigned)total), dim3(kThreads), 0, stream, p);
     }

@@ -67,13 +67,14 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 // chunk (16-byte fragment reads) and four consecutive rows read at a chunk
 // pair (the transposing ds_read_b64_tr_b16) both hit eight different bank
 // groups, so one copy of a tile serves both operand orientations.
-template <int D>
+template <int D, int WAVES = 4>
 struct DirectTile {
     static constexpr int ROW_BYTES = 2 * D;
     static constexpr int BYTES = kTileRows * ROW_BYTES;
-    static constexpr int CPR = D / 8;                  // 16-byte chunks per row
-    static constexpr int RPI = 1024 / ROW_BYTES;       // rows per wave-instruction
-    static constexpr int IPW = kTileRows / RPI / 4;    // instructions per wave (4 waves)
+    static constexpr int CPR = D / 8;                     // 16-byte chunks per row
+    static constexpr int RPI = 1024 / ROW_BYTES;          // rows per wave-instruction
+    static constexpr int IPW = kTileRows / RPI / WAVES;   // instructions per wave
+    static_assert(IPW * RPI * WAVES == kTileRows, "tile copy split");
 
     __device__ __forceinline__ static constexpr int swz(int r) { return 2 * (r & 3) + ((r >> 2) & 1); }
 
