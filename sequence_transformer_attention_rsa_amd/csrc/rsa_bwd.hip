@@ -104,7 +104,7 @@ __device__ __forceinline__ void load_rowvec(uint8_t* lds, const float* src, RowO
 // tile S^T = K Q^T and dP^T = V dO^T (lane <-> query), then
 // dQ^T += K^T dS^T with K^T from the transposing read of the same K tile.
 template <int D, bool CONTIG>
-__global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void rsa_bwd_dq(BwdParams p) {
+__global__ __launch_bounds__(kThreads, D == 64 ? 3 : 1) void rsa_bwd_dq(BwdParams p) {
     using T = DirectTile<D>;
     constexpr int BUF = 2 * T::BYTES;   // K, V
     __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * BUF];
@@ -188,7 +188,7 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void rsa_bwd_dq(BwdParam
         const uint8_t* vb = kb + T::BYTES;
         const uint64_t bits = (tflag[t] & 2) ? ~0ull : key_tile_bits(mrow, n, p.N, p.Lc, CONTIG, t * kKT, p.L);
         // two 32-key halves in turn, to bound the live registers
-#pragma unroll
+#pragma unroll 1
         for (int kb2 = 0; kb2 < 2; ++kb2) {
             // ---- S^T = K Q^T and dP^T - D = V dO^T - D for keys 32 kb2 .. +32
             f32x16 s, dp;
