@@ -9,6 +9,10 @@ rsa_backward_dkdv). Each call launches exactly one kernel, so HIP events
 recorded between the calls on the library's stream (torch's current stream)
 time every kernel separately. Rank-share workloads (--workload rank_share)
 time rsa_forward_rank (split kernel + merge) and have no backward.
+`--forward-variant twopass` times rsa_forward_twopass instead (score rows
+materialised in HBM, row softmax, then P V; forward only): its roofline is
+HBM bandwidth, 12 bytes per (query, key) pair -- fp32 scores written and read
+back, bf16 weights written and read back -- plus Q, K, V and O once.
 
 Algorithmic work (only what the method must compute, recomputation not
 credited): forward 4*B*H*Lq*Lk*d flops, backward 8*B*H*Lq*Lk*d (the dV, dP,
@@ -52,6 +56,9 @@ def parse():
     ap.add_argument("--workload", default="long_seq", choices=sorted(rsa_inputs.WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
     ap.add_argument("--forward-only", action="store_true", help="time the forward alone")
+    ap.add_argument("--forward-variant", default="fused", choices=("fused", "twopass"),
+                    help="fused online-softmax kernel, or the two-stage form with score rows in HBM "
+                         "(implies --forward-only)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (counter calibration)")
     return ap.parse_args()
@@ -61,6 +68,7 @@ KERNEL_SOURCES = {
     "forward": ("rsa_fwd.hip", "rsa_tiles.h", "rsa_device.h"),
     "bwd_dq": ("rsa_bwd.hip", "rsa_tiles.h", "rsa_device.h"),
     "bwd_dkdv": ("rsa_bwd.hip", "rsa_tiles.h", "rsa_device.h"),
+    "forward_twopass": ("rsa_twopass.hip", "rsa_tiles.h", "rsa_device.h"),
 }
 
 
@@ -146,6 +154,10 @@ def main():
     if w.dtype not in ("bf16", "f32"):
         print(f"workload {w.name} is CPU-only", file=sys.stderr)
         return 2
+    twopass = args.forward_variant == "twopass"
+    if twopass and (w.rank is not None or w.dtype != "bf16"):
+        print("the two-stage forward covers full-sequence bf16 workloads", file=sys.stderr)
+        return 2
     dev = torch.device("cuda:0")
     with_dout = w.rank is None
     x = rsa_inputs.make_inputs(w.B, w.H, w.L, w.d, w.seed, w.dtype, w.scale, w.valid_range,
@@ -158,7 +170,7 @@ def main():
     q, k, v = up(x["q"]), up(x["k"]), up(x["v"])
     g = up(x["dout"]) if with_dout else None
     mask = None if x["mask"] is None else torch.from_numpy(x["mask"]).to(dev)
-    do_bwd = with_dout and w.dtype == "bf16" and not args.forward_only
+    do_bwd = with_dout and w.dtype == "bf16" and not args.forward_only and not twopass
 
     out = torch.empty_like(q)
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
@@ -167,6 +179,9 @@ def main():
     ws = None
     if w.rank is not None:
         ws = torch.empty(rsa.forward_rank_workspace_bytes(w.B, w.H, w.L, w.d, w.N), dtype=torch.uint8, device=dev)
+    if twopass:
+        ws = torch.empty(rsa.forward_twopass_workspace_bytes(w.B, w.H, w.L, w.d, w.N), dtype=torch.uint8,
+                         device=dev)
 
     names = ["forward"] + (["bwd_preprocess", "bwd_dq", "bwd_dkdv"] if do_bwd else [])
 
@@ -175,7 +190,9 @@ def main():
             if ev is not None:
                 ev[i].record()
         mark(0)
-        if w.rank is not None:
+        if twopass:
+            rsa.forward_twopass(q, k, v, mask, N=w.N, out=out, lse=lse, workspace=ws)
+        elif w.rank is not None:
             rsa.forward_rank(q, k, v, mask, N=w.N, rank=w.rank, out=out, lse=lse, workspace=ws)
         else:
             rsa.forward(q, k, v, mask, N=w.N, out=out, lse=lse)
@@ -241,20 +258,38 @@ def main():
             per_kernel[name]["gbs"] = nbytes / avg_s / 1e9
     dominant = max((n for n in names if n in credited), key=lambda n: per_kernel[n]["avg_ms"])
     dom_s = per_kernel[dominant]["avg_ms"] * 1e-3
-    achieved = credited[dominant] / dom_s / 1e12
-    roofline = {
-        "kernel": {"forward": "rsa_fwd_kernel" if w.rank is None else "rsa_fwd_kernel + rsa_merge_kernel",
-                   "bwd_dq": "rsa_bwd_dq", "bwd_dkdv": "rsa_bwd_dkdv"}[dominant],
-        "bound": "mfma",
-        "achieved": achieved,
-        "peak": peak,
-        "unit": "TFLOP/s",
-        "frac": achieved / peak,
-        "traffic": recorded_traffic(w.name, dominant),
-        "traffic_unit": "bytes per launch (calibrated FETCH_SIZE + WRITE_SIZE)",
-        "avg_ms": per_kernel[dominant]["avg_ms"],
-        "flops_per_launch": credited[dominant],
-    }
+    if twopass:
+        # 12 bytes per (query, key) pair, plus q, k, v read and out, lse written once
+        pairs = w.B * w.H * w.L * w.L
+        nbytes = 12.0 * pairs + 4 * q.numel() * q.element_size() + lse.numel() * 4
+        achieved = nbytes / dom_s / 1e9
+        roofline = {
+            "kernel": "rsa_2p_scores + rsa_2p_softmax + rsa_2p_pv",
+            "bound": "hbm",
+            "achieved": achieved,
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": achieved / PEAK_HBM_GBS,
+            "traffic": recorded_traffic(w.name, "forward_twopass"),
+            "traffic_unit": "bytes per call (calibrated FETCH_SIZE + WRITE_SIZE, three kernels)",
+            "avg_ms": per_kernel[dominant]["avg_ms"],
+            "bytes_per_launch": nbytes,
+        }
+    else:
+        achieved = credited[dominant] / dom_s / 1e12
+        roofline = {
+            "kernel": {"forward": "rsa_fwd_kernel" if w.rank is None else "rsa_fwd_kernel + rsa_merge_kernel",
+                       "bwd_dq": "rsa_bwd_dq", "bwd_dkdv": "rsa_bwd_dkdv"}[dominant],
+            "bound": "mfma",
+            "achieved": achieved,
+            "peak": peak,
+            "unit": "TFLOP/s",
+            "frac": achieved / peak,
+            "traffic": recorded_traffic(w.name, dominant),
+            "traffic_unit": "bytes per launch (calibrated FETCH_SIZE + WRITE_SIZE)",
+            "avg_ms": per_kernel[dominant]["avg_ms"],
+            "flops_per_launch": credited[dominant],
+        }
 
     fwd_s = per_kernel["forward"]["avg_ms"] * 1e-3
     line = {
@@ -272,7 +307,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "L": w.L, "d": w.d, "N": w.N,
                    "rank": w.rank, "key_mask": w.valid_range is not None,
-                   "pass": "fwd+bwd" if do_bwd else "fwd", "description": w.description},
+                   "pass": "fwd+bwd" if do_bwd else "fwd", "forward": args.forward_variant,
+                   "description": w.description},
         "fwd_tflops": fwd_flops / fwd_s / 1e12,
         "fwd_tflops_nominal_keys": fwd_flops_nominal / fwd_s / 1e12,
         "fwd_frac_peak": fwd_flops / fwd_s / 1e12 / peak,

@@ -94,6 +94,31 @@ int rsa_forward_rank(const void* q_local, const void* k, const void* v, const ui
 size_t rsa_forward_rank_workspace_bytes(int B, int H, int L, int d, int N);
 
 /*
+ * The same forward in the pages' own two-stage form (ABSTRACT and
+ * proposed-method section: the key chunks circulate first and each rank
+ * holds its complete rows of scores; the value chunks circulate second and
+ * are weighted by the softmax of those rows). The score rows of every rank,
+ * [B,H,L,L] fp32, are written to `workspace`, normalised in place to bf16
+ * weights, then multiplied by V. Provided to measure what materialising the
+ * rows costs next to rsa_forward, which never holds a row of scores; its
+ * result agrees with rsa_forward's within rounding, and does not depend on
+ * N (N is validated like rsa_forward's).
+ *   q, k, v, key_mask, out, lse  as rsa_forward
+ *   workspace  device buffer of at least rsa_forward_twopass_workspace_bytes()
+ *              (4 * B * H * L * L bytes); its contents on return are
+ *              unspecified
+ * Only RSA_BF16, L <= 16384 and B * H <= 65535 are supported
+ * (RSA_ERR_UNSUPPORTED otherwise).
+ */
+int rsa_forward_twopass(const void* q, const void* k, const void* v, const uint8_t* key_mask,
+                        int B, int H, int L, int d, int N, int dtype,
+                        void* workspace, size_t workspace_bytes,
+                        void* stream, void* out, float* lse);
+
+/* Workspace bytes rsa_forward_twopass needs for these sizes (0 if they are invalid). */
+size_t rsa_forward_twopass_workspace_bytes(int B, int H, int L, int d, int N);
+
+/*
  * Backward of the loss <O, dO> (proposed-method section: gradients also pass
  * through the ring): dq, dk, dv for all ranks. `out` and `lse` are the
  * forward's outputs for the same inputs. Rank n's query chunk meets every

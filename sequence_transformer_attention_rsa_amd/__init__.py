@@ -9,6 +9,7 @@ the library is not built, every call raises.
     out = rsa.forward(q, k, v, key_mask=None, N=4)
     out, lse = rsa.forward(q, k, v, N=4, return_lse=True)
     out_local = rsa.forward_rank(q_local, k, v, N=64, rank=3)
+    out = rsa.forward_twopass(q, k, v, N=4)      # score rows materialised
     dq, dk, dv = rsa.backward(q, k, v, out, dout, lse, N=8)
 
 Shapes: q, k, v, out, dout: [B, H, L, d] contiguous (q_local and out_local:
@@ -25,9 +26,10 @@ from typing import Optional
 import torch
 
 __all__ = [
-    "RSAError", "lib_path", "load", "forward", "forward_rank", "backward",
+    "RSAError", "lib_path", "load", "forward", "forward_rank", "forward_twopass", "backward",
     "backward_preprocess", "backward_dq", "backward_dkdv",
-    "forward_rank_workspace_bytes", "backward_workspace_bytes", "status_string",
+    "forward_rank_workspace_bytes", "forward_twopass_workspace_bytes", "backward_workspace_bytes",
+    "status_string",
     "RSA_F32", "RSA_BF16",
 ]
 
@@ -47,6 +49,8 @@ SIGNATURES = {
     "rsa_forward": (_ci, [_vp, _vp, _vp, _vp, _ci, _ci, _ci, _ci, _ci, _ci, _vp, _vp, _vp]),
     "rsa_forward_rank": (_ci, [_vp, _vp, _vp, _vp, _ci, _ci, _ci, _ci, _ci, _ci, _ci, _vp, _sz, _vp, _vp, _vp]),
     "rsa_forward_rank_workspace_bytes": (_sz, [_ci, _ci, _ci, _ci, _ci]),
+    "rsa_forward_twopass": (_ci, [_vp, _vp, _vp, _vp, _ci, _ci, _ci, _ci, _ci, _ci, _vp, _sz, _vp, _vp, _vp]),
+    "rsa_forward_twopass_workspace_bytes": (_sz, [_ci, _ci, _ci, _ci, _ci]),
     "rsa_backward": (_ci, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _ci, _ci, _ci, _ci, _ci, _ci,
                            _vp, _sz, _vp, _vp, _vp, _vp]),
     "rsa_backward_workspace_bytes": (_sz, [_ci, _ci, _ci, _ci, _ci, _ci]),
@@ -179,6 +183,39 @@ def forward_rank(q_local, k, v, key_mask=None, N: int = 1, rank: int = 0, return
                                  _stream(dev), _ptr(out), _ptr(lse))
     if st != 0:
         raise RSAError(st, "rsa_forward_rank")
+    return (out, lse) if (return_lse or lse is not None) else out
+
+
+def forward_twopass_workspace_bytes(B: int, H: int, L: int, d: int, N: int) -> int:
+    return int(load().rsa_forward_twopass_workspace_bytes(B, H, L, d, N))
+
+
+def forward_twopass(q, k, v, key_mask=None, N: int = 1, return_lse: bool = False, out=None, lse=None,
+                    workspace=None):
+    """The forward with every score row materialised (fp32 [B,H,L,L] in the
+    workspace), softmax over each row, then the weighted sum of v. bf16 only."""
+    B, H, L, d = q.shape
+    dev = q.device
+    _need(q, "q", (B, H, L, d), q.dtype, dev)
+    _need(k, "k", (B, H, L, d), q.dtype, dev)
+    _need(v, "v", (B, H, L, d), q.dtype, dev)
+    m = _mask(key_mask, B, L, dev)
+    code = _dtype_code(q)
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, "out", (B, H, L, d), q.dtype, dev)
+    if lse is None and return_lse:
+        lse = torch.empty((B, H, L), dtype=torch.float32, device=dev)
+    if lse is not None:
+        _need(lse, "lse", (B, H, L), torch.float32, dev)
+    if workspace is None:
+        need = forward_twopass_workspace_bytes(B, H, L, d, N)
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    st = load().rsa_forward_twopass(_ptr(q), _ptr(k), _ptr(v), _ptr(m), B, H, L, d, int(N), code,
+                                    _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                    _stream(dev), _ptr(out), _ptr(lse))
+    if st != 0:
+        raise RSAError(st, "rsa_forward_twopass")
     return (out, lse) if (return_lse or lse is not None) else out
 
 

@@ -128,6 +128,43 @@ int rsa_forward_rank(const void* q_local, const void* k, const void* v, const ui
     return launch_status(rsa::launch_forward(c, static_cast<hipStream_t>(stream)));
 }
 
+size_t rsa_forward_twopass_workspace_bytes(int B, int H, int L, int d, int N) {
+    if (check_sizes(B, H, L, d, N, RSA_BF16) != RSA_OK) return 0;
+    return rsa::twopass_workspace_bytes(B, H, L);
+}
+
+int rsa_forward_twopass(const void* q, const void* k, const void* v, const uint8_t* key_mask,
+                        int B, int H, int L, int d, int N, int dtype,
+                        void* workspace, size_t workspace_bytes,
+                        void* stream, void* out, float* lse) {
+    if (!q || !k || !v || !out) return RSA_ERR_NULL;
+    int st = check_sizes(B, H, L, d, N, dtype);
+    if (st != RSA_OK) return st;
+    if (dtype != RSA_BF16 || L > rsa::kTwoPassMaxL || (long long)B * H > 65535) return RSA_ERR_UNSUPPORTED;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) ||
+        !aligned(key_mask, 16) || !aligned(lse, 4) || !aligned(workspace, 16))
+        return RSA_ERR_ALIGN;
+    if (!workspace || workspace_bytes < rsa::twopass_workspace_bytes(B, H, L)) return RSA_ERR_WORKSPACE;
+    rsa::ForwardCall c{};
+    c.q = q;
+    c.k = k;
+    c.v = v;
+    c.mask = key_mask;
+    c.out = out;
+    c.lse = lse;
+    c.part = static_cast<float*>(workspace);
+    c.B = B;
+    c.H = H;
+    c.L = L;
+    c.d = d;
+    c.N = N;
+    c.Lq = L;
+    c.q_pos0 = 0;
+    c.groups = 1;
+    c.bf16 = true;
+    return launch_status(rsa::launch_forward_twopass(c, static_cast<hipStream_t>(stream)));
+}
+
 size_t rsa_backward_workspace_bytes(int B, int H, int L, int d, int N, int dtype) {
     if (check_sizes(B, H, L, d, N, dtype) != RSA_OK) return 0;
     return rsa::backward_workspace_bytes(B, H, L, d);

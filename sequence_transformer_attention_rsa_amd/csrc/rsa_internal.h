@@ -36,6 +36,14 @@ int forward_rank_groups(int B, int H, int L, int d, int N);
 
 hipError_t launch_forward(const ForwardCall& c, hipStream_t stream);
 
+// Two-stage forward with the score rows materialised: fp32 scores
+// [B,H,L,L] in `part` (rewritten in place as bf16 weights), then P V. The
+// softmax pass holds a row in the registers of one workgroup (64 values per
+// thread at most), which bounds L.
+constexpr int kTwoPassMaxL = 16384;
+size_t twopass_workspace_bytes(int B, int H, int L);
+hipError_t launch_forward_twopass(const ForwardCall& c, hipStream_t stream);
+
 struct BackwardCall {
     const void* q;
     const void* k;

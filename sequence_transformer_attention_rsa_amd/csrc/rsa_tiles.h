@@ -107,6 +107,17 @@ struct DirectTile {
     // ds_read_b64_tr_b16: in each 16-lane group, lane 4*rho + c supplies
     // elements 4c..4c+3 of row rho of a 4 x 16 block; lane i receives column i.
     __device__ __forceinline__ static u32x4 tfrag(const uint8_t* lds, int row0, int col0) {
+        return tfrag_rows<false>(lds, row0, col0);
+    }
+
+    // The same fragment with rows in sequence: lane half h receives rows
+    // row0 + 8h + {0..7}, the order of a 16-byte row-major operand load.
+    __device__ __forceinline__ static u32x4 tfrag_seq(const uint8_t* lds, int row0, int col0) {
+        return tfrag_rows<true>(lds, row0, col0);
+    }
+
+    template <bool SEQ>
+    __device__ __forceinline__ static u32x4 tfrag_rows(const uint8_t* lds, int row0, int col0) {
         const int lane = threadIdx.x % kWave;
         const int i = lane & 15, ig = (lane >> 4) & 1, h = lane >> 5;
         const int rho = i >> 2, c4 = i & 3;
@@ -115,7 +126,7 @@ struct DirectTile {
         u32x4 f;
 #pragma unroll
         for (int k = 0; k < 2; ++k) {
-            const int r = row0 + 8 * k + 4 * h + rho;
+            const int r = row0 + (SEQ ? 8 * h + 4 * k : 8 * k + 4 * h) + rho;
             const uint8_t* addr = lds + r * ROW_BYTES + 16 * (c ^ swz(r)) + 8 * half;
             const s16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)addr);
             const u32x2 w = __builtin_bit_cast(u32x2, x);

@@ -102,3 +102,25 @@ def test_backward_validation(lib):
     assert call(ws_ptr=None) == EWS
     assert call(ws_bytes=ws - 4) == EWS
     assert call(dq=P + 2) == EALIGN
+
+
+def test_forward_twopass_validation(lib):
+    B, H, L, d, N = 2, 12, 8192, 64, 16
+    ws = lib.rsa_forward_twopass_workspace_bytes(B, H, L, d, N)
+    assert ws == 4 * B * H * L * L          # fp32 score rows of every rank
+    assert lib.rsa_forward_twopass_workspace_bytes(B, H, L - 1, d, N) == 0
+
+    def call(dtype=BF16, ws_ptr=P, ws_bytes=ws, q=P, L_=L, N_=N, B_=B, H_=H, d_=d):
+        return lib.rsa_forward_twopass(q, P, P, None, B_, H_, L_, d_, N_, dtype,
+                                       ws_ptr, ws_bytes, None, P, None)
+
+    assert call(q=None) == ENULL
+    assert call(L_=L - 1) == ESHAPE
+    assert call(d_=96) == EUNSUP
+    assert call(dtype=F32) == EUNSUP
+    assert call(L_=32768, N_=1, ws_bytes=1 << 62) == EUNSUP   # a row must fit one workgroup's registers
+    assert call(B_=65536, H_=1, L_=16, N_=1, ws_bytes=1 << 62) == EUNSUP
+    assert call(ws_ptr=None) == EWS
+    assert call(ws_bytes=ws - 1) == EWS
+    assert call(ws_ptr=P + 4) == EALIGN
+    assert call(q=P + 2) == EALIGN
