@@ -100,6 +100,9 @@ __device__ __forceinline__ void load_rowvec(uint8_t* lds, const float* src, RowO
 }
 
 // ------------------------------------------------------------------ dQ ---
+#ifndef RSA_DQ_NBUF
+#define RSA_DQ_NBUF 2
+#endif
 // Query-stationary, mirror of the forward: 4 waves x 32 query rows; per key
 // tile S^T = K Q^T and dP^T = V dO^T (lane <-> query), then
 // dQ^T += K^T dS^T with K^T from the transposing read of the same K tile.
@@ -107,7 +110,9 @@ template <int D, bool CONTIG>
 __global__ __launch_bounds__(kThreads, D == 64 ? 3 : 1) void rsa_bwd_dq(BwdParams p) {
     using T = DirectTile<D>;
     constexpr int BUF = 2 * T::BYTES;   // K, V
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * BUF];
+    constexpr int NBUF = RSA_DQ_NBUF;
+    constexpr int kCopies = 2 * T::IPW;   // copies per wave and tile
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[NBUF * BUF];
     __shared__ uint8_t tflag[kFwdMaxTiles];
 
     const int lid = xcd_remap(blockIdx.x, p.nt * p.BH);
@@ -151,15 +156,20 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 3 : 1) void rsa_bwd_dq(BwdParam
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[db][r] = 0.0f;
 
+    // the row data above has landed (waited for here, so that the compiler
+    // keeps no wait for it inside the tile loop); tile flags visible
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 
+    uint32_t voff[T::IPW];
+    T::row_offsets(voff);
     auto load = [&](int t, int bi) {
         const int v0 = t * kKT;
         uint8_t* kb = smem + bi * BUF;
         if constexpr (CONTIG) {
             const size_t pos0 = (size_t)ring_pos(v0, n, p.N, p.Lc) * D;
-            T::load(kb, [&](int r) { return kh + pos0 + r * D; });
-            T::load(kb + T::BYTES, [&](int r) { return vh + pos0 + r * D; });
+            T::load_rows(kb, kh + pos0, voff);
+            T::load_rows(kb + T::BYTES, vh + pos0, voff);
         } else {
             auto off = [&](int r) -> size_t {
                 const int vk = v0 + r;
@@ -175,15 +185,29 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 3 : 1) void rsa_bwd_dq(BwdParam
         return t;
     };
 
-    // Two LDS buffers: the copy of tile t+1 is issued right after the barrier
-    // that opens tile t and lands while tile t is computed.
+    // Three LDS buffers at d = 64: the copy of tile t+2 is issued right after
+    // the barrier that opens tile t and may stay in flight until t+1 opens
+    // (two buffers at d = 128: the copy of t+1 lands while t is computed).
     int t = next_tile(-1);
+    int t1 = t < ntile ? next_tile(t) : ntile;
     auto body = [&](auto cb_c) -> bool {
         constexpr int CB = decltype(cb_c)::value;
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();   // tile t landed; buffer CB ^ 1 is free
-        const int tn = next_tile(t);
-        if (tn < ntile) load(tn, CB ^ 1);
+        constexpr int FB = (CB + NBUF - 1) % NBUF;   // buffer of tile t-1
+        if (NBUF == 3 && t1 < ntile)
+            vm_wait<kCopies>();   // tile t landed; the copy of t1 may stay in flight
+        else
+            vm_wait<0>();
+        bare_barrier();   // every wave's part of tile t landed, tile t-1 consumed
+        int tn;
+        if constexpr (NBUF == 3) {
+            tn = t1;
+            const int t2 = t1 < ntile ? next_tile(t1) : ntile;
+            if (t2 < ntile) load(t2, FB);
+            t1 = t2;
+        } else {
+            tn = next_tile(t);
+            if (tn < ntile) load(tn, FB);
+        }
         const uint8_t* kb = smem + CB * BUF;
         const uint8_t* vb = kb + T::BYTES;
         const uint64_t bits = (tflag[t] & 2) ? ~0ull : key_tile_bits(mrow, n, p.N, p.Lc, CONTIG, t * kKT, p.L);
@@ -236,12 +260,22 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 3 : 1) void rsa_bwd_dq(BwdParam
     };
 
     if (t < ntile) {
-        load(t, 0);
         using C0 = std::integral_constant<int, 0>;
         using C1 = std::integral_constant<int, 1>;
-        while (true) {
-            if (body(C0{})) break;
-            if (body(C1{})) break;
+        using C2 = std::integral_constant<int, 2>;
+        load(t, 0);
+        if constexpr (NBUF == 3) {
+            if (t1 < ntile) load(t1, 1);
+            while (true) {
+                if (body(C0{})) break;
+                if (body(C1{})) break;
+                if (body(C2{})) break;
+            }
+        } else {
+            while (true) {
+                if (body(C0{})) break;
+                if (body(C1{})) break;
+            }
         }
     }
 
@@ -321,6 +355,12 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 3 : 1) void rsa_bwd_dkdv(BwdPar
         }
 
     const int ntq = (p.L + kKT - 1) / kKT;
+    // The K and V fragments have landed (waited for here, so that the
+    // compiler keeps no wait for them inside the tile loop).
+    __builtin_amdgcn_s_waitcnt(0);
+    uint32_t voff[T::IPW];
+    T::row_offsets(voff);
+    const uint32_t roff = (uint32_t)(4 * lane);
     // Copy query tile t into buffer bi. Rows past the sequence read row 0
     // (finite data) and get -lse*log2(e) = -inf, so their P is 0.
     auto load = [&](int t, int bi) {
@@ -330,10 +370,10 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 3 : 1) void rsa_bwd_dkdv(BwdPar
         uint8_t* rb = gb + T::BYTES;
         if constexpr (CONTIG) {
             const int pos0 = ring_pos_rev(u0, c, p.N, p.Lc);
-            T::load(qb, [&](int r) { return p.q + hoff + (size_t)(pos0 + r) * D; });
-            T::load(gb, [&](int r) { return p.dout + hoff + (size_t)(pos0 + r) * D; });
-            if (wave == 0) load_rowvec(rb, nDh, [&](int r) { return pos0 + r; });
-            if (wave == 1) load_rowvec(rb + kKT * 4, nLh, [&](int r) { return pos0 + r; });
+            T::load_rows(qb, p.q + hoff + (size_t)pos0 * D, voff);
+            T::load_rows(gb, p.dout + hoff + (size_t)pos0 * D, voff);
+            if (wave == 0) dma_copy4(nDh + pos0, roff, lds_addr(rb));
+            if (wave == 1) dma_copy4(nLh + pos0, roff, lds_addr(rb + kKT * 4));
         } else {
             auto pos = [&](int r) -> int {
                 const int u = u0 + r;
@@ -346,11 +386,21 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 3 : 1) void rsa_bwd_dkdv(BwdPar
         }
     };
     // Rows past the sequence get P = 0. Run by wave 1, which issued the copy
-    // of these values, after its own s_waitcnt (so its write lands last).
+    // of these values, after its own wait for that copy (so its write lands
+    // last).
     auto fix_tail = [&](int t, int bi) {
         if (CONTIG || t >= ntq || t * kKT + kKT <= p.L || wave != 1) return;
         float* nl = reinterpret_cast<float*>(smem + bi * BUF + 2 * T::BYTES) + kKT;
         if (t * kKT + lane >= p.L) nl[lane] = -INFINITY;
+    };
+
+    // This wave's copies per query tile: Q and dO tiles, plus one row vector
+    // for waves 0 and 1. Wait until only one tile's copies remain in flight.
+    auto wait_tile_copies_but_one = [&]() {
+        if (wave < 2)
+            vm_wait<2 * T::IPW + 1>();
+        else
+            vm_wait<2 * T::IPW>();
     };
 
     auto body = [&](auto cb_c, int t) -> bool {
@@ -424,18 +474,25 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 3 : 1) void rsa_bwd_dkdv(BwdPar
             }
         }
         if (t + 1 >= ntq) return true;
-        __builtin_amdgcn_s_waitcnt(0);
-        fix_tail(t + 2, FB);
-        __syncthreads();
+        // tile t+1 landed (this wave's copies of t+2 may stay in flight)
+        if (t + 2 < ntq)
+            wait_tile_copies_but_one();
+        else
+            vm_wait<0>();
+        fix_tail(t + 1, (CB + 1) % NBUF);
+        bare_barrier();   // tile t+1 visible; buffer CB free for tile t+3
         return false;
     };
 
     load(0, 0);
-    if (ntq > 1) load(1, 1);
-    __builtin_amdgcn_s_waitcnt(0);
+    if (ntq > 1) {
+        load(1, 1);
+        wait_tile_copies_but_one();
+    } else {
+        vm_wait<0>();
+    }
     fix_tail(0, 0);
-    fix_tail(1, 1);
-    __syncthreads();
+    bare_barrier();
     {
         using C0 = std::integral_constant<int, 0>;
         using C1 = std::integral_constant<int, 1>;

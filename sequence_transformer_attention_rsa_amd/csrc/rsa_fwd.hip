@@ -45,6 +45,13 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kKT = kFwdKeyTile;   // keys per tile
 constexpr int kQW = 32;            // query rows per wave
+// Initial running base (raw score units) of the bf16 kernel: finite and far
+// below any score, so that every valid weight formed against it overflows to
+// +inf and forces the first rescale, while padded keys (-inf) give weight 0.
+constexpr float kNoBase = -1.0e30f;
+// Largest sum of one lane's 32 weights of a tile before the running base is
+// moved up (each weight then stays <= 2^12, far from fp32 and bf16 limits).
+constexpr float kMaxTileSum = 4096.0f;
 
 struct FwdParams {
     const void* q;
@@ -259,14 +266,17 @@ __global__ __launch_bounds__(kThreads) void rsa_fwd_f32(FwdParams p) {
     }
 }
 
-// bf16 forward. Two LDS buffers: the copy of tile t+1 is issued right after
-// the barrier that opens tile t (its buffer held tile t-1, which every wave
-// has finished) and lands while tile t is computed; one barrier per tile.
-// Register use is kept low enough for three waves per SIMD at d = 64 (two at
-// d = 128): with several workgroups per CU, one wave's MFMAs run while
-// another's softmax occupies the vector ALU. (A variant that overlapped the
-// next tile's score MFMAs with this tile's softmax inside one wave needed
-// more registers, ran at fewer waves per SIMD and was slower.)
+// bf16 forward. Key/value tiles are copied ahead of use: with three LDS
+// buffers (d = 64) the copy of tile t+2 is issued right after the barrier
+// that opens tile t and may stay in flight until tile t+1 opens; with two
+// buffers (d = 128, where LDS allows fewer) the copy of t+1 lands during t.
+// Chunk-aligned key ranges use copies the compiler does not track (see
+// rsa_tiles.h), so nothing but the explicit vm_wait before each barrier waits
+// for them. Register use is kept low enough for three waves per SIMD at
+// d = 64 (two at d = 128): with several workgroups per CU, one wave's MFMAs
+// run while another's softmax occupies the vector ALU. (A variant that
+// overlapped the next tile's score MFMAs with this tile's softmax inside one
+// wave needed more registers, ran at fewer waves per SIMD and was slower.)
 template <int D, bool CONTIG, int QB>
 __global__ __launch_bounds__(256 / QB, (D == 64 && QB == 1) ? 3 : 2)
 void rsa_fwd_bf16(FwdParams p) {
@@ -278,8 +288,10 @@ void rsa_fwd_bf16(FwdParams p) {
     using KTile = DirectTile<D, WAVES>;
     using VTile = DirectTile<D, WAVES>;
     constexpr int BUF = KTile::BYTES + VTile::BYTES;
+    constexpr int NBUF = (D == 64 && QB == 1) ? 3 : 2;
+    constexpr int kCopies = KTile::IPW + VTile::IPW;   // copies per wave and tile
     constexpr int ROWS = 4 * 32;
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * BUF];
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[NBUF * BUF];
     __shared__ uint8_t tflag[kFwdMaxTiles];
 
     const int total = p.nqt * p.BH * p.groups;
@@ -329,23 +341,26 @@ void rsa_fwd_bf16(FwdParams p) {
         for (int db = 0; db < D / 32; ++db)
 #pragma unroll
             for (int r = 0; r < 16; ++r) o[qb][db][r] = 0.0f;
-        m_b[qb] = -INFINITY;
+        m_b[qb] = kNoBase;
         l0[qb] = 0.0f;
         l1[qb] = 0.0f;
     }
 
-    __syncthreads();   // tile flags visible
+    // The Q fragments have landed (waited for here, so that the compiler
+    // keeps no wait for them inside the tile loop); tile flags visible.
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
 
+    uint32_t voff[KTile::IPW];
+    KTile::row_offsets(voff);
     auto load = [&](int t, int bi) {
         const int v0 = vbeg + t * kKT;
         uint8_t* kbuf = smem + bi * BUF;
         uint8_t* vbuf = kbuf + KTile::BYTES;
         if constexpr (CONTIG) {
             const int pos0 = ring_pos(v0, n, p.N, p.Lc);
-            const uint16_t* kb0 = kh + (size_t)pos0 * D;
-            const uint16_t* vb0 = vh + (size_t)pos0 * D;
-            KTile::load(kbuf, [&](int r) { return kb0 + r * D; });
-            VTile::load(vbuf, [&](int r) { return vb0 + r * D; });
+            KTile::load_rows(kbuf, kh + (size_t)pos0 * D, voff);
+            VTile::load_rows(vbuf, vh + (size_t)pos0 * D, voff);
         } else {
             auto rowoff = [&](int r) -> size_t {
                 const int vk = v0 + r;
@@ -362,12 +377,25 @@ void rsa_fwd_bf16(FwdParams p) {
     };
 
     int t = next_tile(-1);
+    int t1 = t < ntile ? next_tile(t) : ntile;
     auto body = [&](auto cb_c) -> bool {
         constexpr int CB = decltype(cb_c)::value;
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();   // tile t landed; buffer CB ^ 1 is free
-        const int tn = next_tile(t);
-        if (tn < ntile) load(tn, CB ^ 1);
+        constexpr int FB = (CB + NBUF - 1) % NBUF;   // buffer of tile t-1, free after the barrier
+        if (NBUF == 3 && t1 < ntile)
+            vm_wait<kCopies>();   // tile t landed; the copy of t1 may stay in flight
+        else
+            vm_wait<0>();
+        bare_barrier();   // every wave's part of tile t landed, tile t-1 consumed
+        int tn;
+        if constexpr (NBUF == 3) {
+            tn = t1;
+            const int t2 = t1 < ntile ? next_tile(t1) : ntile;
+            if (t2 < ntile) load(t2, FB);
+            t1 = t2;
+        } else {
+            tn = next_tile(t);
+            if (tn < ntile) load(tn, FB);
+        }
         const uint8_t* kbuf = smem + CB * BUF;
         const uint8_t* vbuf = kbuf + KTile::BYTES;
 
@@ -403,36 +431,13 @@ void rsa_fwd_bf16(FwdParams p) {
                         for (int qb = 0; qb < QB; ++qb) s[qb][kb][r] = -INFINITY;
                     }
         }
-        // ---- online softmax (base 2, lazy rescale)
-        float mx[QB];
-        bool need = false;
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-            float a = fmaxf(s[qb][0][0], s[qb][0][1]);
-#pragma unroll
-            for (int r = 2; r < 16; r += 2) a = __builtin_fmaxf(a, __builtin_fmaxf(s[qb][0][r], s[qb][0][r + 1]));
-#pragma unroll
-            for (int r = 0; r < 16; r += 2) a = __builtin_fmaxf(a, __builtin_fmaxf(s[qb][1][r], s[qb][1][r + 1]));
-            mx[qb] = fmaxf(a, shfl_xor32(a));
-            need |= mx[qb] > m_b[qb] + p.tau_raw;
-        }
-        if (wave_any(need)) {
-#pragma unroll
-            for (int qb = 0; qb < QB; ++qb) {
-                const float m_new = fmaxf(m_b[qb], mx[qb]);
-                const float alpha = fast_exp2((m_b[qb] - m_new) * p.sl2);
-                m_b[qb] = m_new;
-                l0[qb] *= alpha;
-                l1[qb] *= alpha;
-#pragma unroll
-                for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) o[qb][db][r] *= alpha;
-            }
-        }
+        // ---- online softmax (base 2). The weights are formed against the
+        // running base first; only when some lane's tile sum exceeds
+        // kMaxTileSum (always, while the base is still kNoBase) does the wave
+        // take the row maximum, move the base up, rescale and form them again.
         uint32_t pk[QB][2][8];
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
+        float tl0[QB], tl1[QB];
+        auto weights = [&](int qb) {
             const float nbase = -m_b[qb] * p.sl2;
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
@@ -442,13 +447,47 @@ void rsa_fwd_bf16(FwdParams p) {
                     const float p1 = fast_exp2(fmaf(s[qb][kb][2 * i + 1], p.sl2, nbase));
                     pk[qb][kb][i] = pack_bf16x2(p0, p1);
                 }
+            float a0 = 0.0f, a1 = 0.0f;
 #pragma unroll
             for (int i = 0; i < 8; i += 2) {
-                l0[qb] = add_bf16x2(pk[qb][0][i], l0[qb]);
-                l1[qb] = add_bf16x2(pk[qb][0][i + 1], l1[qb]);
-                l0[qb] = add_bf16x2(pk[qb][1][i], l0[qb]);
-                l1[qb] = add_bf16x2(pk[qb][1][i + 1], l1[qb]);
+                a0 = add_bf16x2(pk[qb][0][i], a0);
+                a1 = add_bf16x2(pk[qb][0][i + 1], a1);
+                a0 = add_bf16x2(pk[qb][1][i], a0);
+                a1 = add_bf16x2(pk[qb][1][i + 1], a1);
             }
+            tl0[qb] = a0;
+            tl1[qb] = a1;
+        };
+        bool over = false;
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+            weights(qb);
+            over |= tl0[qb] + tl1[qb] > kMaxTileSum;
+        }
+        if (wave_any(over)) {
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb) {
+                float a = __builtin_fmaxf(s[qb][0][0], s[qb][0][1]);
+#pragma unroll
+                for (int r = 2; r < 16; r += 2) a = __builtin_fmaxf(a, __builtin_fmaxf(s[qb][0][r], s[qb][0][r + 1]));
+#pragma unroll
+                for (int r = 0; r < 16; r += 2) a = __builtin_fmaxf(a, __builtin_fmaxf(s[qb][1][r], s[qb][1][r + 1]));
+                const float m_new = fmaxf(m_b[qb], fmaxf(a, shfl_xor32(a)));
+                const float alpha = fast_exp2((m_b[qb] - m_new) * p.sl2);
+                m_b[qb] = m_new;
+                l0[qb] *= alpha;
+                l1[qb] *= alpha;
+#pragma unroll
+                for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) o[qb][db][r] *= alpha;
+                weights(qb);
+            }
+        }
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+            l0[qb] += tl0[qb];
+            l1[qb] += tl1[qb];
         }
         // ---- O^T += V^T P^T, four 16-key steps
 #pragma unroll
@@ -467,12 +506,22 @@ void rsa_fwd_bf16(FwdParams p) {
         return t >= ntile;
     };
     if (t < ntile) {
-        load(t, 0);
         using C0 = std::integral_constant<int, 0>;
         using C1 = std::integral_constant<int, 1>;
-        while (true) {
-            if (body(C0{})) break;
-            if (body(C1{})) break;
+        using C2 = std::integral_constant<int, 2>;
+        load(t, 0);
+        if constexpr (NBUF == 3) {
+            if (t1 < ntile) load(t1, 1);
+            while (true) {
+                if (body(C0{})) break;
+                if (body(C1{})) break;
+                if (body(C2{})) break;
+            }
+        } else {
+            while (true) {
+                if (body(C0{})) break;
+                if (body(C1{})) break;
+            }
         }
     }
 

@@ -58,6 +58,52 @@ __device__ __forceinline__ uint64_t key_tile_bits(const uint8_t* mrow, int n, in
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
+// ---- Direct HBM -> LDS copies issued from inline assembly.
+//
+// The compiler tracks copies made with __builtin_amdgcn_global_load_lds and
+// inserts a wait for them before any LDS read it cannot prove disjoint, and
+// the memory counter is in-order, so waiting for any later load (a register
+// spill, a mask byte) waits for every copy in flight too. Copies issued from
+// inline assembly are invisible to that tracking: the kernels that use them
+// wait for them explicitly with vm_wait<N>() (at most N of this wave's
+// memory loads still outstanding) before the barrier that publishes a tile.
+// The copy reads 16 (or 4) bytes at sbase + voff per lane and writes them to
+// LDS at m0 + 16 (or 4) * lane; sbase and m0 must be wave-uniform. One wait
+// state separates the write of m0 from the copy that reads it.
+
+// LDS byte address of a pointer into __shared__ memory.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+__device__ __forceinline__ void dma_copy16(const void* sbase, uint32_t voff, uint32_t lds) {
+    __asm__ volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+                     ::"v"(voff), "s"(sbase), "s"(lds) : "memory", "m0");
+}
+
+__device__ __forceinline__ void dma_copy4(const void* sbase, uint32_t voff, uint32_t lds) {
+    __asm__ volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1"
+                     ::"v"(voff), "s"(sbase), "s"(lds) : "memory", "m0");
+}
+
+// s_waitcnt vmcnt(N), leaving the other counters alone (N < 16).
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+    static_assert(N >= 0 && N < 16, "vmcnt field");
+    __builtin_amdgcn_s_waitcnt(0x0F70 | N);
+}
+
+// Workgroup barrier without the memory fence of __syncthreads() (which
+// waits for every load in flight, prefetches included). LDS visibility is
+// the caller's business (vm_wait for copies; ds reads complete before their
+// results are used). The empty asm statements keep the compiler from moving
+// memory accesses across it.
+__device__ __forceinline__ void bare_barrier() {
+    __asm__ volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    __asm__ volatile("" ::: "memory");
+}
+
 // [64 rows][D] bf16 tile copied from HBM straight into LDS with
 // global_load_lds (16 bytes per lane, no registers, no VALU): each
 // wave-instruction fills one contiguous 1 KB block, so rows are unpadded and
@@ -92,6 +138,26 @@ struct DirectTile {
             __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)src,
                                              (__attribute__((address_space(3))) void*)(lds + blk * 1024), 16, 0, 0);
         }
+    }
+
+    // Per-lane byte offsets of the untracked copy of a tile whose rows are
+    // contiguous in global memory (row pitch ROW_BYTES): row r of the tile
+    // comes from base + r * ROW_BYTES. The same for every tile.
+    __device__ __forceinline__ static void row_offsets(uint32_t (&voff)[IPW]) {
+        const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+#pragma unroll
+        for (int u = 0; u < IPW; ++u) {
+            const int r = (wave * IPW + u) * RPI + lane / CPR;
+            voff[u] = (uint32_t)(r * ROW_BYTES + 16 * ((lane % CPR) ^ swz(r)));
+        }
+    }
+
+    // Untracked copy of 64 contiguous rows starting at `base` (wave-uniform);
+    // IPW copies per wave, waited for with vm_wait.
+    __device__ __forceinline__ static void load_rows(uint8_t* lds, const uint16_t* base, const uint32_t (&voff)[IPW]) {
+        const uint32_t l0 = lds_addr(lds) + (uint32_t)(__builtin_amdgcn_readfirstlane(threadIdx.x / kWave) * IPW * 1024);
+#pragma unroll
+        for (int u = 0; u < IPW; ++u) dma_copy16(base, voff[u], l0 + (uint32_t)(u * 1024));
     }
 
     // 16-byte chunk c of row r (ds_read_b128).
