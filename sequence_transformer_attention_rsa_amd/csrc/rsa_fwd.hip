@@ -381,10 +381,14 @@ void rsa_fwd_bf16(FwdParams p) {
     auto body = [&](auto cb_c) -> bool {
         constexpr int CB = decltype(cb_c)::value;
         constexpr int FB = (CB + NBUF - 1) % NBUF;   // buffer of tile t-1, free after the barrier
-        if (NBUF == 3 && t1 < ntile)
-            vm_wait<kCopies>();   // tile t landed; the copy of t1 may stay in flight
-        else
+        if constexpr (NBUF == 3) {
+            if (t1 < ntile)
+                vm_wait<kCopies>();   // tile t landed; the copy of t1 may stay in flight
+            else
+                vm_wait<0>();
+        } else {
             vm_wait<0>();
+        }
         bare_barrier();   // every wave's part of tile t landed, tile t-1 consumed
         int tn;
         if constexpr (NBUF == 3) {
@@ -411,13 +415,18 @@ void rsa_fwd_bf16(FwdParams p) {
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-                for (int qb = 0; qb < QB; ++qb) {
+                for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
                     for (int r = 0; r < 16; ++r) s[qb][kb][r] = 0.0f;
+            // the 2 * QB accumulation chains interleaved: a dependent MFMA
+            // waits for the whole latency of its predecessor
 #pragma unroll
-                    for (int kq = 0; kq < D / 16; ++kq)
+            for (int kq = 0; kq < D / 16; ++kq)
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                    for (int qb = 0; qb < QB; ++qb)
                         s[qb][kb] = mfma_32x32x16_bf16(kf[kb][kq], qf[qb][kq], s[qb][kb]);
-                }
         }
         // ---- key mask and range tail (tiles not fully valid)
         if (!(tflag[t] & 2)) {

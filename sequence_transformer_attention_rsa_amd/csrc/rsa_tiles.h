@@ -76,6 +76,11 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
     return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
 
+// m0 is reserved to the compiler, which ignores it in a clobber list (and
+// warns); the kernels that issue these copies have no compiler-generated use
+// of m0, and none may be added to them (e.g. the builtin copy).
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
 __device__ __forceinline__ void dma_copy16(const void* sbase, uint32_t voff, uint32_t lds) {
     __asm__ volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
                      ::"v"(voff), "s"(sbase), "s"(lds) : "memory", "m0");
@@ -85,12 +90,14 @@ __device__ __forceinline__ void dma_copy4(const void* sbase, uint32_t voff, uint
     __asm__ volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1"
                      ::"v"(voff), "s"(sbase), "s"(lds) : "memory", "m0");
 }
+#pragma clang diagnostic pop
 
-// s_waitcnt vmcnt(N), leaving the other counters alone (N < 16).
+// s_waitcnt vmcnt(N), leaving the other counters alone (N < 64; the count
+// is split over bits 3:0 and 15:14 of the immediate).
 template <int N>
 __device__ __forceinline__ void vm_wait() {
-    static_assert(N >= 0 && N < 16, "vmcnt field");
-    __builtin_amdgcn_s_waitcnt(0x0F70 | N);
+    static_assert(N >= 0 && N < 64, "vmcnt field");
+    __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
 }
 
 // Workgroup barrier without the memory fence of __syncthreads() (which
