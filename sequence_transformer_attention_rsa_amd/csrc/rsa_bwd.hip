@@ -210,7 +210,10 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 3 : 1) void rsa_bwd_dq(BwdParam
         }
         const uint8_t* kb = smem + CB * BUF;
         const uint8_t* vb = kb + T::BYTES;
-        const uint64_t bits = (tflag[t] & 2) ? ~0ull : key_tile_bits(mrow, n, p.N, p.Lc, CONTIG, t * kKT, p.L);
+        // key acc_row(r, h) = 8 (r / 4) + 4 h + r % 4 of a 32-key half: after one
+        // shift by 4 h every bit position is a constant
+        const uint64_t bits =
+            (tflag[t] & 2) ? ~0ull : key_tile_bits(mrow, n, p.N, p.Lc, CONTIG, t * kKT, p.L) >> (4 * h);
         // two 32-key halves in turn, to bound the live registers
 #pragma unroll 1
         for (int kb2 = 0; kb2 < 2; ++kb2) {
@@ -235,9 +238,10 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 3 : 1) void rsa_bwd_dq(BwdParam
                 }
             }
             if (bits != ~0ull) {
+                const uint32_t hb = (uint32_t)(bits >> (32 * kb2));
 #pragma unroll
                 for (int r = 0; r < 16; ++r)
-                    if (!((bits >> (32 * kb2 + acc_row(r, h))) & 1ull)) s[r] = -INFINITY;
+                    if (!((hb >> (8 * (r >> 2) + (r & 3))) & 1u)) s[r] = -INFINITY;
             }
             uint32_t pk[8];
 #pragma unroll

@@ -266,19 +266,18 @@ __global__ __launch_bounds__(kThreads) void rsa_fwd_f32(FwdParams p) {
     }
 }
 
-// bf16 forward. Key/value tiles are copied ahead of use: with three LDS
-// buffers (d = 64) the copy of tile t+2 is issued right after the barrier
-// that opens tile t and may stay in flight until tile t+1 opens; with two
-// buffers (d = 128, where LDS allows fewer) the copy of t+1 lands during t.
-// Chunk-aligned key ranges use copies the compiler does not track (see
-// rsa_tiles.h), so nothing but the explicit vm_wait before each barrier waits
-// for them. Register use is kept low enough for three waves per SIMD at
-// d = 64 (two at d = 128): with several workgroups per CU, one wave's MFMAs
-// run while another's softmax occupies the vector ALU. (A variant that
-// overlapped the next tile's score MFMAs with this tile's softmax inside one
-// wave needed more registers, ran at fewer waves per SIMD and was slower.)
+// bf16 forward. Two LDS buffers: right after the barrier that opens tile t,
+// the copy of tile t+1 is issued into the buffer that held tile t-1 and
+// lands while tile t is computed. Chunk-aligned key ranges use copies the
+// compiler does not track (see rsa_tiles.h), so nothing but the explicit
+// vm_wait before each barrier waits for them. Registers are held to 128 so
+// that four waves run per SIMD at d = 64 (two at d = 128): with several
+// workgroups per CU, one wave's MFMAs run while another's softmax occupies
+// the vector ALU. (A variant that overlapped the next tile's score MFMAs
+// with this tile's softmax inside one wave needed more registers, ran at
+// fewer waves per SIMD and was slower; so was three buffers at three waves.)
 template <int D, bool CONTIG, int QB>
-__global__ __launch_bounds__(256 / QB, (D == 64 && QB == 1) ? 3 : 2)
+__global__ __launch_bounds__(256 / QB, (D == 64 && QB == 1) ? 4 : 2)
 void rsa_fwd_bf16(FwdParams p) {
     // QB 32-row query blocks per wave; 128 query rows per workgroup either
     // way (4 waves x 32 rows, or 2 waves x 64 rows: each K and V^T fragment
@@ -288,8 +287,7 @@ void rsa_fwd_bf16(FwdParams p) {
     using KTile = DirectTile<D, WAVES>;
     using VTile = DirectTile<D, WAVES>;
     constexpr int BUF = KTile::BYTES + VTile::BYTES;
-    constexpr int NBUF = (D == 64 && QB == 1) ? 3 : 2;
-    constexpr int kCopies = KTile::IPW + VTile::IPW;   // copies per wave and tile
+    constexpr int NBUF = 2;   // 4 x (2 x 16 KB + 4 KB) of LDS per CU at d = 64
     constexpr int ROWS = 4 * 32;
     __shared__ __attribute__((aligned(1024))) uint8_t smem[NBUF * BUF];
     __shared__ uint8_t tflag[kFwdMaxTiles];
@@ -377,29 +375,12 @@ void rsa_fwd_bf16(FwdParams p) {
     };
 
     int t = next_tile(-1);
-    int t1 = t < ntile ? next_tile(t) : ntile;
     auto body = [&](auto cb_c) -> bool {
         constexpr int CB = decltype(cb_c)::value;
-        constexpr int FB = (CB + NBUF - 1) % NBUF;   // buffer of tile t-1, free after the barrier
-        if constexpr (NBUF == 3) {
-            if (t1 < ntile)
-                vm_wait<kCopies>();   // tile t landed; the copy of t1 may stay in flight
-            else
-                vm_wait<0>();
-        } else {
-            vm_wait<0>();
-        }
+        vm_wait<0>();
         bare_barrier();   // every wave's part of tile t landed, tile t-1 consumed
-        int tn;
-        if constexpr (NBUF == 3) {
-            tn = t1;
-            const int t2 = t1 < ntile ? next_tile(t1) : ntile;
-            if (t2 < ntile) load(t2, FB);
-            t1 = t2;
-        } else {
-            tn = next_tile(t);
-            if (tn < ntile) load(tn, FB);
-        }
+        const int tn = next_tile(t);
+        if (tn < ntile) load(tn, CB ^ 1);
         const uint8_t* kbuf = smem + CB * BUF;
         const uint8_t* vbuf = kbuf + KTile::BYTES;
 
@@ -430,12 +411,15 @@ void rsa_fwd_bf16(FwdParams p) {
         }
         // ---- key mask and range tail (tiles not fully valid)
         if (!(tflag[t] & 2)) {
-            const uint64_t bits = key_tile_bits(mrow, n, p.N, p.Lc, CONTIG, vbeg + t * kKT, vend);
+            // key acc_row(r, h) = 8 (r / 4) + 4 h + r % 4 of block kb: after one
+            // shift by 4 h every bit position is a constant (no per-register
+            // masks held in registers)
+            const uint64_t bits = key_tile_bits(mrow, n, p.N, p.Lc, CONTIG, vbeg + t * kKT, vend) >> (4 * h);
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
                 for (int r = 0; r < 16; ++r)
-                    if (!((bits >> (32 * kb + acc_row(r, h))) & 1ull)) {
+                    if (!((bits >> (32 * kb + 8 * (r >> 2) + (r & 3))) & 1ull)) {
 #pragma unroll
                         for (int qb = 0; qb < QB; ++qb) s[qb][kb][r] = -INFINITY;
                     }
@@ -517,20 +501,10 @@ void rsa_fwd_bf16(FwdParams p) {
     if (t < ntile) {
         using C0 = std::integral_constant<int, 0>;
         using C1 = std::integral_constant<int, 1>;
-        using C2 = std::integral_constant<int, 2>;
         load(t, 0);
-        if constexpr (NBUF == 3) {
-            if (t1 < ntile) load(t1, 1);
-            while (true) {
-                if (body(C0{})) break;
-                if (body(C1{})) break;
-                if (body(C2{})) break;
-            }
-        } else {
-            while (true) {
-                if (body(C0{})) break;
-                if (body(C1{})) break;
-            }
+        while (true) {
+            if (body(C0{})) break;
+            if (body(C1{})) break;
         }
     }
 
