@@ -35,6 +35,8 @@ def check_grads(got, want, what):
     (200, 5, (120, 200)),    # chunks of 40: tiles straddle chunks, ragged tails
     (130, 13, (60, 130)),    # chunks of 10, 130 = one 128-row tile + 2 rows
     (64, 64, None),          # one token per chunk
+    (128, 2, (70, 128)),     # two query tiles: the copy two tiles ahead never issued
+    (192, 3, None),          # three query tiles
     (32, 8, (24, 32)),       # the finite-difference slice's shape
 ])
 def test_backward_small_parity(oracle_lib, d, L, N, valid):
@@ -121,3 +123,25 @@ def test_backward_workload_sampled_heads(oracle_lib):
         want = oracle_lib.backward(x["q"][sl], x["k"][sl], x["v"][sl], x["dout"][sl],
                                    x["mask"][b:b + 1], N=w.N)
         check_grads((dq[sl], dk[sl], dv[sl]), want, f"backward b={b} h={h}")
+
+
+def test_backward_longest_key_range():
+    """L = 262144, the longest sequence one launch covers, with key padding.
+    The oracle cannot evaluate a head this long, so the gradients are checked
+    through identities that hold at any size: the key gradients sum to zero
+    over the keys, the value gradients sum to the sum of dO over the queries,
+    and padded keys get exactly zero."""
+    dev = device()
+    L, d, N = 64 * 4096, 64, 64
+    x = inputs(1, 1, L, d, seed=45, dtype="bf16", valid_range=(L - 7000, L - 3000), with_dout=True)
+    vl = int(x["valid_len"][0])
+    say("backward longest key range, valid", vl)
+    dq, dk, dv = gpu_fwd_bwd(x, N, dev)
+    for name, g in (("dq", dq), ("dk", dk), ("dv", dv)):
+        assert np.all(np.isfinite(g)), name
+    assert np.all(dk[0, :, vl:] == 0) and np.all(dv[0, :, vl:] == 0)
+    scale_k = np.abs(dk).sum(axis=2)
+    assert np.all(np.abs(dk.sum(axis=2)) <= 2e-2 * scale_k + 1e-3)
+    gsum = x["dout"].astype(np.float64).sum(axis=2)
+    assert np.abs(dv.sum(axis=2) - gsum).max() <= 2e-2 * np.abs(gsum).max() + 0.05
+    assert np.abs(dq).max() > 0

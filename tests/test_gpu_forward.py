@@ -47,6 +47,7 @@ def check_lse(got, want, dtype, what):
     (320, 8, (1, 320)),      # very short valid lengths possible
     (130, 13, None),         # chunks of 10 keys, 130 = 2 query tiles + 2 rows
     (64, 64, None),          # one key per chunk
+    (128, 2, (90, 128)),     # two key tiles, one query tile
 ])
 def test_forward_small_parity(oracle_lib, dtype, d, L, N, valid):
     dev = device()
@@ -219,3 +220,19 @@ def test_rank_share_matches_oracle_small(oracle_lib, dtype, L, N, d):
         want, want_lse = oracle_lib.forward(x["q"][:, :, rows], x["k"], x["v"], x["mask"], N=N, qpos=rows)
         assert_parity(from_dev(out), want, dtype, f"rank {rank}")
         check_lse(lse.cpu().numpy().astype(np.float64), want_lse, dtype, f"rank {rank}")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_forward_longest_key_range(oracle_lib, d):
+    """L = 262144, the longest key range one launch covers (its tile table
+    holds 4096 tiles of 64 keys), with key padding; sampled rows of every
+    part of the sequence against the oracle."""
+    dev = device()
+    L, N = 64 * 4096, 64
+    x = inputs(1, 1, L, d, seed=40 + d, dtype="bf16", valid_range=(L - 5000, L - 1000))
+    say("forward longest key range", d, "valid", x["valid_len"])
+    out, lse = gpu_forward(x, "bf16", N, dev)
+    rows = sample_rows(L, 24, seed=41)
+    want, want_lse = oracle_lib.forward(x["q"][:, :, rows], x["k"], x["v"], x["mask"], N=N, qpos=rows)
+    assert_parity(out[0, 0, rows], want[0, 0], "bf16", f"L={L} d={d}")
+    check_lse(lse[0, 0, rows], want_lse[0, 0], "bf16", f"L={L} d={d}")
