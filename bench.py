@@ -59,6 +59,9 @@ def parse():
     ap.add_argument("--forward-variant", default="fused", choices=("fused", "twopass"),
                     help="fused online-softmax kernel, or the two-stage form with score rows in HBM "
                          "(implies --forward-only)")
+    ap.add_argument("--capacity", action="store_true",
+                    help="single-GPU sequence-length capacity of the fused and the two-stage forward "
+                         "(B=H=1, d=64) instead of the step benchmark")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (counter calibration)")
     return ap.parse_args()
@@ -139,8 +142,75 @@ def cpu_baseline(w, x, threads):
     }
 
 
+def capacity(args):
+    """Longest sequence one GPU runs in each form, B = H = 1, d = 64, bf16.
+    The fused forward needs O(L d) memory and is bounded by the key range one
+    launch covers (1048576); the two-stage form holds 4 L^2 bytes of score rows,
+    so its bound is the device memory. Each form is run once at its bound
+    (after one warm-up call) and timed with events."""
+    import torch
+
+    import sequence_transformer_attention_rsa_amd as rsa
+
+    dev = torch.device("cuda:0")
+    d = 64
+    res = {}
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1)
+
+    def tensors(L):
+        g = torch.Generator(device=dev).manual_seed(7)
+        return [torch.randn((1, 1, L, d), generator=g, device=dev).to(torch.bfloat16) for _ in range(3)]
+
+    # fused: the longest key range of one launch
+    L = 64 * 16384
+    q, k, v = tensors(L)
+    out = torch.empty_like(q)
+    ms = timed(lambda: rsa.forward(q, k, v, None, N=64, out=out))
+    res["fused"] = {"L": L, "bound": "key range of one launch (tile table)", "ms": ms,
+                    "device_bytes": 4 * L * d * 2, "tflops": 4.0 * L * L * d / ms / 1e9}
+    del q, k, v, out
+    torch.cuda.empty_cache()
+
+    # two-stage: the longest L (multiple of 1024) whose score rows fit the free memory
+    free, total = torch.cuda.mem_get_info(dev)
+    L = 1024
+    while True:
+        nxt = L + 1024
+        need = rsa.forward_twopass_workspace_bytes(1, 1, nxt, d, 1) + 4 * nxt * d * 2 + nxt * 4
+        if need > 0.85 * free:
+            break
+        L = nxt
+    q, k, v = tensors(L)
+    out = torch.empty_like(q)
+    ws = torch.empty(rsa.forward_twopass_workspace_bytes(1, 1, L, d, 1), dtype=torch.uint8, device=dev)
+    ms = timed(lambda: rsa.forward_twopass(q, k, v, None, N=1, out=out, workspace=ws))
+    res["twopass"] = {"L": L, "bound": "device memory (4 L^2 bytes of score rows)", "ms": ms,
+                      "device_bytes": ws.numel() + 4 * L * d * 2, "tflops": 4.0 * L * L * d / ms / 1e9}
+    del q, k, v, out, ws
+    torch.cuda.empty_cache()
+    line = {"metric": "single-GPU sequence-length capacity, B=H=1, d=64, bf16", "unit": "tokens",
+            "device_memory_bytes": total, "fused": res["fused"], "twopass": res["twopass"],
+            "ratio": res["fused"]["L"] / res["twopass"]["L"], "gpu": torch.cuda.get_device_name(dev)}
+    print(json.dumps(line), flush=True)
+    return 0
+
+
 def main():
     args = parse()
+    if args.capacity:
+        if args.gpus != 1:
+            print("bench.py measures one GPU only", file=sys.stderr)
+            return 2
+        return capacity(args)
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(this build has no multi-GPU path)", file=sys.stderr)

@@ -107,7 +107,7 @@ size_t rsa_forward_rank_workspace_bytes(int B, int H, int L, int d, int N);
  *   workspace  device buffer of at least rsa_forward_twopass_workspace_bytes()
  *              (4 * B * H * L * L bytes); its contents on return are
  *              unspecified
- * Only RSA_BF16, L <= 16384 and B * H <= 65535 are supported
+ * Only RSA_BF16, L <= 1048576 and B * H <= 65535 are supported
  * (RSA_ERR_UNSUPPORTED otherwise).
  */
 int rsa_forward_twopass(const void* q, const void* k, const void* v, const uint8_t* key_mask,

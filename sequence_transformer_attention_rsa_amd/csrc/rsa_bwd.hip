@@ -113,7 +113,8 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 3 : 1) void rsa_bwd_dq(BwdParam
     constexpr int NBUF = RSA_DQ_NBUF;
     constexpr int kCopies = 2 * T::IPW;   // copies per wave and tile
     __shared__ __attribute__((aligned(1024))) uint8_t smem[NBUF * BUF];
-    __shared__ uint8_t tflag[kFwdMaxTiles];
+    __shared__ uint8_t tflag_bytes[kFwdMaxTiles / 4];
+    const TileTable tflag{tflag_bytes};
 
     const int lid = xcd_remap(blockIdx.x, p.nt * p.BH);
     const int qt = lid % p.nt, bh = lid / p.nt, b = bh / p.H;
@@ -132,8 +133,7 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 3 : 1) void rsa_bwd_dq(BwdParam
     const uint8_t* mrow = p.mask ? p.mask + (size_t)b * p.L : nullptr;
     const size_t rows_all = (size_t)p.BH * p.L;
 
-    for (int t = threadIdx.x; t < ntile; t += kThreads)
-        tflag[t] = key_tile_flags(mrow, n, p.N, p.Lc, CONTIG, t * kKT, p.L);
+    tflag.build(ntile, kThreads, [&](int t) { return key_tile_flags(mrow, n, p.N, p.Lc, CONTIG, t * kKT, p.L); });
 
     u32x4 qf[D / 16], gf[D / 16];
 #pragma unroll
@@ -181,7 +181,7 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 3 : 1) void rsa_bwd_dq(BwdParam
     };
     auto next_tile = [&](int t) {
         ++t;
-        while (t < ntile && !(tflag[t] & 1)) ++t;
+        while (t < ntile && !(tflag.get(t) & 1)) ++t;
         return t;
     };
 
@@ -213,7 +213,7 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 3 : 1) void rsa_bwd_dq(BwdParam
         // key acc_row(r, h) = 8 (r / 4) + 4 h + r % 4 of a 32-key half: after one
         // shift by 4 h every bit position is a constant
         const uint64_t bits =
-            (tflag[t] & 2) ? ~0ull : key_tile_bits(mrow, n, p.N, p.Lc, CONTIG, t * kKT, p.L) >> (4 * h);
+            (tflag.get(t) & 2) ? ~0ull : key_tile_bits(mrow, n, p.N, p.Lc, CONTIG, t * kKT, p.L) >> (4 * h);
         // two 32-key halves in turn, to bound the live registers
 #pragma unroll 1
         for (int kb2 = 0; kb2 < 2; ++kb2) {

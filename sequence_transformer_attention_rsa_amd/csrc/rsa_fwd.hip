@@ -86,7 +86,8 @@ template <int D>
 __global__ __launch_bounds__(kThreads) void rsa_fwd_f32(FwdParams p) {
     using C = F32Cfg<D>;
     __shared__ __attribute__((aligned(16))) float smem[2 * C::BUF];
-    __shared__ uint8_t tflag[kFwdMaxTiles];
+    __shared__ uint8_t tflag_bytes[kFwdMaxTiles / 4];
+    const TileTable tflag{tflag_bytes};
 
     const int total = p.nqt * p.BH * p.groups;
     const int lid = xcd_remap(blockIdx.x, total);
@@ -115,8 +116,7 @@ __global__ __launch_bounds__(kThreads) void rsa_fwd_f32(FwdParams p) {
     if (ntile > kFwdMaxTiles) return;   // the host never launches such a range
     const bool contig = p.contiguous != 0;
 
-    for (int t = threadIdx.x; t < ntile; t += kThreads)
-        tflag[t] = key_tile_flags(mrow, n, p.N, p.Lc, contig, vbeg + t * kKT, vend);
+    tflag.build(ntile, kThreads, [&](int t) { return key_tile_flags(mrow, n, p.N, p.Lc, contig, vbeg + t * kKT, vend); });
 
     // Q^T fragments (B operand of S^T = K Q^T): lane (j, h) holds Q[row][2 ks + h]
     float qf[D / 2];
@@ -167,7 +167,7 @@ __global__ __launch_bounds__(kThreads) void rsa_fwd_f32(FwdParams p) {
     };
 
     int t = 0;
-    while (t < ntile && !(tflag[t] & 1)) ++t;
+    while (t < ntile && !(tflag.get(t) & 1)) ++t;
     int buf = 0;
     if (t < ntile) {
         load(t);
@@ -175,7 +175,7 @@ __global__ __launch_bounds__(kThreads) void rsa_fwd_f32(FwdParams p) {
     }
     while (t < ntile) {
         int tn = t + 1;
-        while (tn < ntile && !(tflag[tn] & 1)) ++tn;
+        while (tn < ntile && !(tflag.get(tn) & 1)) ++tn;
         if (tn < ntile) load(tn);
         __syncthreads();   // buffer `buf` complete; the other one is free
 
@@ -191,7 +191,7 @@ __global__ __launch_bounds__(kThreads) void rsa_fwd_f32(FwdParams p) {
 #pragma unroll
             for (int kq = 0; kq < D / 2; ++kq) s[kb] = mfma_32x32x2_f32(ks_[(32 * kb + j) * C::KP + 2 * kq + h], qf[kq], s[kb]);
         }
-        if (!(tflag[t] & 2)) {
+        if (!(tflag.get(t) & 2)) {
             const uint64_t bits = key_tile_bits(mrow, n, p.N, p.Lc, contig, v0, vend);
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
@@ -290,7 +290,8 @@ void rsa_fwd_bf16(FwdParams p) {
     constexpr int NBUF = 2;   // 4 x (2 x 16 KB + 4 KB) of LDS per CU at d = 64
     constexpr int ROWS = 4 * 32;
     __shared__ __attribute__((aligned(1024))) uint8_t smem[NBUF * BUF];
-    __shared__ uint8_t tflag[kFwdMaxTiles];
+    __shared__ uint8_t tflag_bytes[kFwdMaxTiles / 4];
+    const TileTable tflag{tflag_bytes};
 
     const int total = p.nqt * p.BH * p.groups;
     const int lid = xcd_remap(blockIdx.x, total);
@@ -317,8 +318,7 @@ void rsa_fwd_bf16(FwdParams p) {
     const uint8_t* mrow = p.mask ? p.mask + (size_t)b * p.L : nullptr;
     if (ntile > kFwdMaxTiles) return;   // the host never launches such a range
 
-    for (int t = threadIdx.x; t < ntile; t += NTH)
-        tflag[t] = key_tile_flags(mrow, n, p.N, p.Lc, CONTIG, vbeg + t * kKT, vend);
+    tflag.build(ntile, NTH, [&](int t) { return key_tile_flags(mrow, n, p.N, p.Lc, CONTIG, vbeg + t * kKT, vend); });
 
     u32x4 qf[QB][D / 16];
 #pragma unroll
@@ -370,7 +370,7 @@ void rsa_fwd_bf16(FwdParams p) {
     };
     auto next_tile = [&](int t) {
         ++t;
-        while (t < ntile && !(tflag[t] & 1)) ++t;
+        while (t < ntile && !(tflag.get(t) & 1)) ++t;
         return t;
     };
 
@@ -410,7 +410,7 @@ void rsa_fwd_bf16(FwdParams p) {
                         s[qb][kb] = mfma_32x32x16_bf16(kf[kb][kq], qf[qb][kq], s[qb][kb]);
         }
         // ---- key mask and range tail (tiles not fully valid)
-        if (!(tflag[t] & 2)) {
+        if (!(tflag.get(t) & 2)) {
             // key acc_row(r, h) = 8 (r / 4) + 4 h + r % 4 of block kb: after one
             // shift by 4 h every bit position is a constant (no per-register
             // masks held in registers)

@@ -9,9 +9,10 @@
 namespace rsa {
 
 // Keys per tile of the forward kernels, and the most tiles one workgroup's
-// key range may hold (the tile-occupancy table lives in LDS).
+// key range may hold (the tile-occupancy table lives in LDS, two bits per
+// tile: 4 KB for 16384 tiles = 1048576 keys).
 constexpr int kFwdKeyTile = 64;
-constexpr int kFwdMaxTiles = 4096;
+constexpr int kFwdMaxTiles = 16384;
 
 struct ForwardCall {
     const void* q;          // [B,H,Lq,d]
@@ -38,9 +39,9 @@ hipError_t launch_forward(const ForwardCall& c, hipStream_t stream);
 
 // Two-stage forward with the score rows materialised: fp32 scores
 // [B,H,L,L] in `part` (rewritten in place as bf16 weights), then P V. The
-// softmax pass holds a row in the registers of one workgroup (64 values per
-// thread at most), which bounds L.
-constexpr int kTwoPassMaxL = 16384;
+// softmax pass holds a row in one workgroup's registers up to 16384 keys and
+// makes two passes over longer rows; the workspace bounds L in practice.
+constexpr int kTwoPassMaxL = kFwdKeyTile * kFwdMaxTiles;
 size_t twopass_workspace_bytes(int B, int H, int L);
 hipError_t launch_forward_twopass(const ForwardCall& c, hipStream_t stream);
 

@@ -45,6 +45,26 @@ __device__ __forceinline__ uint8_t key_tile_flags(const uint8_t* mrow, int n, in
     return (any ? 1 : 0) | (all ? 2 : 0);
 }
 
+// Occupancy table of a workgroup's key tiles in LDS: the two bits of
+// key_tile_flags per tile, four tiles per byte. build() is called by all
+// `nthreads` threads and must be followed by a barrier before get().
+struct TileTable {
+    uint8_t* bytes;
+
+    __device__ __forceinline__ uint32_t get(int t) const { return (bytes[t >> 2] >> (2 * (t & 3))) & 3u; }
+
+    template <class Flags>
+    __device__ __forceinline__ void build(int ntile, int nthreads, Flags flags) const {
+        for (int i = threadIdx.x; 4 * i < ntile; i += nthreads) {
+            uint32_t b = 0;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (4 * i + e < ntile) b |= (uint32_t)flags(4 * i + e) << (2 * e);
+            bytes[i] = (uint8_t)b;
+        }
+    }
+};
+
 // Valid-key bits of a 64-key tile in ring order (lane i <-> key v0 + i).
 __device__ __forceinline__ uint64_t key_tile_bits(const uint8_t* mrow, int n, int N, int Lc, bool contiguous,
                                                   int v0, int vend) {

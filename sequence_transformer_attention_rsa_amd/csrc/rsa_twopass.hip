@@ -121,6 +121,61 @@ __global__ __launch_bounds__(kThreads) void rsa_2p_softmax(float* __restrict__ S
     if (threadIdx.x == 0 && lse) lse[ri] = l > 0.0f ? (base + __log2f(l)) * (1.0f / kLog2e) : -INFINITY;
 }
 
+// Rows longer than the register-held kernel covers: one workgroup per row,
+// two passes over it in chunks of 512 elements. Pass 1 keeps a running
+// (maximum, sum of exp2) per thread, merged across the workgroup; pass 2
+// writes the bf16 weights in place. Chunk c's weights land on fp32 elements
+// [256 c, 256 c + 256), which lie in chunks already read; a barrier per chunk
+// keeps a lagging thread's reads ahead of every overwrite.
+__global__ __launch_bounds__(kThreads) void rsa_2p_softmax_long(float* __restrict__ S, float* __restrict__ lse,
+                                                                int L, float sl2) {
+    __shared__ float red_m[kThreads / kWave], red_s[kThreads / kWave];
+    const size_t ri = blockIdx.x;
+    float* row = S + ri * (size_t)L;
+    // running maximum (raw units) and sum of exp2((v - m) * sl2)
+    float m = -INFINITY, sum = 0.0f;
+    for (int x = threadIdx.x; x < L; x += kThreads) {
+        const float v = row[x];
+        if (v > m) {
+            sum = (m == -INFINITY ? 0.0f : sum * fast_exp2((m - v) * sl2)) + 1.0f;
+            m = v;
+        } else if (v != -INFINITY) {
+            sum += fast_exp2((v - m) * sl2);
+        }
+    }
+    auto merge = [&](float om, float os) {
+        const float nm = fmaxf(m, om);
+        if (nm == -INFINITY) return;
+        sum = (m == -INFINITY ? 0.0f : sum * fast_exp2((m - nm) * sl2)) +
+              (om == -INFINITY ? 0.0f : os * fast_exp2((om - nm) * sl2));
+        m = nm;
+    };
+    for (int off = kWave / 2; off > 0; off >>= 1) {
+        const float om = __shfl_xor(m, off), os = __shfl_xor(sum, off);
+        merge(om, os);
+    }
+    if (threadIdx.x % kWave == 0) {
+        red_m[threadIdx.x / kWave] = m;
+        red_s[threadIdx.x / kWave] = sum;
+    }
+    __syncthreads();
+    m = red_m[0];
+    sum = red_s[0];
+    for (int w = 1; w < kThreads / kWave; ++w) merge(red_m[w], red_s[w]);
+    const float base = m == -INFINITY ? 0.0f : m * sl2;
+    const float inv = sum > 0.0f ? 1.0f / sum : 0.0f;
+    uint32_t* prow = reinterpret_cast<uint32_t*>(row);
+    for (int c0 = 0; c0 < L; c0 += 2 * kThreads) {
+        const int x = c0 + 2 * (int)threadIdx.x;
+        const float v0 = x < L ? row[x] : -INFINITY;
+        const float v1 = x + 1 < L ? row[x + 1] : -INFINITY;
+        __syncthreads();   // every thread's reads of this chunk precede the writes below
+        if (x < L) prow[x / 2] = pack_bf16x2(fast_exp2(fmaf(v0, sl2, -base)) * inv, fast_exp2(fmaf(v1, sl2, -base)) * inv);
+        __syncthreads();   // writes land before a lagging thread reads the next chunk
+    }
+    if (threadIdx.x == 0 && lse) lse[ri] = sum > 0.0f ? (base + __log2f(sum)) * (1.0f / kLog2e) : -INFINITY;
+}
+
 // O^T = V^T P^T for 128 queries (4 waves x 32, lane <-> query), keys in
 // 64-row tiles: V through LDS (transposing read, keys in sequence), P
 // straight from the materialised rows (pitch 4L bytes): lane half h loads
@@ -199,7 +254,8 @@ hipError_t launch_t(const ForwardCall& c, hipStream_t stream) {
     else if (pairs <= 4) hipLaunchKernelGGL(rsa_2p_softmax<4>, rows, dim3(kThreads), 0, stream, S, c.lse, c.L, sl2);
     else if (pairs <= 8) hipLaunchKernelGGL(rsa_2p_softmax<8>, rows, dim3(kThreads), 0, stream, S, c.lse, c.L, sl2);
     else if (pairs <= 16) hipLaunchKernelGGL(rsa_2p_softmax<16>, rows, dim3(kThreads), 0, stream, S, c.lse, c.L, sl2);
-    else hipLaunchKernelGGL(rsa_2p_softmax<32>, rows, dim3(kThreads), 0, stream, S, c.lse, c.L, sl2);
+    else if (pairs <= 32) hipLaunchKernelGGL(rsa_2p_softmax<32>, rows, dim3(kThreads), 0, stream, S, c.lse, c.L, sl2);
+    else hipLaunchKernelGGL(rsa_2p_softmax_long, rows, dim3(kThreads), 0, stream, S, c.lse, c.L, sl2);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((rsa_2p_pv<D>), dim3((unsigned)(BH * nt)), dim3(kThreads), 0, stream, S,

@@ -61,7 +61,7 @@ def test_forward_validation(lib):
     assert fwd(lib, d=32) == EUNSUP
     assert fwd(lib, d=96) == EUNSUP
     assert fwd(lib, dtype=7) == EUNSUP
-    assert fwd(lib, L=64 * 4096 * 2, N=1) == EUNSUP   # longer than one launch's tile table
+    assert fwd(lib, L=64 * 16384 * 2, N=1) == EUNSUP   # longer than one launch's tile table
     assert fwd(lib, q=P + 8) == EALIGN
     assert fwd(lib, out=P + 4) == EALIGN
     assert fwd(lib, mask=P + 1) == EALIGN
@@ -118,7 +118,7 @@ def test_forward_twopass_validation(lib):
     assert call(L_=L - 1) == ESHAPE
     assert call(d_=96) == EUNSUP
     assert call(dtype=F32) == EUNSUP
-    assert call(L_=32768, N_=1, ws_bytes=1 << 62) == EUNSUP   # a row must fit one workgroup's registers
+    assert call(L_=64 * 16384 * 2, N_=1, ws_bytes=1 << 62) == EUNSUP   # longer than one launch covers
     assert call(B_=65536, H_=1, L_=16, N_=1, ws_bytes=1 << 62) == EUNSUP
     assert call(ws_ptr=None) == EWS
     assert call(ws_bytes=ws - 1) == EWS

@@ -126,13 +126,13 @@ def test_backward_workload_sampled_heads(oracle_lib):
 
 
 def test_backward_longest_key_range():
-    """L = 262144, the longest sequence one launch covers, with key padding.
+    """L = 1048576, the longest sequence one launch covers, with key padding.
     The oracle cannot evaluate a head this long, so the gradients are checked
     through identities that hold at any size: the key gradients sum to zero
     over the keys, the value gradients sum to the sum of dO over the queries,
     and padded keys get exactly zero."""
     dev = device()
-    L, d, N = 64 * 4096, 64, 64
+    L, d, N = 64 * 16384, 64, 64
     x = inputs(1, 1, L, d, seed=45, dtype="bf16", valid_range=(L - 7000, L - 3000), with_dout=True)
     vl = int(x["valid_len"][0])
     say("backward longest key range, valid", vl)

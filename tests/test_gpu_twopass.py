@@ -129,14 +129,18 @@ def test_twopass_long_sequence_sampled_rows(oracle_lib):
         check_lse(lse[b, h, rows], want_lse[0, 0], "twopass long_seq")
 
 
-def test_twopass_longest_row(oracle_lib):
-    """L = 16384, the longest row the softmax pass holds in registers."""
+@pytest.mark.parametrize("L,N,valid", [
+    (16384, 16, (12000, 16384)),   # the longest row the softmax pass holds in registers
+    (16896, 16, (16500, 16896)),   # the shortest row of the two-pass-per-row kernel
+    (17000, 17, (9000, 17000)),    # a row that ends inside a 512-element chunk
+    (65536, 64, None),             # 16 GiB of score rows
+])
+def test_twopass_long_rows(oracle_lib, L, N, valid):
     dev = device()
-    L, d, N = 16384, 64, 16
-    x = inputs(1, 1, L, d, seed=34, dtype="bf16", valid_range=(12000, 16384))
-    say("twopass longest row")
+    x = inputs(1, 1, L, 64, seed=34 + L % 97, dtype="bf16", valid_range=valid)
+    say("twopass long rows", L, N, valid)
     out, lse = run(x, N, dev)
-    rows = sample_rows(L, 96, seed=34)
+    rows = sample_rows(L, 64, seed=34)
     want, want_lse = oracle_lib.forward(x["q"][:, :, rows], x["k"], x["v"], x["mask"], N=N, qpos=rows)
-    assert_parity(out[0, 0, rows], want[0, 0], "bf16", "twopass L=16384")
-    check_lse(lse[0, 0, rows], want_lse[0, 0], "twopass L=16384")
+    assert_parity(out[0, 0, rows], want[0, 0], "bf16", f"twopass L={L}")
+    check_lse(lse[0, 0, rows], want_lse[0, 0], f"twopass L={L}")
