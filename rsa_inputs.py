@@ -37,6 +37,9 @@ __all__ = [
     "WORKLOADS",
     "make_inputs",
     "prefix_mask",
+    "LayerShape",
+    "LAYERS",
+    "make_layer_inputs",
 ]
 
 
@@ -169,3 +172,93 @@ def workload_inputs(w: Workload) -> dict:
     """Inputs of a named workload, following the module's recipe."""
     return make_inputs(w.B, w.H, w.L, w.d, w.seed, w.dtype, w.scale, w.valid_range,
                        Lq=w.Lq, with_dout=w.backward)
+
+
+# ---------------------------------------------------------------------------
+# The sequence-parallel layer around RSA: the token-local steps on either side
+# of the attention (QKV projection, output projection, two fully connected
+# layers with GeLU, residual sums and layer normalisation). Inputs are a
+# hidden-state tensor x [B, L, E] and random-initialised weights in the
+# shapes of a BERT-style encoder layer (E = H * d, F = 4 E):
+#   w_qkv [3E, E], b_qkv [3E]   rows 0..E-1 give Q, E..2E-1 K, 2E..3E-1 V,
+#                               head h owning rows h*d .. h*d + d - 1 of each
+#   w_o   [E, E],  b_o   [E]
+#   ln1_gamma, ln1_beta [E]
+#   w_ff1 [F, E],  b_ff1 [F]
+#   w_ff2 [E, F],  b_ff2 [E]
+#   ln2_gamma, ln2_beta [E]
+# Recipe: generator PCG64(seed); standard-normal fp64 draws in the order x,
+# w_qkv, b_qkv, w_o, b_o, ln1_gamma, ln1_beta, w_ff1, b_ff1, w_ff2, b_ff2,
+# ln2_gamma, ln2_beta; x is N(0,1), weight matrices and biases N(0,1) * 0.02,
+# gammas 1 + N(0,1) * 0.1, betas N(0,1) * 0.1; matrices and x are rounded to
+# bf16 (fp32 holders), vectors stay fp32. Then the valid lengths, as for
+# make_inputs.
+
+
+@dataclasses.dataclass(frozen=True)
+class LayerShape:
+    """One named layer workload: B, L, hidden size E, heads H, FFN width F, N."""
+
+    name: str
+    B: int
+    L: int
+    E: int
+    H: int
+    F: int
+    N: int
+    seed: int
+    valid_range: Optional[Tuple[int, int]] = None
+    description: str = ""
+
+    @property
+    def d(self) -> int:
+        return self.E // self.H
+
+
+LAYERS = {
+    "layer_bert_base": LayerShape(
+        "layer_bert_base", B=8, L=512, E=768, H=12, F=3072, N=4, seed=12, valid_range=(384, 512),
+        description="BERT-Base-shaped layer, B=8 L=512 E=768 H=12 F=3072, N=4, key padding"),
+    "layer_long_seq": LayerShape(
+        "layer_long_seq", B=2, L=8192, E=768, H=12, F=3072, N=16, seed=13,
+        description="long-sequence layer, B=2 L=8192 E=768 H=12 (d=64) F=3072, N=16, no mask"),
+}
+
+
+def make_layer_inputs(B: int, L: int, E: int, H: int, F: int, seed: int,
+                      valid_range: Optional[Tuple[int, int]] = None) -> dict:
+    """Draw the layer's input x and weights following the recipe above."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+
+    def mat(shape, scale):
+        return bf16_round((rng.standard_normal(shape) * scale).astype(np.float32))
+
+    def vec(n, scale, offset=0.0):
+        return (offset + rng.standard_normal(n) * scale).astype(np.float32)
+
+    out = {"x": mat((B, L, E), 1.0)}
+    out["w_qkv"] = mat((3 * E, E), 0.02)
+    out["b_qkv"] = vec(3 * E, 0.02)
+    out["w_o"] = mat((E, E), 0.02)
+    out["b_o"] = vec(E, 0.02)
+    out["ln1_gamma"] = vec(E, 0.1, 1.0)
+    out["ln1_beta"] = vec(E, 0.1)
+    out["w_ff1"] = mat((F, E), 0.02)
+    out["b_ff1"] = vec(F, 0.02)
+    out["w_ff2"] = mat((E, F), 0.02)
+    out["b_ff2"] = vec(E, 0.02)
+    out["ln2_gamma"] = vec(E, 0.1, 1.0)
+    out["ln2_beta"] = vec(E, 0.1)
+    if valid_range is not None:
+        lo, hi = valid_range
+        out["valid_len"] = rng.integers(lo, hi + 1, size=B)
+        out["mask"] = prefix_mask(out["valid_len"], L)
+    else:
+        out["valid_len"] = None
+        out["mask"] = None
+    return out
+
+
+def layer_inputs(w: LayerShape) -> dict:
+    """Inputs of a named layer workload."""
+    return make_layer_inputs(w.B, w.L, w.E, w.H, w.F, w.seed, w.valid_range)
