@@ -164,6 +164,92 @@ int rsa_backward_dkdv(const void* q, const void* k, const void* v, const void* d
                       const uint8_t* key_mask, int B, int H, int L, int d, int N, int dtype,
                       void* stream, void* dk, void* dv);
 
+/*
+ * ---- The sequence-parallel layer around RSA -------------------------------
+ * Review page, ABSTRACT: RSA sits inside a Transformer whose sequence is split
+ * into chunks, one per device; every other step of the layer acts on one
+ * token at a time and so runs on a chunk with no exchange. The tensor-
+ * parallelism page ("一文捋順千億模型訓練技術", section 二, 1D tensor
+ * parallelism, parts (2) and (3)) describes those steps: two fully connected
+ * layers with GeLU between them, and attention heads that are independent.
+ * Residual sums and post-normalisation follow BERT's encoder layer (the
+ * pages' workloads are BERT-shaped; the pages do not print the layer).
+ *
+ * Conventions of these entry points: matrices and activations are bf16,
+ * biases, gamma and beta fp32; products accumulate in fp32 and each result
+ * is rounded once to bf16 (nearest even). A weight matrix w [N,K] maps K
+ * inputs to N outputs (out = in w^T), the layout of a PyTorch Linear weight.
+ * Widths: N % 128 == 0 and K % 64 == 0 for products (RSA_ERR_UNSUPPORTED
+ * otherwise); the hidden size E = H*d with d in {64, 128} and E % 128 == 0.
+ * Pointers are device memory owned by the caller, 16-byte aligned (NULL
+ * allowed where stated); validation, streams and errors as above.
+ */
+
+/*
+ * out[M,N] = act(a[M,K] w[N,K]^T + bias[N]) + residual[M,N]
+ *   activation  0: none, 1: GeLU (exact erf form) applied before the residual
+ *   bias, residual  may be NULL
+ */
+int rsa_linear(const void* a, const void* w, const float* bias, const void* residual, int M, int N, int K,
+               int activation, void* stream, void* out);
+
+/*
+ * Q, K, V [B,H,L,d] from x [B,L,E]: t = x w_qkv^T + b_qkv, w_qkv [3E,E];
+ * columns [0,E) of t give Q, [E,2E) K, [2E,3E) V, and head h takes columns
+ * h*d .. h*d+d-1 of each (the head split is fused into the product's store).
+ * b_qkv [3E] may be NULL.
+ */
+int rsa_qkv_projection(const void* x, const void* w_qkv, const float* b_qkv, int B, int L, int E, int H,
+                       void* stream, void* q, void* k, void* v);
+
+/*
+ * out[B,L,E] = merge(o) w_o^T + b_o + residual, where merge reads the
+ * attention output o [B,H,L,d] as [B,L,H*d] (fused into the product's
+ * operand load). b_o and residual may be NULL.
+ */
+int rsa_output_projection(const void* o, const void* w_o, const float* b_o, const void* residual, int B, int L,
+                          int E, int H, void* stream, void* out);
+
+/*
+ * y = (x - mean) / sqrt(var + eps) * gamma + beta over each row of x
+ * [rows, E] (var the population variance, statistics in fp32);
+ * E % 8 == 0 and E <= 4096.
+ */
+int rsa_layernorm(const void* x, const float* gamma, const float* beta, int rows, int E, float eps, void* stream,
+                  void* y);
+
+/* The layer's weights (device pointers): matrices bf16, vectors fp32. */
+typedef struct rsa_layer_weights {
+    const void* w_qkv;          /* [3E, E] */
+    const float* b_qkv;         /* [3E] or NULL */
+    const void* w_o;            /* [E, E] */
+    const float* b_o;           /* [E] or NULL */
+    const float* ln1_gamma;     /* [E] */
+    const float* ln1_beta;      /* [E] */
+    const void* w_ff1;          /* [F, E] */
+    const float* b_ff1;         /* [F] or NULL */
+    const void* w_ff2;          /* [E, F] */
+    const float* b_ff2;         /* [E] or NULL */
+    const float* ln2_gamma;     /* [E] */
+    const float* ln2_beta;      /* [E] */
+} rsa_layer_weights;
+
+/*
+ * One encoder layer over the whole sequence (every chunk), RSA as its
+ * attention:
+ *   Q,K,V = split(x w_qkv^T + b_qkv);  O = RSA(Q, K, V, key_mask, N)
+ *   A1 = merge(O) w_o^T + b_o + x;     h1 = LayerNorm(A1; ln1)
+ *   F1 = GeLU(h1 w_ff1^T + b_ff1);     A2 = F1 w_ff2^T + b_ff2 + h1
+ *   y  = LayerNorm(A2; ln2)            (eps = 1e-12)
+ *   x, y       [B,L,E] bf16; key_mask as rsa_forward; F % 128 == 0
+ *   workspace  at least rsa_layer_forward_workspace_bytes() (intermediates)
+ */
+int rsa_layer_forward(const void* x, const uint8_t* key_mask, const rsa_layer_weights* w, int B, int L, int E,
+                      int H, int F, int N, void* workspace, size_t workspace_bytes, void* stream, void* y);
+
+/* Workspace bytes rsa_layer_forward needs (0 if the sizes are invalid). */
+size_t rsa_layer_forward_workspace_bytes(int B, int L, int E, int H, int F, int N);
+
 /* A static, human-readable name for a status code. */
 const char* rsa_status_string(int status);
 

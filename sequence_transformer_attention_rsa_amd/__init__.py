@@ -11,6 +11,7 @@ the library is not built, every call raises.
     out_local = rsa.forward_rank(q_local, k, v, N=64, rank=3)
     out = rsa.forward_twopass(q, k, v, N=4)      # score rows materialised
     dq, dk, dv = rsa.backward(q, k, v, out, dout, lse, N=8)
+    y = rsa.layer_forward(x, weights, H=12, N=16)  # the encoder layer around RSA
 
 Shapes: q, k, v, out, dout: [B, H, L, d] contiguous (q_local and out_local:
 [B, H, L/N, d]); key_mask: [B, L] bool or uint8 (nonzero = valid key);
@@ -29,7 +30,8 @@ __all__ = [
     "RSAError", "lib_path", "load", "forward", "forward_rank", "forward_twopass", "backward",
     "backward_preprocess", "backward_dq", "backward_dkdv",
     "forward_rank_workspace_bytes", "forward_twopass_workspace_bytes", "backward_workspace_bytes",
-    "status_string",
+    "status_string", "linear", "qkv_projection", "output_projection", "layernorm", "layer_forward",
+    "layer_forward_workspace_bytes", "LAYER_WEIGHTS",
     "RSA_F32", "RSA_BF16",
 ]
 
@@ -57,8 +59,22 @@ SIGNATURES = {
     "rsa_backward_preprocess": (_ci, [_vp, _vp, _vp, _ci, _ci, _ci, _ci, _ci, _vp, _vp]),
     "rsa_backward_dq": (_ci, [_vp, _vp, _vp, _vp, _vp, _vp, _ci, _ci, _ci, _ci, _ci, _ci, _vp, _vp]),
     "rsa_backward_dkdv": (_ci, [_vp, _vp, _vp, _vp, _vp, _vp, _ci, _ci, _ci, _ci, _ci, _ci, _vp, _vp, _vp]),
+    "rsa_linear": (_ci, [_vp, _vp, _vp, _vp, _ci, _ci, _ci, _ci, _vp, _vp]),
+    "rsa_qkv_projection": (_ci, [_vp, _vp, _vp, _ci, _ci, _ci, _ci, _vp, _vp, _vp, _vp]),
+    "rsa_output_projection": (_ci, [_vp, _vp, _vp, _vp, _ci, _ci, _ci, _ci, _vp, _vp]),
+    "rsa_layernorm": (_ci, [_vp, _vp, _vp, _ci, _ci, ctypes.c_float, _vp, _vp]),
+    "rsa_layer_forward": (_ci, [_vp, _vp, _vp, _ci, _ci, _ci, _ci, _ci, _ci, _vp, _sz, _vp, _vp]),
+    "rsa_layer_forward_workspace_bytes": (_sz, [_ci, _ci, _ci, _ci, _ci, _ci]),
     "rsa_status_string": (ctypes.c_char_p, [_ci]),
 }
+
+# Field order of struct rsa_layer_weights (matrices bf16, vectors fp32).
+LAYER_WEIGHTS = ("w_qkv", "b_qkv", "w_o", "b_o", "ln1_gamma", "ln1_beta",
+                 "w_ff1", "b_ff1", "w_ff2", "b_ff2", "ln2_gamma", "ln2_beta")
+
+
+class _LayerWeights(ctypes.Structure):
+    _fields_ = [(name, ctypes.c_void_p) for name in LAYER_WEIGHTS]
 
 
 class RSAError(RuntimeError):
@@ -300,3 +316,122 @@ def backward(q, k, v, out, dout, lse, key_mask=None, N: int = 1, dq=None, dk=Non
     if st != 0:
         raise RSAError(st, "rsa_backward")
     return dq, dk, dv
+
+
+# ------------------------------------------------ the layer around RSA ---
+
+def _bf16(t, name, shape, device):
+    _need(t, name, shape, torch.bfloat16, device)
+
+
+def _vec(t, name, n, device, optional=True):
+    if t is None and optional:
+        return None
+    _need(t, name, (n,), torch.float32, device)
+    return t
+
+
+def linear(a, w, bias=None, residual=None, activation: str = "none", out=None):
+    """out = act(a w^T + bias) + residual; a [M,K], w [N,K] bf16, bias [N] fp32;
+    activation "none" or "gelu" (applied before the residual)."""
+    M, K = a.shape
+    N = w.shape[0]
+    dev = a.device
+    _bf16(a, "a", (M, K), dev)
+    _bf16(w, "w", (N, K), dev)
+    _vec(bias, "bias", N, dev)
+    if residual is not None:
+        _bf16(residual, "residual", (M, N), dev)
+    act = {"none": 0, "gelu": 1}[activation]
+    out = torch.empty((M, N), dtype=torch.bfloat16, device=dev) if out is None else out
+    _bf16(out, "out", (M, N), dev)
+    st = load().rsa_linear(_ptr(a), _ptr(w), _ptr(bias), _ptr(residual), M, N, K, act, _stream(dev), _ptr(out))
+    if st != 0:
+        raise RSAError(st, "rsa_linear")
+    return out
+
+
+def qkv_projection(x, w_qkv, b_qkv, H: int):
+    """Q, K, V [B,H,L,d] from x [B,L,E] (head split fused into the product)."""
+    B, L, E = x.shape
+    dev = x.device
+    _bf16(x, "x", (B, L, E), dev)
+    _bf16(w_qkv, "w_qkv", (3 * E, E), dev)
+    _vec(b_qkv, "b_qkv", 3 * E, dev)
+    if E % H != 0:
+        raise ValueError("H must divide E")
+    q, k, v = (torch.empty((B, H, L, E // H), dtype=torch.bfloat16, device=dev) for _ in range(3))
+    st = load().rsa_qkv_projection(_ptr(x), _ptr(w_qkv), _ptr(b_qkv), B, L, E, H, _stream(dev),
+                                   _ptr(q), _ptr(k), _ptr(v))
+    if st != 0:
+        raise RSAError(st, "rsa_qkv_projection")
+    return q, k, v
+
+
+def output_projection(o, w_o, b_o=None, residual=None):
+    """merge(o) w_o^T + b_o + residual, o [B,H,L,d] -> [B,L,E]."""
+    B, H, L, d = o.shape
+    E = H * d
+    dev = o.device
+    _bf16(o, "o", (B, H, L, d), dev)
+    _bf16(w_o, "w_o", (E, E), dev)
+    _vec(b_o, "b_o", E, dev)
+    if residual is not None:
+        _bf16(residual, "residual", (B, L, E), dev)
+    out = torch.empty((B, L, E), dtype=torch.bfloat16, device=dev)
+    st = load().rsa_output_projection(_ptr(o), _ptr(w_o), _ptr(b_o), _ptr(residual), B, L, E, H, _stream(dev),
+                                      _ptr(out))
+    if st != 0:
+        raise RSAError(st, "rsa_output_projection")
+    return out
+
+
+def layernorm(x, gamma, beta, eps: float = 1e-12):
+    """Layer normalisation over the last axis of a bf16 tensor."""
+    E = x.shape[-1]
+    rows = x.numel() // E
+    dev = x.device
+    _bf16(x, "x", tuple(x.shape), dev)
+    _vec(gamma, "gamma", E, dev, optional=False)
+    _vec(beta, "beta", E, dev, optional=False)
+    y = torch.empty_like(x)
+    st = load().rsa_layernorm(_ptr(x), _ptr(gamma), _ptr(beta), rows, E, float(eps), _stream(dev), _ptr(y))
+    if st != 0:
+        raise RSAError(st, "rsa_layernorm")
+    return y
+
+
+def layer_forward_workspace_bytes(B: int, L: int, E: int, H: int, F: int, N: int) -> int:
+    return int(load().rsa_layer_forward_workspace_bytes(B, L, E, H, F, N))
+
+
+def layer_forward(x, weights: dict, H: int, N: int = 1, key_mask=None, out=None, workspace=None):
+    """The encoder layer around RSA: x [B,L,E] bf16 -> y [B,L,E] bf16.
+
+    weights: dict with the LAYER_WEIGHTS names; matrices bf16 (w_qkv [3E,E],
+    w_o [E,E], w_ff1 [F,E], w_ff2 [E,F]), vectors fp32 (biases may be None).
+    """
+    B, L, E = x.shape
+    dev = x.device
+    _bf16(x, "x", (B, L, E), dev)
+    F = weights["w_ff1"].shape[0]
+    _bf16(weights["w_qkv"], "w_qkv", (3 * E, E), dev)
+    _bf16(weights["w_o"], "w_o", (E, E), dev)
+    _bf16(weights["w_ff1"], "w_ff1", (F, E), dev)
+    _bf16(weights["w_ff2"], "w_ff2", (E, F), dev)
+    for name, n in (("b_qkv", 3 * E), ("b_o", E), ("b_ff1", F), ("b_ff2", E)):
+        _vec(weights.get(name), name, n, dev)
+    for name in ("ln1_gamma", "ln1_beta", "ln2_gamma", "ln2_beta"):
+        _vec(weights[name], name, E, dev, optional=False)
+    m = _mask(key_mask, B, L, dev)
+    ws = _LayerWeights(*[None if weights.get(n) is None else weights[n].data_ptr() for n in LAYER_WEIGHTS])
+    y = torch.empty_like(x) if out is None else out
+    _bf16(y, "out", (B, L, E), dev)
+    if workspace is None:
+        need = layer_forward_workspace_bytes(B, L, E, H, F, N)
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    st = load().rsa_layer_forward(_ptr(x), _ptr(m), ctypes.addressof(ws), B, L, E, H, F, int(N), _ptr(workspace),
+                                  workspace.numel() * workspace.element_size(), _stream(dev), _ptr(y))
+    if st != 0:
+        raise RSAError(st, "rsa_layer_forward")
+    return y

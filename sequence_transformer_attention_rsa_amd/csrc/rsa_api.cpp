@@ -51,6 +51,38 @@ rsa::BackwardCall backward_call(const void* q, const void* k, const void* v, con
     return c;
 }
 
+// The token-local steps: bf16 only, widths the 128x128 product tiles and
+// the 64-wide contraction steps divide, hidden sizes the head split and
+// the layer normalisation cover.
+int check_linear(int M, int N, int K, int act) {
+    if (M <= 0 || N <= 0 || K <= 0) return RSA_ERR_SHAPE;
+    if (N % 128 != 0 || K % 64 != 0 || (act != 0 && act != 1)) return RSA_ERR_UNSUPPORTED;
+    if ((long long)M > (1ll << 30) || (long long)K > (1ll << 20) || (long long)N > (1ll << 20))
+        return RSA_ERR_UNSUPPORTED;
+    if ((long long)((M + 127) / 128) * (N / 128) > (1ll << 31) - 1) return RSA_ERR_UNSUPPORTED;   // grid size
+    return RSA_OK;
+}
+
+int check_heads(int B, int L, int E, int H) {
+    if (B <= 0 || L <= 0 || E <= 0 || H <= 0 || E % H != 0) return RSA_ERR_SHAPE;
+    const int d = E / H;
+    if ((d != 64 && d != 128) || E % 128 != 0) return RSA_ERR_UNSUPPORTED;
+    // the head-layout operand is addressed with 32-bit byte offsets
+    if ((long long)B * L * E * 2 >= (1ll << 32)) return RSA_ERR_UNSUPPORTED;
+    return check_linear(B * L, E, E, 0);
+}
+
+int check_layernorm(int rows, int E, float eps) {
+    if (rows <= 0 || E <= 0) return RSA_ERR_SHAPE;
+    if (E % 8 != 0 || E > 4096 || !(eps >= 0.0f)) return RSA_ERR_UNSUPPORTED;
+    return RSA_OK;
+}
+
+size_t layer_workspace(int B, int L, int E, int F) {
+    const size_t M = (size_t)B * L;
+    return (4 * M * E + M * F) * 2;   // Q, K, V, O, then F1 (A1, h1, A2 reuse Q, K, V)
+}
+
 }  // namespace
 
 extern "C" {
@@ -231,6 +263,191 @@ int rsa_backward_dkdv(const void* q, const void* k, const void* v, const void* d
     c.dk = dk;
     c.dv = dv;
     return launch_status(rsa::launch_backward(c, rsa::kBwdStageDkDv, static_cast<hipStream_t>(stream)));
+}
+
+int rsa_linear(const void* a, const void* w, const float* bias, const void* residual, int M, int N, int K,
+               int activation, void* stream, void* out) {
+    if (!a || !w || !out) return RSA_ERR_NULL;
+    int st = check_linear(M, N, K, activation);
+    if (st != RSA_OK) return st;
+    if (!aligned(a, 16) || !aligned(w, 16) || !aligned(out, 16) || !aligned(bias, 16) || !aligned(residual, 16))
+        return RSA_ERR_ALIGN;
+    rsa::LinearCall c{};
+    c.a = a;
+    c.w = w;
+    c.bias = bias;
+    c.residual = residual;
+    c.out0 = out;
+    c.M = M;
+    c.N = N;
+    c.K = K;
+    c.act = activation;
+    c.layout = rsa::kLinearRows;
+    return launch_status(rsa::launch_linear(c, static_cast<hipStream_t>(stream)));
+}
+
+int rsa_qkv_projection(const void* x, const void* w_qkv, const float* b_qkv, int B, int L, int E, int H,
+                       void* stream, void* q, void* k, void* v) {
+    if (!x || !w_qkv || !q || !k || !v) return RSA_ERR_NULL;
+    int st = check_heads(B, L, E, H);
+    if (st != RSA_OK) return st;
+    if (!aligned(x, 16) || !aligned(w_qkv, 16) || !aligned(b_qkv, 16) || !aligned(q, 16) || !aligned(k, 16) ||
+        !aligned(v, 16))
+        return RSA_ERR_ALIGN;
+    rsa::LinearCall c{};
+    c.a = x;
+    c.w = w_qkv;
+    c.bias = b_qkv;
+    c.out0 = q;
+    c.out1 = k;
+    c.out2 = v;
+    c.M = B * L;
+    c.N = 3 * E;
+    c.K = E;
+    c.layout = rsa::kLinearQkv;
+    c.L = L;
+    c.H = H;
+    c.d = E / H;
+    return launch_status(rsa::launch_linear(c, static_cast<hipStream_t>(stream)));
+}
+
+int rsa_output_projection(const void* o, const void* w_o, const float* b_o, const void* residual, int B, int L,
+                          int E, int H, void* stream, void* out) {
+    if (!o || !w_o || !out) return RSA_ERR_NULL;
+    int st = check_heads(B, L, E, H);
+    if (st != RSA_OK) return st;
+    if (!aligned(o, 16) || !aligned(w_o, 16) || !aligned(b_o, 16) || !aligned(residual, 16) || !aligned(out, 16))
+        return RSA_ERR_ALIGN;
+    rsa::LinearCall c{};
+    c.a = o;
+    c.w = w_o;
+    c.bias = b_o;
+    c.residual = residual;
+    c.out0 = out;
+    c.M = B * L;
+    c.N = E;
+    c.K = E;
+    c.layout = rsa::kLinearHeadsIn;
+    c.L = L;
+    c.H = H;
+    c.d = E / H;
+    return launch_status(rsa::launch_linear(c, static_cast<hipStream_t>(stream)));
+}
+
+int rsa_layernorm(const void* x, const float* gamma, const float* beta, int rows, int E, float eps, void* stream,
+                  void* y) {
+    if (!x || !gamma || !beta || !y) return RSA_ERR_NULL;
+    int st = check_layernorm(rows, E, eps);
+    if (st != RSA_OK) return st;
+    if (!aligned(x, 16) || !aligned(gamma, 16) || !aligned(beta, 16) || !aligned(y, 16)) return RSA_ERR_ALIGN;
+    return launch_status(rsa::launch_layernorm(x, gamma, beta, rows, E, eps, y, static_cast<hipStream_t>(stream)));
+}
+
+size_t rsa_layer_forward_workspace_bytes(int B, int L, int E, int H, int F, int N) {
+    if (check_heads(B, L, E, H) != RSA_OK || check_linear(B * L, F, E, 1) != RSA_OK ||
+        check_linear(B * L, E, F, 0) != RSA_OK || check_sizes(B, H, L, E / H, N, RSA_BF16) != RSA_OK)
+        return 0;
+    return layer_workspace(B, L, E, F);
+}
+
+int rsa_layer_forward(const void* x, const uint8_t* key_mask, const rsa_layer_weights* w, int B, int L, int E,
+                      int H, int F, int N, void* workspace, size_t workspace_bytes, void* stream, void* y) {
+    if (!x || !w || !y || !w->w_qkv || !w->w_o || !w->w_ff1 || !w->w_ff2 || !w->ln1_gamma || !w->ln1_beta ||
+        !w->ln2_gamma || !w->ln2_beta)
+        return RSA_ERR_NULL;
+    int st = check_heads(B, L, E, H);
+    if (st == RSA_OK) st = check_linear(B * L, F, E, 1);
+    if (st == RSA_OK) st = check_linear(B * L, E, F, 0);
+    if (st == RSA_OK) st = check_sizes(B, H, L, E / H, N, RSA_BF16);
+    if (st == RSA_OK) st = check_layernorm(B * L, E, 1e-12f);
+    if (st != RSA_OK) return st;
+    if (L > kMaxL) return RSA_ERR_UNSUPPORTED;
+    const void* ptrs[] = {x, key_mask, y, workspace, w->w_qkv, w->b_qkv, w->w_o, w->b_o, w->ln1_gamma, w->ln1_beta,
+                          w->w_ff1, w->b_ff1, w->w_ff2, w->b_ff2, w->ln2_gamma, w->ln2_beta};
+    for (const void* p : ptrs)
+        if (!aligned(p, 16)) return RSA_ERR_ALIGN;
+    if (!workspace || workspace_bytes < layer_workspace(B, L, E, F)) return RSA_ERR_WORKSPACE;
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const size_t me = (size_t)B * L * E;
+    uint16_t* ws = static_cast<uint16_t*>(workspace);
+    uint16_t *q = ws, *k = ws + me, *v = ws + 2 * me, *o = ws + 3 * me, *f1 = ws + 4 * me;
+    uint16_t *a1 = q, *h1 = k, *a2 = v;   // Q, K, V are dead once the attention has run
+    const int M = B * L, d = E / H;
+
+    rsa::LinearCall c{};
+    c.a = x;
+    c.w = w->w_qkv;
+    c.bias = w->b_qkv;
+    c.out0 = q;
+    c.out1 = k;
+    c.out2 = v;
+    c.M = M;
+    c.N = 3 * E;
+    c.K = E;
+    c.layout = rsa::kLinearQkv;
+    c.L = L;
+    c.H = H;
+    c.d = d;
+    hipError_t e = rsa::launch_linear(c, s);
+    if (e != hipSuccess) return RSA_ERR_HIP;
+
+    rsa::ForwardCall fc{};
+    fc.q = q;
+    fc.k = k;
+    fc.v = v;
+    fc.mask = key_mask;
+    fc.out = o;
+    fc.B = B;
+    fc.H = H;
+    fc.L = L;
+    fc.d = d;
+    fc.N = N;
+    fc.Lq = L;
+    fc.groups = 1;
+    fc.bf16 = true;
+    if (rsa::launch_forward(fc, s) != hipSuccess) return RSA_ERR_HIP;
+
+    c = rsa::LinearCall{};
+    c.a = o;
+    c.w = w->w_o;
+    c.bias = w->b_o;
+    c.residual = x;
+    c.out0 = a1;
+    c.M = M;
+    c.N = E;
+    c.K = E;
+    c.layout = rsa::kLinearHeadsIn;
+    c.L = L;
+    c.H = H;
+    c.d = d;
+    if (rsa::launch_linear(c, s) != hipSuccess) return RSA_ERR_HIP;
+    if (rsa::launch_layernorm(a1, w->ln1_gamma, w->ln1_beta, M, E, 1e-12f, h1, s) != hipSuccess) return RSA_ERR_HIP;
+
+    c = rsa::LinearCall{};
+    c.a = h1;
+    c.w = w->w_ff1;
+    c.bias = w->b_ff1;
+    c.out0 = f1;
+    c.M = M;
+    c.N = F;
+    c.K = E;
+    c.act = 1;
+    c.layout = rsa::kLinearRows;
+    if (rsa::launch_linear(c, s) != hipSuccess) return RSA_ERR_HIP;
+
+    c = rsa::LinearCall{};
+    c.a = f1;
+    c.w = w->w_ff2;
+    c.bias = w->b_ff2;
+    c.residual = h1;
+    c.out0 = a2;
+    c.M = M;
+    c.N = E;
+    c.K = F;
+    c.layout = rsa::kLinearRows;
+    if (rsa::launch_linear(c, s) != hipSuccess) return RSA_ERR_HIP;
+    return launch_status(rsa::launch_layernorm(a2, w->ln2_gamma, w->ln2_beta, M, E, 1e-12f, y, s));
 }
 
 const char* rsa_status_string(int status) {

@@ -70,4 +70,29 @@ constexpr int kBwdStageAll = kBwdStagePre | kBwdStageDq | kBwdStageDkDv;
 
 hipError_t launch_backward(const BackwardCall& c, int stages, hipStream_t stream);
 
+// Token-local steps of the layer around the attention (rsa_layer.hip).
+// Matrix product out = act(a w^T + bias) + residual, bf16 operands, fp32
+// accumulation; N % 128 == 0 and K % 64 == 0.
+constexpr int kLinearRows = 0;      // a [M,K], out0 [M,N]
+constexpr int kLinearQkv = 1;       // a [M,K] = x [B*L,E]; out0/1/2 = Q/K/V [B,H,L,d] (N = 3E)
+constexpr int kLinearHeadsIn = 2;   // a = attention output [B,H,L,d] read as [B*L,H*d]; out0 [M,N]
+
+struct LinearCall {
+    const void* a;
+    const void* w;          // [N,K]
+    const float* bias;      // [N] or nullptr
+    const void* residual;   // [M,N] or nullptr
+    void* out0;
+    void* out1;
+    void* out2;
+    int M, N, K;
+    int act;                // 0: none, 1: GeLU
+    int layout;             // kLinear*
+    int L, H, d;            // token/head layout for kLinearQkv and kLinearHeadsIn
+};
+
+hipError_t launch_linear(const LinearCall& c, hipStream_t stream);
+hipError_t launch_layernorm(const void* x, const float* gamma, const float* beta, int rows, int E, float eps,
+                            void* y, hipStream_t stream);
+
 }  // namespace rsa

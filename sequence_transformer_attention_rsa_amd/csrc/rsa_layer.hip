@@ -1,0 +1,333 @@
+// rsa_layer.hip -- the token-local steps of the sequence-parallel layer
+// around RSA on gfx950: a bf16 MFMA matrix product with fused prologue and
+// epilogue variants (head split of Q/K/V, head merge of the attention output,
+// bias, GeLU, residual sum), and a layer normalisation over the hidden size.
+//
+// Review page of "Sequence Parallelism: Making 4D Parallelism Possible"
+// (ABSTRACT): each device holds one chunk of the sequence, and every step of
+// the Transformer layer other than the attention acts on one token at a
+// time, so these run on a chunk without any exchange. The tensor-parallelism
+// page ("一文捋順千億模型訓練技術", section 二, 1D tensor parallelism, parts
+// (2) and (3)) describes the two fully connected layers with GeLU and the
+// independent attention heads.
+
+#include "rsa_internal.h"
+#include "rsa_tiles.h"
+
+namespace rsa {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kGT = 128;                         // output tile: 128 rows x 128 columns
+constexpr int kGK = 64;                          // contraction step
+using GTile = DirectTile<64>;                    // [64 rows][64 bf16], 8 KB, swizzled
+constexpr int kStageBytes = 4 * GTile::BYTES;    // A rows 0-63, 64-127; W rows 0-63, 64-127
+constexpr int kGemmBuf = 3;
+constexpr int kStagePitch = kGT * 4 + 16;        // fp32 epilogue row, bytes (16 B pad)
+constexpr int kGemmLds = (kGemmBuf * kStageBytes > kGT * kStagePitch) ? kGemmBuf * kStageBytes
+                                                                       : kGT * kStagePitch;
+
+// A operand layouts: [M, K] rows, or the attention output [B, H, L, d] read
+// as [B*L, H*d] (head merge). Output layouts: [M, N] rows, or Q/K/V
+// [B, H, L, d] from column blocks [0, E), [E, 2E), [2E, 3E) (head split).
+enum { kProRows = 0, kProHeads = 1 };
+enum { kEpiRows = 0, kEpiQkv = 1 };
+
+struct GemmParams {
+    const uint16_t* a;
+    const uint16_t* w;      // [N, K]
+    const float* bias;      // [N] or nullptr
+    const uint16_t* res;    // [M, N] or nullptr
+    uint16_t* out0;         // [M, N], or Q
+    uint16_t* out1;         // K
+    uint16_t* out2;         // V
+    int M, N, K;
+    int act;                // 0: none, 1: GeLU (before the residual sum)
+    int L, H, d, E;         // token/head layout of the head variants
+    int mt, nt;             // tile counts
+};
+
+// GeLU(z) = z Phi(z) = z/2 erfc(-z / sqrt 2): the complementary form keeps
+// full fp32 accuracy for negative z, where 1 + erf(z / sqrt 2) would cancel.
+__device__ __forceinline__ float gelu(float z) { return 0.5f * z * erfcf(-z * 0.70710678118654752f); }
+
+// out = act(A W^T + bias) + res for one 128x128 tile. Four waves, each a
+// 64x64 quarter as 2x2 MFMA blocks. The MFMA computes the transposed block
+// (W rows as its A operand) so that each lane holds one output row and
+// registers run along the columns: the epilogue then writes four
+// consecutive fp32 columns per lane into an LDS staging tile, from which
+// the whole workgroup stores 16-byte chunks of rows.
+template <int PRO, int EPI>
+__global__ __launch_bounds__(kThreads) void rsa_gemm_bf16(GemmParams p) {
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[kGemmLds];
+
+    const int lid = xcd_remap(blockIdx.x, p.mt * p.nt);
+    const int m0 = (lid / p.nt) * kGT, n0 = (lid % p.nt) * kGT;
+    const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+    const int j = lane & 31, h = lane >> 5;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int nk = p.K / kGK;
+
+    // Per-lane source offsets of this workgroup's copies (the same for every
+    // contraction step; the step moves the scalar base). Rows past M read row
+    // M - 1 (their results are never stored).
+    uint32_t va[2][GTile::IPW], vw[2][GTile::IPW];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int u = 0; u < GTile::IPW; ++u) {
+            const int r = (wave * GTile::IPW + u) * GTile::RPI + lane / GTile::CPR;
+            const uint32_t sw = 16u * (uint32_t)((lane % GTile::CPR) ^ GTile::swz(r));
+            const int m = min(m0 + 64 * t + r, p.M - 1);
+            if constexpr (PRO == kProRows) {
+                va[t][u] = (uint32_t)(m - m0) * (uint32_t)(2 * p.K) + sw;
+            } else {
+                const int b = m / p.L, l = m - b * p.L;
+                va[t][u] = ((uint32_t)(b * p.H) * (uint32_t)p.L + (uint32_t)l) * (uint32_t)(2 * p.d) + sw;
+            }
+            vw[t][u] = (uint32_t)(64 * t + r) * (uint32_t)(2 * p.K) + sw;
+        }
+
+    auto load = [&](int s, int bi) {
+        uint8_t* sb = smem + bi * kStageBytes;
+        const uint16_t* abase;
+        if constexpr (PRO == kProRows) {
+            abase = p.a + (size_t)m0 * p.K + (size_t)s * kGK;
+        } else {
+            const int k0 = s * kGK, hh = k0 / p.d;
+            abase = p.a + (size_t)hh * p.L * p.d + (k0 - hh * p.d);
+        }
+        const uint16_t* wbase = p.w + (size_t)n0 * p.K + (size_t)s * kGK;
+        const uint32_t l0 = lds_addr(sb) + (uint32_t)(__builtin_amdgcn_readfirstlane(wave) * GTile::IPW * 1024);
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int u = 0; u < GTile::IPW; ++u) {
+                dma_copy16(abase, va[t][u], l0 + (uint32_t)(t * GTile::BYTES + u * 1024));
+                dma_copy16(wbase, vw[t][u], l0 + (uint32_t)((2 + t) * GTile::BYTES + u * 1024));
+            }
+    };
+    constexpr int kCopies = 4 * GTile::IPW;   // this wave's copies per step
+
+    f32x16 acc[2][2];
+#pragma unroll
+    for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+        for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[ni][mi][r] = 0.0f;
+
+    load(0, 0);
+    if (nk > 1) load(1, 1);
+    for (int s = 0; s < nk; ++s) {
+        // step s landed (step s + 1 may stay in flight); after the barrier
+        // every wave is done with step s - 1, whose buffer takes step s + 2
+        if (s + 1 < nk)
+            vm_wait<kCopies>();
+        else
+            vm_wait<0>();
+        bare_barrier();
+        if (s + 2 < nk) load(s + 2, (s + 2) % kGemmBuf);
+        const uint8_t* sb = smem + (s % kGemmBuf) * kStageBytes;
+        const uint8_t* at = sb + wm * GTile::BYTES;
+        const uint8_t* wt = sb + (2 + wn) * GTile::BYTES;
+#pragma unroll
+        for (int ks = 0; ks < kGK / 16; ++ks) {
+            u32x4 af[2], wf[2];
+#pragma unroll
+            for (int x = 0; x < 2; ++x) {
+                af[x] = GTile::chunk(at, 32 * x + j, 2 * ks + h);
+                wf[x] = GTile::chunk(wt, 32 * x + j, 2 * ks + h);
+            }
+#pragma unroll
+            for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+                for (int mi = 0; mi < 2; ++mi) acc[ni][mi] = mfma_32x32x16_bf16(wf[ni], af[mi], acc[ni][mi]);
+        }
+    }
+    bare_barrier();   // every wave's last reads of the stage buffers are done
+
+    // bias and activation in registers, fp32 tile to LDS
+#pragma unroll
+    for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+            const int nl = 64 * wn + 32 * ni + 8 * r4 + 4 * h;   // first of 4 columns
+            f32x4 bv = {0.0f, 0.0f, 0.0f, 0.0f};
+            if (p.bias) bv = *reinterpret_cast<const f32x4*>(p.bias + n0 + nl);
+#pragma unroll
+            for (int mi = 0; mi < 2; ++mi) {
+                f32x4 o;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float z = acc[ni][mi][4 * r4 + e] + bv[e];
+                    o[e] = p.act ? gelu(z) : z;
+                }
+                const int ml = 64 * wm + 32 * mi + j;
+                *reinterpret_cast<f32x4*>(smem + ml * kStagePitch + nl * 4) = o;
+            }
+        }
+    __syncthreads();
+
+    // 16-byte output chunks: 128 rows x 16 chunks of 8 columns
+    uint16_t* dst = p.out0;
+    int ncol0 = n0;
+    if constexpr (EPI == kEpiQkv) {
+        const int which = n0 / p.E;   // a tile never straddles Q, K and V (E % 128 == 0)
+        dst = which == 0 ? p.out0 : (which == 1 ? p.out1 : p.out2);
+        ncol0 = n0 - which * p.E;
+    }
+#pragma unroll 2
+    for (int it = 0; it < kGT * 16 / kThreads; ++it) {
+        const int idx = it * kThreads + threadIdx.x;
+        const int row = idx >> 4, c = idx & 15;
+        const int m = m0 + row;
+        if (m >= p.M) continue;
+        const uint8_t* src = smem + row * kStagePitch + c * 32;
+        const f32x4 lo = *reinterpret_cast<const f32x4*>(src);
+        const f32x4 hi = *reinterpret_cast<const f32x4*>(src + 16);
+        float x[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        if (p.res) {
+            const u32x4 rv = *reinterpret_cast<const u32x4*>(p.res + (size_t)m * p.N + n0 + 8 * c);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                x[2 * e] += bf16_lo(rv[e]);
+                x[2 * e + 1] += bf16_hi(rv[e]);
+            }
+        }
+        const u32x4 pk = {pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]), pack_bf16x2(x[4], x[5]),
+                          pack_bf16x2(x[6], x[7])};
+        size_t off;
+        if constexpr (EPI == kEpiQkv) {
+            const int nn = ncol0 + 8 * c, hh = nn / p.d, dd = nn - hh * p.d;
+            const int b = m / p.L, l = m - b * p.L;
+            off = ((size_t)(b * p.H + hh) * p.L + l) * p.d + dd;
+        } else {
+            off = (size_t)m * p.N + n0 + 8 * c;
+        }
+        *reinterpret_cast<u32x4*>(dst + off) = pk;
+    }
+}
+
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
+    return x;
+}
+
+// y = (x - mean) / sqrt(var + eps) * gamma + beta over each row of E bf16
+// values; one wave per row, CPL 16-byte chunks per lane, statistics in fp32
+// (the mean first, then the mean squared deviation from it).
+template <int CPL>
+__global__ __launch_bounds__(kThreads) void rsa_layernorm_bf16(const uint16_t* __restrict__ x,
+                                                               const float* __restrict__ gamma,
+                                                               const float* __restrict__ beta,
+                                                               uint16_t* __restrict__ y, int rows, int E,
+                                                               float eps) {
+    const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+    const long long row = (long long)blockIdx.x * (kThreads / kWave) + wave;
+    if (row >= rows) return;
+    const int nch = E / 8;
+    const uint16_t* xr = x + row * E;
+    float v[CPL][8];
+    float s = 0.0f;
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+        const int ch = lane + kWave * c;
+        u32x4 w = {0u, 0u, 0u, 0u};
+        if (ch < nch) w = *reinterpret_cast<const u32x4*>(xr + 8 * ch);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            v[c][2 * e] = bf16_lo(w[e]);
+            v[c][2 * e + 1] = bf16_hi(w[e]);
+            s += v[c][2 * e] + v[c][2 * e + 1];
+        }
+    }
+    const float mean = wave_sum(s) / (float)E;
+    float q = 0.0f;
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+        if (lane + kWave * c < nch) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float dv = v[c][e] - mean;
+                q += dv * dv;
+            }
+        }
+    }
+    const float rstd = 1.0f / sqrtf(wave_sum(q) / (float)E + eps);
+    uint16_t* yr = y + row * E;
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+        const int ch = lane + kWave * c;
+        if (ch >= nch) continue;
+        const f32x4 g0 = *reinterpret_cast<const f32x4*>(gamma + 8 * ch);
+        const f32x4 g1 = *reinterpret_cast<const f32x4*>(gamma + 8 * ch + 4);
+        const f32x4 b0 = *reinterpret_cast<const f32x4*>(beta + 8 * ch);
+        const f32x4 b1 = *reinterpret_cast<const f32x4*>(beta + 8 * ch + 4);
+        const float g[8] = {g0[0], g0[1], g0[2], g0[3], g1[0], g1[1], g1[2], g1[3]};
+        const float b[8] = {b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
+        u32x4 o;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            o[e] = pack_bf16x2((v[c][2 * e] - mean) * rstd * g[2 * e] + b[2 * e],
+                               (v[c][2 * e + 1] - mean) * rstd * g[2 * e + 1] + b[2 * e + 1]);
+        *reinterpret_cast<u32x4*>(yr + 8 * ch) = o;
+    }
+}
+
+template <int PRO, int EPI>
+hipError_t launch_gemm_t(const GemmParams& p0, hipStream_t stream) {
+    GemmParams p = p0;
+    p.mt = (p.M + kGT - 1) / kGT;
+    p.nt = p.N / kGT;
+    hipLaunchKernelGGL((rsa_gemm_bf16<PRO, EPI>), dim3((unsigned)(p.mt * p.nt)), dim3(kThreads), 0, stream, p);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_linear(const LinearCall& c, hipStream_t stream) {
+    GemmParams p{};
+    p.a = static_cast<const uint16_t*>(c.a);
+    p.w = static_cast<const uint16_t*>(c.w);
+    p.bias = c.bias;
+    p.res = static_cast<const uint16_t*>(c.residual);
+    p.out0 = static_cast<uint16_t*>(c.out0);
+    p.out1 = static_cast<uint16_t*>(c.out1);
+    p.out2 = static_cast<uint16_t*>(c.out2);
+    p.M = c.M;
+    p.N = c.N;
+    p.K = c.K;
+    p.act = c.act;
+    p.L = c.L;
+    p.H = c.H;
+    p.d = c.d;
+    p.E = c.N / 3;
+    if (c.layout == kLinearQkv) return launch_gemm_t<kProRows, kEpiQkv>(p, stream);
+    if (c.layout == kLinearHeadsIn) return launch_gemm_t<kProHeads, kEpiRows>(p, stream);
+    return launch_gemm_t<kProRows, kEpiRows>(p, stream);
+}
+
+hipError_t launch_layernorm(const void* x, const float* gamma, const float* beta, int rows, int E, float eps,
+                            void* y, hipStream_t stream) {
+    const unsigned blocks = (unsigned)((rows + 3) / 4);
+    const uint16_t* xi = static_cast<const uint16_t*>(x);
+    uint16_t* yo = static_cast<uint16_t*>(y);
+    const int cpl = (E / 8 + kWave - 1) / kWave;
+    if (cpl <= 1)
+        hipLaunchKernelGGL((rsa_layernorm_bf16<1>), dim3(blocks), dim3(kThreads), 0, stream, xi, gamma, beta, yo,
+                           rows, E, eps);
+    else if (cpl <= 2)
+        hipLaunchKernelGGL((rsa_layernorm_bf16<2>), dim3(blocks), dim3(kThreads), 0, stream, xi, gamma, beta, yo,
+                           rows, E, eps);
+    else if (cpl <= 4)
+        hipLaunchKernelGGL((rsa_layernorm_bf16<4>), dim3(blocks), dim3(kThreads), 0, stream, xi, gamma, beta, yo,
+                           rows, E, eps);
+    else
+        hipLaunchKernelGGL((rsa_layernorm_bf16<8>), dim3(blocks), dim3(kThreads), 0, stream, xi, gamma, beta, yo,
+                           rows, E, eps);
+    return hipGetLastError();
+}
+
+}  // namespace rsa

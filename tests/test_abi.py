@@ -124,3 +124,73 @@ def test_forward_twopass_validation(lib):
     assert call(ws_bytes=ws - 1) == EWS
     assert call(ws_ptr=P + 4) == EALIGN
     assert call(q=P + 2) == EALIGN
+
+
+def test_linear_and_layernorm_validation(lib):
+    def lin(a=P, w=P, bias=None, res=None, M=256, N=256, K=128, act=0, out=P):
+        return lib.rsa_linear(a, w, bias, res, M, N, K, act, None, out)
+
+    assert lin(a=None) == ENULL
+    assert lin(out=None) == ENULL
+    assert lin(M=0) == ESHAPE
+    assert lin(N=200) == EUNSUP          # not a multiple of 128
+    assert lin(K=96) == EUNSUP           # not a multiple of 64
+    assert lin(act=2) == EUNSUP
+    assert lin(bias=P + 4) == EALIGN
+    assert lin(res=P + 8) == EALIGN
+
+    def ln(x=P, g=P, b=P, rows=10, E=768, eps=1e-12, y=P):
+        return lib.rsa_layernorm(x, g, b, rows, E, eps, None, y)
+
+    assert ln(g=None) == ENULL
+    assert ln(rows=0) == ESHAPE
+    assert ln(E=100) == EUNSUP
+    assert ln(E=8192) == EUNSUP
+    assert ln(eps=-1.0) == EUNSUP
+    assert ln(y=P + 2) == EALIGN
+
+
+def test_projection_validation(lib):
+    def qkv(x=P, B=2, L=64, E=768, H=12, q=P):
+        return lib.rsa_qkv_projection(x, P, None, B, L, E, H, None, q, P, P)
+
+    assert qkv(x=None) == ENULL
+    assert qkv(H=7) == ESHAPE            # H must divide E
+    assert qkv(E=768, H=24) == EUNSUP    # d = 32
+    assert qkv(E=576, H=9) == EUNSUP     # d = 64 but E % 128 != 0
+    assert qkv(B=1024, L=2048, E=1024, H=16) == EUNSUP   # 4 GiB operand
+    assert qkv(q=P + 2) == EALIGN
+
+    def oproj(o=P, res=None, E=1024, H=8):
+        return lib.rsa_output_projection(o, P, None, res, 2, 64, E, H, None, P)
+
+    assert oproj(o=None) == ENULL
+    assert oproj(H=5) == ESHAPE
+    assert oproj(res=P + 8) == EALIGN
+
+
+def test_layer_forward_validation(lib):
+    import ctypes
+
+    B, L, E, H, F, N = 2, 256, 768, 12, 3072, 4
+    ws = lib.rsa_layer_forward_workspace_bytes(B, L, E, H, F, N)
+    assert ws == (4 * B * L * E + B * L * F) * 2
+    assert lib.rsa_layer_forward_workspace_bytes(B, L, E, H, 3000, N) == 0
+    assert lib.rsa_layer_forward_workspace_bytes(B, 255, E, H, F, N) == 0
+
+    w = rsa._LayerWeights(*([P] * len(rsa.LAYER_WEIGHTS)))
+
+    def call(x=P, wp=None, L_=L, F_=F, ws_ptr=P, ws_bytes=ws):
+        wp = ctypes.addressof(w) if wp is None else wp
+        return lib.rsa_layer_forward(x, None, wp, B, L_, E, H, F_, N, ws_ptr, ws_bytes, None, P)
+
+    assert call(x=None) == ENULL
+    w.w_o = None
+    assert call() == ENULL
+    w.w_o = P
+    assert call(L_=L - 1) == ESHAPE      # N must divide L
+    assert call(F_=3000) == EUNSUP
+    assert call(ws_ptr=None) == EWS
+    assert call(ws_bytes=ws - 2) == EWS
+    w.b_ff1 = P + 4
+    assert call() == EALIGN
