@@ -62,6 +62,10 @@ def parse():
     ap.add_argument("--capacity", action="store_true",
                     help="single-GPU sequence-length capacity of the fused and the two-stage forward "
                          "(B=H=1, d=64) instead of the step benchmark")
+    ap.add_argument("--layer", action="store_true",
+                    help="time the encoder layer around RSA (QKV projection, attention, output projection, "
+                         "layer norms, GeLU MLP) instead of the attention step")
+    ap.add_argument("--layer-workload", default="layer_long_seq", choices=sorted(rsa_inputs.LAYERS))
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (counter calibration)")
     return ap.parse_args()
@@ -204,8 +208,119 @@ def capacity(args):
     return 0
 
 
+def layer_bench(args):
+    """The encoder layer around RSA, step by step: QKV projection (head split
+    fused), RSA forward, output projection (head merge, bias and residual
+    fused), layer norm, first MLP product (bias and GeLU fused), second MLP
+    product (bias and residual fused), layer norm. One launch per step, timed
+    with events between the calls; the chain equals rsa_layer_forward bit for
+    bit (checked once here). Work: products 2*M*E*(3E + E + F + F) flops with
+    M = B*L, attention 4*B*H*L*Lk*d; layer norms read and write M*E bf16."""
+    import torch
+
+    import sequence_transformer_attention_rsa_amd as rsa
+
+    shp = rsa_inputs.LAYERS[args.layer_workload]
+    dev = torch.device("cuda:0")
+    x = rsa_inputs.layer_inputs(shp)
+    B, L, E, H, F, N = shp.B, shp.L, shp.E, shp.H, shp.F, shp.N
+    M = B * L
+
+    def bf(a):
+        return torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(torch.bfloat16).to(dev)
+
+    w = {n: (bf(x[n]) if n.startswith("w_") else torch.from_numpy(x[n]).to(dev)) for n in rsa.LAYER_WEIGHTS}
+    xin = bf(x["x"])
+    mask = None if x["mask"] is None else torch.from_numpy(x["mask"]).to(dev)
+    names = ["qkv_projection", "attention", "output_projection", "layernorm1", "ff1_gelu", "ff2_residual",
+             "layernorm2"]
+    keep = {}
+
+    def step(ev=None):
+        def mark(i):
+            if ev is not None:
+                ev[i].record()
+        mark(0)
+        q, k, v = rsa.qkv_projection(xin, w["w_qkv"], w["b_qkv"], H)
+        mark(1)
+        o = rsa.forward(q, k, v, mask, N=N)
+        mark(2)
+        a1 = rsa.output_projection(o, w["w_o"], w["b_o"], xin)
+        mark(3)
+        h1 = rsa.layernorm(a1, w["ln1_gamma"], w["ln1_beta"]).view(M, E)
+        mark(4)
+        f1 = rsa.linear(h1, w["w_ff1"], w["b_ff1"], activation="gelu")
+        mark(5)
+        a2 = rsa.linear(f1, w["w_ff2"], w["b_ff2"], residual=h1)
+        mark(6)
+        keep["y"] = rsa.layernorm(a2, w["ln2_gamma"], w["ln2_beta"])
+        mark(7)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ref = rsa.layer_forward(xin, w, H=H, N=N, key_mask=mask)
+    torch.cuda.synchronize()
+    same = bool(torch.equal(ref.view(M, E), keep["y"]))
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(args.steps)]
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for s in range(args.steps):
+        step(events[s])
+    stop.record()
+    torch.cuda.synchronize()
+    ms_per_step = start.elapsed_time(stop) / args.steps
+    lk = float(x["valid_len"].sum()) if x["valid_len"] is not None else float(B * L)
+    d = E // H
+    flops = {"qkv_projection": 2.0 * M * E * 3 * E, "attention": 4.0 * H * L * d * lk,
+             "output_projection": 2.0 * M * E * E, "ff1_gelu": 2.0 * M * E * F, "ff2_residual": 2.0 * M * F * E}
+    ln_bytes = 2.0 * M * E * 2 + 2 * E * 4
+    per = {}
+    for i, n in enumerate(names):
+        durs = [events[s][i].elapsed_time(events[s][i + 1]) for s in range(args.steps)]
+        per[n] = {"avg_ms": float(np.mean(durs)), "median_ms": float(np.median(durs))}
+        if n in flops:
+            per[n]["tflops"] = flops[n] / (per[n]["avg_ms"] * 1e-3) / 1e12
+            per[n]["frac_peak"] = per[n]["tflops"] / PEAK_BF16_TFLOPS
+        else:
+            per[n]["gbs"] = ln_bytes / (per[n]["avg_ms"] * 1e-3) / 1e9
+            per[n]["frac_hbm_peak"] = per[n]["gbs"] / PEAK_HBM_GBS
+    total = sum(flops.values())
+    value = total / (ms_per_step * 1e-3) / 1e12
+    gemm = [n for n in names if n in flops and n != "attention"]
+    gemm_ms = sum(per[n]["avg_ms"] for n in gemm)
+    dom = max(gemm, key=lambda n: per[n]["avg_ms"])
+    line = {
+        "metric": "SP encoder layer forward TFLOP/s (QKV proj + RSA + out proj + LN + GeLU MLP + LN), "
+                  "% of MI355X bf16 MFMA peak",
+        "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": shp.name, "B": B, "L": L, "E": E, "H": H, "F": F, "N": N,
+                   "key_mask": shp.valid_range is not None, "description": shp.description},
+        "frac_peak": value / PEAK_BF16_TFLOPS,
+        "products_tflops": sum(flops[n] for n in gemm) / (gemm_ms * 1e-3) / 1e12,
+        "products_share_of_step": gemm_ms / ms_per_step,
+        "chain_equals_rsa_layer_forward": same,
+        "kernels": per,
+        "roofline": {"kernel": f"rsa_gemm_bf16 ({dom})", "bound": "mfma",
+                     "achieved": per[dom]["tflops"], "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": per[dom]["tflops"] / PEAK_BF16_TFLOPS, "traffic": None,
+                     "avg_ms": per[dom]["avg_ms"], "flops_per_launch": flops[dom]},
+        "gpu": torch.cuda.get_device_name(dev),
+    }
+    print(json.dumps(line), flush=True)
+    return 0 if same else 1
+
+
 def main():
     args = parse()
+    if args.layer:
+        if args.gpus != 1:
+            print("bench.py measures one GPU only", file=sys.stderr)
+            return 2
+        return layer_bench(args)
     if args.capacity:
         if args.gpus != 1:
             print("bench.py measures one GPU only", file=sys.stderr)

@@ -22,7 +22,11 @@ constexpr int kGT = 128;                         // output tile: 128 rows x 128 
 constexpr int kGK = 64;                          // contraction step
 using GTile = DirectTile<64>;                    // [64 rows][64 bf16], 8 KB, swizzled
 constexpr int kStageBytes = 4 * GTile::BYTES;    // A rows 0-63, 64-127; W rows 0-63, 64-127
-constexpr int kGemmBuf = 3;
+#ifndef RSA_GEMM_NBUF
+#define RSA_GEMM_NBUF 2
+#endif
+constexpr int kGemmBuf = RSA_GEMM_NBUF;          // stage buffers: kGemmBuf - 1 steps in flight
+static_assert(kGemmBuf >= 2 && kGemmBuf <= 4, "stage buffers");
 constexpr int kStagePitch = kGT * 4 + 16;        // fp32 epilogue row, bytes (16 B pad)
 constexpr int kGemmLds = (kGemmBuf * kStageBytes > kGT * kStagePitch) ? kGemmBuf * kStageBytes
                                                                        : kGT * kStagePitch;
@@ -117,17 +121,20 @@ __global__ __launch_bounds__(kThreads) void rsa_gemm_bf16(GemmParams p) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[ni][mi][r] = 0.0f;
 
-    load(0, 0);
-    if (nk > 1) load(1, 1);
+    for (int s = 0; s < kGemmBuf - 1 && s < nk; ++s) load(s, s);
     for (int s = 0; s < nk; ++s) {
-        // step s landed (step s + 1 may stay in flight); after the barrier
-        // every wave is done with step s - 1, whose buffer takes step s + 2
-        if (s + 1 < nk)
+        // step s landed (the steps after it that were issued may stay in
+        // flight); after the barrier every wave is done with step s - 1,
+        // whose buffer takes step s + kGemmBuf - 1
+        const int ahead = min(kGemmBuf - 2, nk - 1 - s);
+        if (kGemmBuf >= 4 && ahead >= 2)
+            vm_wait<2 * kCopies>();
+        else if (kGemmBuf >= 3 && ahead >= 1)
             vm_wait<kCopies>();
         else
             vm_wait<0>();
         bare_barrier();
-        if (s + 2 < nk) load(s + 2, (s + 2) % kGemmBuf);
+        if (s + kGemmBuf - 1 < nk) load(s + kGemmBuf - 1, (s + kGemmBuf - 1) % kGemmBuf);
         const uint8_t* sb = smem + (s % kGemmBuf) * kStageBytes;
         const uint8_t* at = sb + wm * GTile::BYTES;
         const uint8_t* wt = sb + (2 + wn) * GTile::BYTES;
