@@ -138,18 +138,24 @@ __global__ __launch_bounds__(kThreads) void rsa_gemm_bf16(GemmParams p) {
         const uint8_t* sb = smem + (s % kGemmBuf) * kStageBytes;
         const uint8_t* at = sb + wm * GTile::BYTES;
         const uint8_t* wt = sb + (2 + wn) * GTile::BYTES;
-#pragma unroll
-        for (int ks = 0; ks < kGK / 16; ++ks) {
-            u32x4 af[2], wf[2];
+        // fragments of sub-step ks + 1 are read while the MFMAs of ks run
+        u32x4 af[2][2], wf[2][2];
+        auto frags = [&](int ks, int slot) {
 #pragma unroll
             for (int x = 0; x < 2; ++x) {
-                af[x] = GTile::chunk(at, 32 * x + j, 2 * ks + h);
-                wf[x] = GTile::chunk(wt, 32 * x + j, 2 * ks + h);
+                af[slot][x] = GTile::chunk(at, 32 * x + j, 2 * ks + h);
+                wf[slot][x] = GTile::chunk(wt, 32 * x + j, 2 * ks + h);
             }
+        };
+        frags(0, 0);
+#pragma unroll
+        for (int ks = 0; ks < kGK / 16; ++ks) {
+            if (ks + 1 < kGK / 16) frags(ks + 1, (ks + 1) & 1);
 #pragma unroll
             for (int ni = 0; ni < 2; ++ni)
 #pragma unroll
-                for (int mi = 0; mi < 2; ++mi) acc[ni][mi] = mfma_32x32x16_bf16(wf[ni], af[mi], acc[ni][mi]);
+                for (int mi = 0; mi < 2; ++mi)
+                    acc[ni][mi] = mfma_32x32x16_bf16(wf[ks & 1][ni], af[ks & 1][mi], acc[ni][mi]);
         }
     }
     bare_barrier();   // every wave's last reads of the stage buffers are done
@@ -213,6 +219,163 @@ __global__ __launch_bounds__(kThreads) void rsa_gemm_bf16(GemmParams p) {
             off = (size_t)m * p.N + n0 + 8 * c;
         }
         *reinterpret_cast<u32x4*>(dst + off) = pk;
+    }
+}
+
+// ---- 256x256 tiles, eight waves ------------------------------------------
+// The same product with twice the tile edge: each contraction step copies
+// (256 + 256) x 64 bf16 for 2 x 256 x 256 x 64 flops, half the L2-to-LDS
+// bytes per flop of the 128x128 tile, and each wave (a 128 x 64 strip, 4x2
+// MFMA blocks) reads 6 fragments per 8 MFMAs instead of 4 per 4. Two stage
+// buffers fill 128 KB of LDS (one workgroup per CU, two waves per SIMD).
+// The epilogue finishes each value in registers (bias, GeLU, residual read
+// as 8-byte pieces), rounds once to bf16 and stages each wave's strip in
+// its own 16 KB of LDS (16-byte chunks XOR-swizzled by row), from which the
+// wave stores whole 128-byte row segments.
+constexpr int kBigThreads = 512;
+constexpr int kBT = 256;
+using BTile = DirectTile<64, 8>;                 // one copy instruction per wave per 64-row tile
+constexpr int kBigStage = 8 * BTile::BYTES;      // A: tiles 0-3, W: tiles 4-7
+constexpr int kBigLds = 2 * kBigStage;           // 128 KB; the epilogue reuses it
+
+template <int PRO, int EPI>
+__global__ __launch_bounds__(kBigThreads) void rsa_gemm_bf16_256(GemmParams p) {
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[kBigLds];
+
+    const int lid = xcd_remap(blockIdx.x, p.mt * p.nt);
+    const int m0 = (lid / p.nt) * kBT, n0 = (lid % p.nt) * kBT;
+    const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+    const int j = lane & 31, h = lane >> 5;
+    const int wm = wave & 1, wn = wave >> 1;     // rows 128 wm .., columns 64 wn ..
+    const int nk = p.K / kGK;
+
+    uint32_t va[4], vw[4];
+    {
+        const int r = wave * BTile::RPI + lane / BTile::CPR;   // tile row this lane copies
+        const uint32_t sw = 16u * (uint32_t)((lane % BTile::CPR) ^ BTile::swz(r));
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const int m = min(m0 + 64 * t + r, p.M - 1);
+            if constexpr (PRO == kProRows) {
+                va[t] = (uint32_t)(m - m0) * (uint32_t)(2 * p.K) + sw;
+            } else {
+                const int b = m / p.L, l = m - b * p.L;
+                va[t] = ((uint32_t)(b * p.H) * (uint32_t)p.L + (uint32_t)l) * (uint32_t)(2 * p.d) + sw;
+            }
+            vw[t] = (uint32_t)(64 * t + r) * (uint32_t)(2 * p.K) + sw;
+        }
+    }
+    auto load = [&](int s, int bi) {
+        uint8_t* sb = smem + bi * kBigStage;
+        const uint16_t* abase;
+        if constexpr (PRO == kProRows) {
+            abase = p.a + (size_t)m0 * p.K + (size_t)s * kGK;
+        } else {
+            const int k0 = s * kGK, hh = k0 / p.d;
+            abase = p.a + (size_t)hh * p.L * p.d + (k0 - hh * p.d);
+        }
+        const uint16_t* wbase = p.w + (size_t)n0 * p.K + (size_t)s * kGK;
+        const uint32_t l0 = lds_addr(sb) + (uint32_t)(__builtin_amdgcn_readfirstlane(wave) * 1024);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            dma_copy16(abase, va[t], l0 + (uint32_t)(t * BTile::BYTES));
+            dma_copy16(wbase, vw[t], l0 + (uint32_t)((4 + t) * BTile::BYTES));
+        }
+    };
+
+    f32x16 acc[2][4];
+#pragma unroll
+    for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+        for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[ni][mi][r] = 0.0f;
+
+    load(0, 0);
+    for (int s = 0; s < nk; ++s) {
+        vm_wait<0>();   // step s landed
+        bare_barrier(); // ... for every wave; every wave is done with step s - 1
+        if (s + 1 < nk) load(s + 1, (s + 1) & 1);
+        const uint8_t* sb = smem + (s & 1) * kBigStage;
+        const uint8_t* wt = sb + (4 + wn) * BTile::BYTES;
+        // fragments of sub-step ks + 1 are read while the MFMAs of ks run
+        u32x4 af[2][4], wf[2][2];
+        auto frags = [&](int ks, int slot) {
+#pragma unroll
+            for (int mi = 0; mi < 4; ++mi)
+                af[slot][mi] = BTile::chunk(sb + (2 * wm + (mi >> 1)) * BTile::BYTES, 32 * (mi & 1) + j, 2 * ks + h);
+#pragma unroll
+            for (int ni = 0; ni < 2; ++ni) wf[slot][ni] = BTile::chunk(wt, 32 * ni + j, 2 * ks + h);
+        };
+        frags(0, 0);
+#pragma unroll
+        for (int ks = 0; ks < kGK / 16; ++ks) {
+            if (ks + 1 < kGK / 16) frags(ks + 1, (ks + 1) & 1);
+#pragma unroll
+            for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+                for (int mi = 0; mi < 4; ++mi)
+                    acc[ni][mi] = mfma_32x32x16_bf16(wf[ks & 1][ni], af[ks & 1][mi], acc[ni][mi]);
+        }
+    }
+    bare_barrier();   // every wave's last reads of the stage buffers are done
+
+    uint8_t* st = smem + wave * (128 * 128);     // this wave's 128 x 64 bf16 strip
+#pragma unroll
+    for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+            const int nl = 32 * ni + 8 * r4 + 4 * h;             // strip column of 4
+            const int n = n0 + 64 * wn + nl;
+            f32x4 bv = {0.0f, 0.0f, 0.0f, 0.0f};
+            if (p.bias) bv = *reinterpret_cast<const f32x4*>(p.bias + n);
+#pragma unroll
+            for (int mi = 0; mi < 4; ++mi) {
+                const int ml = 32 * mi + j;                       // strip row
+                const int m = m0 + 128 * wm + ml;
+                float o[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float z = acc[ni][mi][4 * r4 + e] + bv[e];
+                    o[e] = p.act ? gelu(z) : z;
+                }
+                if (p.res && m < p.M) {
+                    const u32x2 rv = *reinterpret_cast<const u32x2*>(p.res + (size_t)m * p.N + n);
+                    o[0] += bf16_lo(rv[0]);
+                    o[1] += bf16_hi(rv[0]);
+                    o[2] += bf16_lo(rv[1]);
+                    o[3] += bf16_hi(rv[1]);
+                }
+                const u32x2 pk = {pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+                const int c = nl >> 3;                            // 16-byte chunk of the row
+                *reinterpret_cast<u32x2*>(st + ml * 128 + 16 * (c ^ (ml & 7)) + 8 * h) = pk;
+            }
+        }
+    __syncthreads();
+
+    uint16_t* dst = p.out0;
+    int ncol0 = n0 + 64 * wn;
+    if constexpr (EPI == kEpiQkv) {
+        const int which = n0 / p.E;   // a 256-column tile never straddles Q, K and V (E % 256 == 0)
+        dst = which == 0 ? p.out0 : (which == 1 ? p.out1 : p.out2);
+        ncol0 -= which * p.E;
+    }
+    const int c = lane & 7;
+#pragma unroll 4
+    for (int it = 0; it < 16; ++it) {
+        const int ml = 8 * it + (lane >> 3);
+        const int m = m0 + 128 * wm + ml;
+        if (m >= p.M) continue;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(st + ml * 128 + 16 * (c ^ (ml & 7)));
+        size_t off;
+        if constexpr (EPI == kEpiQkv) {
+            const int nn = ncol0 + 8 * c, hh = nn / p.d, dd = nn - hh * p.d;
+            const int b = m / p.L, l = m - b * p.L;
+            off = ((size_t)(b * p.H + hh) * p.L + l) * p.d + dd;
+        } else {
+            off = (size_t)m * p.N + ncol0 + 8 * c;
+        }
+        *reinterpret_cast<u32x4*>(dst + off) = v;
     }
 }
 
@@ -283,12 +446,27 @@ __global__ __launch_bounds__(kThreads) void rsa_layernorm_bf16(const uint16_t* _
     }
 }
 
+#ifndef RSA_GEMM_BIG
+#define RSA_GEMM_BIG 1
+#endif
+
 template <int PRO, int EPI>
 hipError_t launch_gemm_t(const GemmParams& p0, hipStream_t stream) {
     GemmParams p = p0;
-    p.mt = (p.M + kGT - 1) / kGT;
-    p.nt = p.N / kGT;
-    hipLaunchKernelGGL((rsa_gemm_bf16<PRO, EPI>), dim3((unsigned)(p.mt * p.nt)), dim3(kThreads), 0, stream, p);
+    // 256x256 tiles where the widths allow them (a Q/K/V block must not
+    // straddle a 256-column tile), else 128x128
+    const bool big = RSA_GEMM_BIG && p.N % kBT == 0 && (EPI != kEpiQkv || p.E % kBT == 0);
+    if (big) {
+        p.mt = (p.M + kBT - 1) / kBT;
+        p.nt = p.N / kBT;
+        hipLaunchKernelGGL((rsa_gemm_bf16_256<PRO, EPI>), dim3((unsigned)(p.mt * p.nt)), dim3(kBigThreads), 0,
+                           stream, p);
+    } else {
+        p.mt = (p.M + kGT - 1) / kGT;
+        p.nt = p.N / kGT;
+        hipLaunchKernelGGL((rsa_gemm_bf16<PRO, EPI>), dim3((unsigned)(p.mt * p.nt)), dim3(kThreads), 0, stream,
+                           p);
+    }
     return hipGetLastError();
 }
 

@@ -91,7 +91,12 @@ def test_linear_parity(oracle_lib, M, N, K, act, bias, res):
     check_product(from_dev(out), want, S, K, f"linear {M}x{N}x{K}")
 
 
-@pytest.mark.parametrize("B,L,E,H", [(2, 96, 256, 4), (1, 130, 512, 4), (3, 64, 768, 12)])
+@pytest.mark.parametrize("B,L,E,H", [
+    (2, 96, 256, 4),      # 256-column tiles (E % 256 == 0)
+    (1, 130, 512, 4),     # d = 128, ragged rows
+    (3, 64, 768, 12),     # BERT-base widths
+    (2, 80, 384, 6),      # 128-column tiles (E % 256 != 0)
+])
 def test_qkv_and_output_projection(oracle_lib, B, L, E, H):
     from oracle import layer as OL
     dev = device()
