@@ -49,9 +49,9 @@ def _load():
         u8p = ctypes.POINTER(ctypes.c_uint8)
         i64p = ctypes.POINTER(ctypes.c_int64)
         ci = ctypes.c_int
-        lib.oracle_forward.argtypes = [dp, dp, dp, u8p, ci, ci, ci, ci, ci, ci, i64p, dp, dp]
+        lib.oracle_forward.argtypes = [dp, dp, dp, u8p, ci, ci, ci, ci, ci, ci, i64p, ci, dp, dp]
         lib.oracle_forward.restype = ci
-        lib.oracle_backward.argtypes = [dp, dp, dp, dp, u8p, ci, ci, ci, ci, ci, dp, dp, dp]
+        lib.oracle_backward.argtypes = [dp, dp, dp, dp, u8p, ci, ci, ci, ci, ci, ci, dp, dp, dp]
         lib.oracle_backward.restype = ci
         lib.oracle_num_threads.argtypes = []
         lib.oracle_num_threads.restype = ci
@@ -74,12 +74,13 @@ def num_threads() -> int:
     return int(_load().oracle_num_threads())
 
 
-def forward(q, k, v, mask=None, N: int = 1, qpos=None) -> Tuple[np.ndarray, np.ndarray]:
+def forward(q, k, v, mask=None, N: int = 1, qpos=None, causal: bool = False) -> Tuple[np.ndarray, np.ndarray]:
     """fp64 attention output and natural-log lse through RSA's ring stages.
 
     q: [B,H,Lq,d]; k, v: [B,H,L,d]; mask: [B,L] (nonzero = valid) or None;
     qpos: absolute positions of q's rows (default 0..Lq-1), which fix each
-    row's rank and so its ring order. Returns (out [B,H,Lq,d], lse [B,H,Lq]).
+    row's rank and so its ring order; causal: the row at position i sees
+    keys j <= i only. Returns (out [B,H,Lq,d], lse [B,H,Lq]).
     """
     q, k, v = _f64(q), _f64(k), _f64(v)
     B, H, Lq, d = q.shape
@@ -100,15 +101,15 @@ def forward(q, k, v, mask=None, N: int = 1, qpos=None) -> Tuple[np.ndarray, np.n
     lse = np.empty((B, H, Lq), dtype=np.float64)
     st = _load().oracle_forward(_ptr(q, ctypes.c_double), _ptr(k, ctypes.c_double),
                                 _ptr(v, ctypes.c_double), _ptr(m, ctypes.c_uint8),
-                                B, H, L, d, N, Lq, _ptr(pos, ctypes.c_int64),
+                                B, H, L, d, N, Lq, _ptr(pos, ctypes.c_int64), int(bool(causal)),
                                 _ptr(out, ctypes.c_double), _ptr(lse, ctypes.c_double))
     if st != 0:
         raise ValueError(f"oracle_forward failed with status {st}")
     return out, lse
 
 
-def backward(q, k, v, dout, mask=None, N: int = 1) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
-    """fp64 gradients (dQ, dK, dV) of <O, dO>, all [B,H,L,d]."""
+def backward(q, k, v, dout, mask=None, N: int = 1, causal: bool = False) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """fp64 gradients (dQ, dK, dV) of <O, dO>, all [B,H,L,d] (causal as in forward)."""
     q, k, v, g = _f64(q), _f64(k), _f64(v), _f64(dout)
     B, H, L, d = q.shape
     for name, a in (("k", k), ("v", v), ("dout", g)):
@@ -122,7 +123,7 @@ def backward(q, k, v, dout, mask=None, N: int = 1) -> Tuple[np.ndarray, np.ndarr
     dv = np.empty_like(q)
     st = _load().oracle_backward(_ptr(q, ctypes.c_double), _ptr(k, ctypes.c_double),
                                  _ptr(v, ctypes.c_double), _ptr(g, ctypes.c_double),
-                                 _ptr(m, ctypes.c_uint8), B, H, L, d, N,
+                                 _ptr(m, ctypes.c_uint8), B, H, L, d, N, int(bool(causal)),
                                  _ptr(dq, ctypes.c_double), _ptr(dk, ctypes.c_double),
                                  _ptr(dv, ctypes.c_double))
     if st != 0:

@@ -30,6 +30,12 @@
  * ring communication): the ordinary softmax-attention gradients of the loss
  * <O, dO>, accumulated over query chunks and ring steps in the same order.
  *
+ * Causal variant (`causal` nonzero). The pages do not mention one; it
+ * follows the standard autoregressive definition: the query at sequence
+ * position i sees key j only if j <= i, on top of the key-padding mask. The
+ * ring order is unchanged (chunks after the query's own are then entirely
+ * hidden).
+ *
  * Everything is fp64 with plain loops; no BLAS, no blocking, no reordering
  * beyond the ring order. Rows without a valid key give O = 0, lse = -inf and
  * zero gradients.
@@ -56,11 +62,11 @@ static int ring_chunk(int n, int t, int N) { return ((n - t) % N + N) % N; }
  * n = qpos[i] / (L/N) and therefore its ring order. k, v: [B,H,L,d].
  * mask: [B,L], nonzero = valid key; NULL = all keys valid.
  * out: [B,H,Lq,d]; lse: [B,H,Lq] natural-log sum-exp of the scaled scores
- * (may be NULL).
+ * (may be NULL). causal: hide keys j > qpos[i].
  */
 int oracle_forward(const double* q, const double* k, const double* v,
                    const uint8_t* mask, int B, int H, int L, int d, int N,
-                   int Lq, const int64_t* qpos, double* out, double* lse)
+                   int Lq, const int64_t* qpos, int causal, double* out, double* lse)
 {
     if (B < 0 || H < 0 || L <= 0 || d <= 0 || N <= 0 || Lq < 0 || L % N != 0)
         return ORACLE_ERR_SHAPE;
@@ -96,7 +102,7 @@ int oracle_forward(const double* q, const double* k, const double* v,
                 for (int t = 0; t < N; ++t) {
                     const int c = ring_chunk(n, t, N);
                     for (int j = c * Lc; j < (c + 1) * Lc; ++j) {
-                        ok[j] = mb ? (mb[j] != 0) : 1;
+                        ok[j] = (mb ? (mb[j] != 0) : 1) && !(causal && j > pos);
                         if (!ok[j]) continue;
                         double dot = 0.0;
                         for (int x = 0; x < d; ++x) dot += qi[x] * kh[(int64_t)j * d + x];
@@ -148,10 +154,12 @@ int oracle_forward(const double* q, const double* k, const double* v,
  *   dS_ij = P_ij (dP_ij - D_i)
  *   dQ_i  = scale * sum_j dS_ij k_j
  *   dK_j += scale * dS_ij q_i,   dV_j += P_ij dO_i.
+ *
+ * causal: keys j > i are hidden from row i (P_ij = 0).
  */
 int oracle_backward(const double* q, const double* k, const double* v,
                     const double* dout, const uint8_t* mask, int B, int H, int L,
-                    int d, int N, double* dq, double* dk, double* dv)
+                    int d, int N, int causal, double* dq, double* dk, double* dv)
 {
     if (B < 0 || H < 0 || L <= 0 || d <= 0 || N <= 0 || L % N != 0)
         return ORACLE_ERR_SHAPE;
@@ -196,7 +204,7 @@ int oracle_backward(const double* q, const double* k, const double* v,
                         for (int t = 0; t < N; ++t) {
                             const int c = ring_chunk(n, t, N);
                             for (int j = c * Lc; j < (c + 1) * Lc; ++j) {
-                                ok[j] = mb ? (mb[j] != 0) : 1;
+                                ok[j] = (mb ? (mb[j] != 0) : 1) && !(causal && j > i);
                                 if (!ok[j]) continue;
                                 double dot = 0.0;
                                 for (int x = 0; x < d; ++x) dot += qi[x] * kh[(int64_t)j * d + x];
