@@ -59,6 +59,8 @@ def parse():
     ap.add_argument("--forward-variant", default="fused", choices=("fused", "twopass"),
                     help="fused online-softmax kernel, or the two-stage form with score rows in HBM "
                          "(implies --forward-only)")
+    ap.add_argument("--causal", action="store_true",
+                    help="the causal variant (row i sees keys j <= i); the backward is timed as one call")
     ap.add_argument("--capacity", action="store_true",
                     help="single-GPU sequence-length capacity of the fused and the two-stage forward "
                          "(B=H=1, d=64) instead of the step benchmark")
@@ -109,7 +111,18 @@ def valid_key_count(w, x):
     return int(x["valid_len"].sum())
 
 
-def cpu_baseline(w, x, threads):
+def pair_count(w, x, causal):
+    """(query row, visible valid key) pairs of one head, summed over batch
+    rows: Lq * valid keys, or with the causal mask sum_i min(i + 1, valid)
+    over the query positions i (keys are valid up to a prefix length)."""
+    vls = [w.L] * w.B if x["mask"] is None else [int(v) for v in x["valid_len"]]
+    if not causal:
+        return float(w.Lq * sum(vls))
+    pos = np.arange(w.Lq, dtype=np.int64) + (w.rank * w.Lc if w.rank is not None else 0)
+    return float(sum(np.minimum(pos + 1, vl).sum() for vl in vls))
+
+
+def cpu_baseline(w, x, threads, causal=False):
     """fp64 oracle, forward (+ backward) on `threads` heads of batch row 0
     (full sequence length), timed once."""
     import oracle
@@ -120,20 +133,23 @@ def cpu_baseline(w, x, threads):
     q, k, v = x["q"][sl], x["k"][sl], x["v"][sl]
     vl = w.L if x["mask"] is None else int(x["valid_len"][0])
     t0 = time.perf_counter()
+    rows = np.arange(w.Lq) + (w.rank * w.Lc if w.rank is not None else 0)
+    pairs = float(np.minimum(rows + 1, vl).sum()) if causal else float(w.Lq * vl)
     if w.rank is not None:
-        pos = np.arange(w.rank * w.Lc, (w.rank + 1) * w.Lc)
-        oracle.forward(q, k, v, m, N=w.N, qpos=pos)
-        flops = 4.0 * heads * w.Lc * vl * w.d
+        oracle.forward(q, k, v, m, N=w.N, qpos=rows, causal=causal)
+        flops = 4.0 * heads * pairs * w.d
         what = "forward"
     else:
-        oracle.forward(q, k, v, m, N=w.N)
-        flops = 4.0 * heads * w.L * vl * w.d
+        oracle.forward(q, k, v, m, N=w.N, causal=causal)
+        flops = 4.0 * heads * pairs * w.d
         what = "forward"
         if x.get("dout") is not None:
             g = x["dout"][sl]
-            oracle.backward(q, k, v, g, m, N=w.N)
-            flops += 8.0 * heads * w.L * vl * w.d
+            oracle.backward(q, k, v, g, m, N=w.N, causal=causal)
+            flops += 8.0 * heads * pairs * w.d
             what = "forward+backward"
+    if causal:
+        what = "causal " + what
     dt = time.perf_counter() - t0
     return {
         "value": flops / dt / 1e12,
@@ -340,8 +356,9 @@ def main():
         print(f"workload {w.name} is CPU-only", file=sys.stderr)
         return 2
     twopass = args.forward_variant == "twopass"
-    if twopass and (w.rank is not None or w.dtype != "bf16"):
-        print("the two-stage forward covers full-sequence bf16 workloads", file=sys.stderr)
+    causal = args.causal
+    if twopass and (w.rank is not None or w.dtype != "bf16" or causal):
+        print("the two-stage forward covers full-sequence, non-causal bf16 workloads", file=sys.stderr)
         return 2
     dev = torch.device("cuda:0")
     with_dout = w.rank is None
@@ -367,8 +384,14 @@ def main():
     if twopass:
         ws = torch.empty(rsa.forward_twopass_workspace_bytes(w.B, w.H, w.L, w.d, w.N), dtype=torch.uint8,
                          device=dev)
+    bws = None
+    if do_bwd and causal:
+        bws = torch.empty(rsa.backward_workspace_bytes(w.B, w.H, w.L, w.d, w.N), dtype=torch.uint8, device=dev)
 
-    names = ["forward"] + (["bwd_preprocess", "bwd_dq", "bwd_dkdv"] if do_bwd else [])
+    if causal:
+        names = ["forward"] + (["backward"] if do_bwd else [])
+    else:
+        names = ["forward"] + (["bwd_preprocess", "bwd_dq", "bwd_dkdv"] if do_bwd else [])
 
     def step(ev=None):
         def mark(i):
@@ -378,11 +401,14 @@ def main():
         if twopass:
             rsa.forward_twopass(q, k, v, mask, N=w.N, out=out, lse=lse, workspace=ws)
         elif w.rank is not None:
-            rsa.forward_rank(q, k, v, mask, N=w.N, rank=w.rank, out=out, lse=lse, workspace=ws)
+            rsa.forward_rank(q, k, v, mask, N=w.N, rank=w.rank, out=out, lse=lse, workspace=ws, causal=causal)
         else:
-            rsa.forward(q, k, v, mask, N=w.N, out=out, lse=lse)
+            rsa.forward(q, k, v, mask, N=w.N, out=out, lse=lse, causal=causal)
         mark(1)
-        if do_bwd:
+        if do_bwd and causal:
+            rsa.backward(q, k, v, out, g, lse, mask, N=w.N, dq=dq, dk=dk, dv=dv, workspace=bws, causal=True)
+            mark(2)
+        elif do_bwd:
             rsa.backward_preprocess(out, g, lse, rowstats=stats)
             mark(2)
             rsa.backward_dq(q, k, v, g, stats, mask, N=w.N, dq=dq)
@@ -421,18 +447,19 @@ def main():
         per_kernel[name] = {"avg_ms": float(np.mean(durs)), "median_ms": float(np.median(durs)),
                             "p10_ms": float(np.percentile(durs, 10)), "p90_ms": float(np.percentile(durs, 90))}
 
-    # algorithmic work
-    lk_valid = valid_key_count(w, x)         # sum over batch rows of valid keys
-    unit = w.H * w.Lq * w.d                  # per (batch row, valid key)
-    fwd_flops = 4.0 * unit * lk_valid
-    fwd_flops_nominal = 4.0 * w.B * unit * w.L
-    bwd_flops = 8.0 * unit * lk_valid if do_bwd else 0.0
+    # algorithmic work: 4 d flops per visible (query, key) pair forward, 8 d backward
+    pairs = w.H * pair_count(w, x, causal)
+    fwd_flops = 4.0 * w.d * pairs
+    fwd_flops_nominal = 4.0 * w.B * w.H * w.Lq * w.L * w.d
+    bwd_flops = 8.0 * w.d * pairs if do_bwd else 0.0
     step_flops = fwd_flops + bwd_flops
     value = step_flops / (ms_per_step * 1e-3) / 1e12
     peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_MATRIX_TFLOPS
 
-    credited = {"forward": fwd_flops, "bwd_dq": 4.0 * unit * lk_valid, "bwd_dkdv": 4.0 * unit * lk_valid}
-    executed = {"forward": fwd_flops, "bwd_dq": 6.0 * unit * lk_valid, "bwd_dkdv": 8.0 * unit * lk_valid}
+    credited = {"forward": fwd_flops, "bwd_dq": 4.0 * w.d * pairs, "bwd_dkdv": 4.0 * w.d * pairs,
+                "backward": 8.0 * w.d * pairs}
+    executed = {"forward": fwd_flops, "bwd_dq": 6.0 * w.d * pairs, "bwd_dkdv": 8.0 * w.d * pairs,
+                "backward": 14.0 * w.d * pairs}
     for name in names:
         avg_s = per_kernel[name]["avg_ms"] * 1e-3
         if name in credited:
@@ -464,13 +491,14 @@ def main():
         achieved = credited[dominant] / dom_s / 1e12
         roofline = {
             "kernel": {"forward": "rsa_fwd_kernel" if w.rank is None else "rsa_fwd_kernel + rsa_merge_kernel",
-                       "bwd_dq": "rsa_bwd_dq", "bwd_dkdv": "rsa_bwd_dkdv"}[dominant],
+                       "bwd_dq": "rsa_bwd_dq", "bwd_dkdv": "rsa_bwd_dkdv",
+                       "backward": "rsa_bwd_pre + rsa_bwd_dq + rsa_bwd_dkdv"}[dominant],
             "bound": "mfma",
             "achieved": achieved,
             "peak": peak,
             "unit": "TFLOP/s",
             "frac": achieved / peak,
-            "traffic": recorded_traffic(w.name, dominant),
+            "traffic": None if causal else recorded_traffic(w.name, dominant),
             "traffic_unit": "bytes per launch (calibrated FETCH_SIZE + WRITE_SIZE)",
             "avg_ms": per_kernel[dominant]["avg_ms"],
             "flops_per_launch": credited[dominant],
@@ -492,7 +520,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "L": w.L, "d": w.d, "N": w.N,
                    "rank": w.rank, "key_mask": w.valid_range is not None,
-                   "pass": "fwd+bwd" if do_bwd else "fwd", "forward": args.forward_variant,
+                   "pass": "fwd+bwd" if do_bwd else "fwd", "forward": args.forward_variant, "causal": causal,
                    "description": w.description},
         "fwd_tflops": fwd_flops / fwd_s / 1e12,
         "fwd_tflops_nominal_keys": fwd_flops_nominal / fwd_s / 1e12,
@@ -508,7 +536,7 @@ def main():
     if not args.no_cpu_baseline:
         threads = len(os.sched_getaffinity(0))
         os.environ.setdefault("OMP_NUM_THREADS", str(min(threads, 16)))
-        line["cpu_baseline"] = cpu_baseline(w, x, int(os.environ["OMP_NUM_THREADS"]))
+        line["cpu_baseline"] = cpu_baseline(w, x, int(os.environ["OMP_NUM_THREADS"]), causal)
     else:
         line["cpu_baseline"] = None
     print(json.dumps(line), flush=True)

@@ -60,6 +60,15 @@ typedef enum rsa_status {
 typedef enum rsa_dtype { RSA_F32 = 0, RSA_BF16 = 1 } rsa_dtype;
 
 /*
+ * Flags of the *_ex entry points. RSA_CAUSAL: the query at sequence position
+ * i sees the keys at positions j <= i only (on top of key_mask). The pages
+ * describe no causal variant; this is the standard autoregressive mask. In
+ * ring order rank n then meets its own chunk first, chunks n-1 .. 0 after it,
+ * and the chunks after its own not at all (their tiles are skipped).
+ */
+#define RSA_CAUSAL 1
+
+/*
  * Full RSA forward: all N ranks' shares at once. Rank n owns query rows
  * [n*L/N, (n+1)*L/N) and visits key/value chunks (n - t) mod N for
  * t = 0..N-1 (ABSTRACT: each chunk on its own device, attention output
@@ -72,6 +81,11 @@ typedef enum rsa_dtype { RSA_F32 = 0, RSA_BF16 = 1 } rsa_dtype;
 int rsa_forward(const void* q, const void* k, const void* v, const uint8_t* key_mask,
                 int B, int H, int L, int d, int N, int dtype,
                 void* stream, void* out, float* lse);
+
+/* rsa_forward with flags (0 or RSA_CAUSAL; other bits: RSA_ERR_UNSUPPORTED). */
+int rsa_forward_ex(const void* q, const void* k, const void* v, const uint8_t* key_mask,
+                   int B, int H, int L, int d, int N, int dtype, int flags,
+                   void* stream, void* out, float* lse);
 
 /*
  * One rank's share, as one device of the ring computes it (ABSTRACT: no
@@ -89,6 +103,12 @@ int rsa_forward_rank(const void* q_local, const void* k, const void* v, const ui
                      int B, int H, int L, int d, int N, int rank, int dtype,
                      void* workspace, size_t workspace_bytes,
                      void* stream, void* out_local, float* lse_local);
+
+/* rsa_forward_rank with flags (query positions rank * L/N + row). */
+int rsa_forward_rank_ex(const void* q_local, const void* k, const void* v, const uint8_t* key_mask,
+                        int B, int H, int L, int d, int N, int rank, int dtype, int flags,
+                        void* workspace, size_t workspace_bytes,
+                        void* stream, void* out_local, float* lse_local);
 
 /* Workspace bytes rsa_forward_rank needs for these sizes (0 if they are invalid). */
 size_t rsa_forward_rank_workspace_bytes(int B, int H, int L, int d, int N);
@@ -135,6 +155,14 @@ int rsa_backward(const void* q, const void* k, const void* v, const void* out, c
                  int B, int H, int L, int d, int N, int dtype,
                  void* workspace, size_t workspace_bytes,
                  void* stream, void* dq, void* dk, void* dv);
+
+/* rsa_backward with flags; out and lse must come from the forward with the
+ * same flags. */
+int rsa_backward_ex(const void* q, const void* k, const void* v, const void* out, const void* dout,
+                    const float* lse, const uint8_t* key_mask,
+                    int B, int H, int L, int d, int N, int dtype, int flags,
+                    void* workspace, size_t workspace_bytes,
+                    void* stream, void* dq, void* dk, void* dv);
 
 /* Workspace bytes rsa_backward needs for these sizes (0 if they are invalid). */
 size_t rsa_backward_workspace_bytes(int B, int H, int L, int d, int N, int dtype);

@@ -37,6 +37,7 @@ __all__ = [
 
 RSA_F32 = 0
 RSA_BF16 = 1
+RSA_CAUSAL = 1
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "librsa.so")
@@ -49,12 +50,17 @@ _sz = ctypes.c_size_t
 # (name, restype, argtypes) for every symbol of include/rsa.h
 SIGNATURES = {
     "rsa_forward": (_ci, [_vp, _vp, _vp, _vp, _ci, _ci, _ci, _ci, _ci, _ci, _vp, _vp, _vp]),
+    "rsa_forward_ex": (_ci, [_vp, _vp, _vp, _vp, _ci, _ci, _ci, _ci, _ci, _ci, _ci, _vp, _vp, _vp]),
     "rsa_forward_rank": (_ci, [_vp, _vp, _vp, _vp, _ci, _ci, _ci, _ci, _ci, _ci, _ci, _vp, _sz, _vp, _vp, _vp]),
+    "rsa_forward_rank_ex": (_ci, [_vp, _vp, _vp, _vp, _ci, _ci, _ci, _ci, _ci, _ci, _ci, _ci, _vp, _sz, _vp, _vp,
+                                  _vp]),
     "rsa_forward_rank_workspace_bytes": (_sz, [_ci, _ci, _ci, _ci, _ci]),
     "rsa_forward_twopass": (_ci, [_vp, _vp, _vp, _vp, _ci, _ci, _ci, _ci, _ci, _ci, _vp, _sz, _vp, _vp, _vp]),
     "rsa_forward_twopass_workspace_bytes": (_sz, [_ci, _ci, _ci, _ci, _ci]),
     "rsa_backward": (_ci, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _ci, _ci, _ci, _ci, _ci, _ci,
                            _vp, _sz, _vp, _vp, _vp, _vp]),
+    "rsa_backward_ex": (_ci, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _ci, _ci, _ci, _ci, _ci, _ci, _ci,
+                              _vp, _sz, _vp, _vp, _vp, _vp]),
     "rsa_backward_workspace_bytes": (_sz, [_ci, _ci, _ci, _ci, _ci, _ci]),
     "rsa_backward_preprocess": (_ci, [_vp, _vp, _vp, _ci, _ci, _ci, _ci, _ci, _vp, _vp]),
     "rsa_backward_dq": (_ci, [_vp, _vp, _vp, _vp, _vp, _vp, _ci, _ci, _ci, _ci, _ci, _ci, _vp, _vp]),
@@ -145,8 +151,10 @@ def _mask(key_mask, B, L, device):
     return key_mask
 
 
-def forward(q, k, v, key_mask=None, N: int = 1, return_lse: bool = False, out=None, lse=None):
-    """RSA forward over all N ranks: softmax(q k^T / sqrt(d) + mask) v."""
+def forward(q, k, v, key_mask=None, N: int = 1, return_lse: bool = False, out=None, lse=None,
+            causal: bool = False):
+    """RSA forward over all N ranks: softmax(q k^T / sqrt(d) + mask) v
+    (causal: the row at position i sees keys j <= i only)."""
     B, H, L, d = q.shape
     dev = q.device
     _need(q, "q", (B, H, L, d), q.dtype, dev)
@@ -161,8 +169,12 @@ def forward(q, k, v, key_mask=None, N: int = 1, return_lse: bool = False, out=No
         lse = torch.empty((B, H, L), dtype=torch.float32, device=dev)
     if lse is not None:
         _need(lse, "lse", (B, H, L), torch.float32, dev)
-    st = load().rsa_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(m), B, H, L, d, int(N), code,
-                            _stream(dev), _ptr(out), _ptr(lse))
+    if causal:
+        st = load().rsa_forward_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(m), B, H, L, d, int(N), code, RSA_CAUSAL,
+                                   _stream(dev), _ptr(out), _ptr(lse))
+    else:
+        st = load().rsa_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(m), B, H, L, d, int(N), code,
+                                _stream(dev), _ptr(out), _ptr(lse))
     if st != 0:
         raise RSAError(st, "rsa_forward")
     return (out, lse) if (return_lse or lse is not None) else out
@@ -173,7 +185,7 @@ def forward_rank_workspace_bytes(B: int, H: int, L: int, d: int, N: int) -> int:
 
 
 def forward_rank(q_local, k, v, key_mask=None, N: int = 1, rank: int = 0, return_lse: bool = False,
-                 out=None, lse=None, workspace=None):
+                 out=None, lse=None, workspace=None, causal: bool = False):
     """One rank's share: q_local [B,H,L/N,d] against all L keys in that rank's ring order."""
     B, H, L, d = k.shape
     dev = k.device
@@ -194,9 +206,15 @@ def forward_rank(q_local, k, v, key_mask=None, N: int = 1, rank: int = 0, return
     need = forward_rank_workspace_bytes(B, H, L, d, N)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
-    st = load().rsa_forward_rank(_ptr(q_local), _ptr(k), _ptr(v), _ptr(m), B, H, L, d, int(N), int(rank),
-                                 code, _ptr(workspace), workspace.numel() * workspace.element_size(),
-                                 _stream(dev), _ptr(out), _ptr(lse))
+    if causal:
+        st = load().rsa_forward_rank_ex(_ptr(q_local), _ptr(k), _ptr(v), _ptr(m), B, H, L, d, int(N), int(rank),
+                                        code, RSA_CAUSAL, _ptr(workspace),
+                                        workspace.numel() * workspace.element_size(), _stream(dev), _ptr(out),
+                                        _ptr(lse))
+    else:
+        st = load().rsa_forward_rank(_ptr(q_local), _ptr(k), _ptr(v), _ptr(m), B, H, L, d, int(N), int(rank),
+                                     code, _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                     _stream(dev), _ptr(out), _ptr(lse))
     if st != 0:
         raise RSAError(st, "rsa_forward_rank")
     return (out, lse) if (return_lse or lse is not None) else out
@@ -292,8 +310,10 @@ def backward_dkdv(q, k, v, dout, rowstats, key_mask=None, N: int = 1, dk=None, d
     return dk, dv
 
 
-def backward(q, k, v, out, dout, lse, key_mask=None, N: int = 1, dq=None, dk=None, dv=None, workspace=None):
-    """Gradients (dq, dk, dv) of <out, dout>; out and lse come from forward()."""
+def backward(q, k, v, out, dout, lse, key_mask=None, N: int = 1, dq=None, dk=None, dv=None, workspace=None,
+             causal: bool = False):
+    """Gradients (dq, dk, dv) of <out, dout>; out and lse come from forward()
+    with the same causal setting."""
     B, H, L, d = q.shape
     dev = q.device
     for name, t in (("q", q), ("k", k), ("v", v), ("out", out), ("dout", dout)):
@@ -309,10 +329,16 @@ def backward(q, k, v, out, dout, lse, key_mask=None, N: int = 1, dq=None, dk=Non
     need = backward_workspace_bytes(B, H, L, d, N, code)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
-    st = load().rsa_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(lse), _ptr(m),
-                             B, H, L, d, int(N), code, _ptr(workspace),
-                             workspace.numel() * workspace.element_size(), _stream(dev),
-                             _ptr(dq), _ptr(dk), _ptr(dv))
+    if causal:
+        st = load().rsa_backward_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(lse), _ptr(m),
+                                    B, H, L, d, int(N), code, RSA_CAUSAL, _ptr(workspace),
+                                    workspace.numel() * workspace.element_size(), _stream(dev),
+                                    _ptr(dq), _ptr(dk), _ptr(dv))
+    else:
+        st = load().rsa_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(lse), _ptr(m),
+                                 B, H, L, d, int(N), code, _ptr(workspace),
+                                 workspace.numel() * workspace.element_size(), _stream(dev),
+                                 _ptr(dq), _ptr(dk), _ptr(dv))
     if st != 0:
         raise RSAError(st, "rsa_backward")
     return dq, dk, dv

@@ -90,9 +90,16 @@ extern "C" {
 int rsa_forward(const void* q, const void* k, const void* v, const uint8_t* key_mask,
                 int B, int H, int L, int d, int N, int dtype,
                 void* stream, void* out, float* lse) {
+    return rsa_forward_ex(q, k, v, key_mask, B, H, L, d, N, dtype, 0, stream, out, lse);
+}
+
+int rsa_forward_ex(const void* q, const void* k, const void* v, const uint8_t* key_mask,
+                   int B, int H, int L, int d, int N, int dtype, int flags,
+                   void* stream, void* out, float* lse) {
     if (!q || !k || !v || !out) return RSA_ERR_NULL;
     int st = check_sizes(B, H, L, d, N, dtype);
     if (st != RSA_OK) return st;
+    if (flags & ~RSA_CAUSAL) return RSA_ERR_UNSUPPORTED;
     if (L > kMaxL) return RSA_ERR_UNSUPPORTED;
     if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) ||
         !aligned(key_mask, 16) || !aligned(lse, 4))
@@ -114,6 +121,7 @@ int rsa_forward(const void* q, const void* k, const void* v, const uint8_t* key_
     c.q_pos0 = 0;
     c.groups = 1;
     c.bf16 = dtype == RSA_BF16;
+    c.causal = (flags & RSA_CAUSAL) != 0;
     return launch_status(rsa::launch_forward(c, static_cast<hipStream_t>(stream)));
 }
 
@@ -128,9 +136,18 @@ int rsa_forward_rank(const void* q_local, const void* k, const void* v, const ui
                      int B, int H, int L, int d, int N, int rank, int dtype,
                      void* workspace, size_t workspace_bytes,
                      void* stream, void* out_local, float* lse_local) {
+    return rsa_forward_rank_ex(q_local, k, v, key_mask, B, H, L, d, N, rank, dtype, 0, workspace, workspace_bytes,
+                               stream, out_local, lse_local);
+}
+
+int rsa_forward_rank_ex(const void* q_local, const void* k, const void* v, const uint8_t* key_mask,
+                        int B, int H, int L, int d, int N, int rank, int dtype, int flags,
+                        void* workspace, size_t workspace_bytes,
+                        void* stream, void* out_local, float* lse_local) {
     if (!q_local || !k || !v || !out_local) return RSA_ERR_NULL;
     int st = check_sizes(B, H, L, d, N, dtype);
     if (st != RSA_OK) return st;
+    if (flags & ~RSA_CAUSAL) return RSA_ERR_UNSUPPORTED;
     if (rank < 0 || rank >= N) return RSA_ERR_SHAPE;
     if (!aligned(q_local, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out_local, 16) ||
         !aligned(key_mask, 16) || !aligned(lse_local, 4) || !aligned(workspace, 16))
@@ -157,6 +174,7 @@ int rsa_forward_rank(const void* q_local, const void* k, const void* v, const ui
     c.q_pos0 = rank * (L / N);
     c.groups = g;
     c.bf16 = dtype == RSA_BF16;
+    c.causal = (flags & RSA_CAUSAL) != 0;
     return launch_status(rsa::launch_forward(c, static_cast<hipStream_t>(stream)));
 }
 
@@ -207,9 +225,19 @@ int rsa_backward(const void* q, const void* k, const void* v, const void* out, c
                  int B, int H, int L, int d, int N, int dtype,
                  void* workspace, size_t workspace_bytes,
                  void* stream, void* dq, void* dk, void* dv) {
+    return rsa_backward_ex(q, k, v, out, dout, lse, key_mask, B, H, L, d, N, dtype, 0, workspace, workspace_bytes,
+                           stream, dq, dk, dv);
+}
+
+int rsa_backward_ex(const void* q, const void* k, const void* v, const void* out, const void* dout,
+                    const float* lse, const uint8_t* key_mask,
+                    int B, int H, int L, int d, int N, int dtype, int flags,
+                    void* workspace, size_t workspace_bytes,
+                    void* stream, void* dq, void* dk, void* dv) {
     if (!q || !k || !v || !out || !dout || !lse || !dq || !dk || !dv) return RSA_ERR_NULL;
     int st = check_backward(B, H, L, d, N, dtype);
     if (st != RSA_OK) return st;
+    if (flags & ~RSA_CAUSAL) return RSA_ERR_UNSUPPORTED;
     if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) || !aligned(dout, 16) ||
         !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) || !aligned(key_mask, 16) ||
         !aligned(lse, 4) || !aligned(workspace, 16))
@@ -220,6 +248,7 @@ int rsa_backward(const void* q, const void* k, const void* v, const void* out, c
     c.dq = dq;
     c.dk = dk;
     c.dv = dv;
+    c.causal = (flags & RSA_CAUSAL) != 0;
     return launch_status(rsa::launch_backward(c, rsa::kBwdStageAll, static_cast<hipStream_t>(stream)));
 }
 

@@ -53,6 +53,7 @@ struct BwdParams {
     int H, L, N, Lc, BH, nt;   // nt: 128-row tiles per head
     float sl2;                 // log2(e) / sqrt(d)
     float scale;               // 1 / sqrt(d)
+    int causal;                // the query at position i sees keys at positions <= i only
 };
 
 // Sequence position of the u-th query row that key chunk c meets: ring step
@@ -106,7 +107,7 @@ __device__ __forceinline__ void load_rowvec(uint8_t* lds, const float* src, RowO
 // Query-stationary, mirror of the forward: 4 waves x 32 query rows; per key
 // tile S^T = K Q^T and dP^T = V dO^T (lane <-> query), then
 // dQ^T += K^T dS^T with K^T from the transposing read of the same K tile.
-template <int D, bool CONTIG>
+template <int D, bool CONTIG, bool CAUSAL>
 __global__ __launch_bounds__(kThreads, D == 64 ? 3 : 1) void rsa_bwd_dq(BwdParams p) {
     using T = DirectTile<D>;
     constexpr int BUF = 2 * T::BYTES;   // K, V
@@ -133,7 +134,11 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 3 : 1) void rsa_bwd_dq(BwdParam
     const uint8_t* mrow = p.mask ? p.mask + (size_t)b * p.L : nullptr;
     const size_t rows_all = (size_t)p.BH * p.L;
 
-    tflag.build(ntile, kThreads, [&](int t) { return key_tile_flags(mrow, n, p.N, p.Lc, CONTIG, t * kKT, p.L); });
+    const int qhi = min(row0 + 128, p.L) - 1;
+    tflag.build(ntile, kThreads, [&](int t) {
+        const uint32_t f = key_tile_flags(mrow, n, p.N, p.Lc, CONTIG, t * kKT, p.L);
+        return CAUSAL ? f & causal_tile_class(t * kKT, min(kKT, p.L - t * kKT), n, p.N, p.Lc, CONTIG, row0, qhi) : f;
+    });
 
     u32x4 qf[D / 16], gf[D / 16];
 #pragma unroll
@@ -212,8 +217,10 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 3 : 1) void rsa_bwd_dq(BwdParam
         const uint8_t* vb = kb + T::BYTES;
         // key acc_row(r, h) = 8 (r / 4) + 4 h + r % 4 of a 32-key half: after one
         // shift by 4 h every bit position is a constant
-        const uint64_t bits =
-            (tflag.get(t) & 2) ? ~0ull : key_tile_bits(mrow, n, p.N, p.Lc, CONTIG, t * kKT, p.L) >> (4 * h);
+        const bool partial = !(tflag.get(t) & 2);
+        const uint64_t bits = partial ? key_tile_bits(mrow, n, p.N, p.Lc, CONTIG, t * kKT, p.L) >> (4 * h) : ~0ull;
+        // causal: key i of a chunk-aligned tile sits at position kp0 + i
+        const int kp0 = (CAUSAL && CONTIG) ? ring_pos(t * kKT, n, p.N, p.Lc) : 0;
         // two 32-key halves in turn, to bound the live registers
 #pragma unroll 1
         for (int kb2 = 0; kb2 < 2; ++kb2) {
@@ -242,6 +249,21 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 3 : 1) void rsa_bwd_dq(BwdParam
 #pragma unroll
                 for (int r = 0; r < 16; ++r)
                     if (!((hb >> (8 * (r >> 2) + (r & 3))) & 1u)) s[r] = -INFINITY;
+            }
+            if (CAUSAL && partial) {   // keys after this lane's row
+                const int rel = row - kp0 - 32 * kb2 - 4 * h;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int i = 8 * (r >> 2) + (r & 3);
+                    bool hide;
+                    if constexpr (CONTIG) {
+                        hide = i > rel;
+                    } else {
+                        const int vk = t * kKT + 32 * kb2 + 4 * h + i;
+                        hide = vk < p.L && ring_pos(vk, n, p.N, p.Lc) > row;
+                    }
+                    if (hide) s[r] = -INFINITY;
+                }
             }
             uint32_t pk[8];
 #pragma unroll
@@ -302,7 +324,7 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 3 : 1) void rsa_bwd_dq(BwdParam
 // dO V^T (lane <-> key, registers <-> query rows), P and dS elementwise, then
 // dV^T += dO^T P and dK^T += Q^T dS, with Q^T and dO^T from the transposing
 // read of the same Q and dO tiles.
-template <int D, bool CONTIG>
+template <int D, bool CONTIG, bool CAUSAL>
 __global__ __launch_bounds__(kThreads, D == 64 ? 3 : 1) void rsa_bwd_dkdv(BwdParams p) {
     using T = DirectTile<D>;
     constexpr int NBUF = 3;
@@ -358,7 +380,17 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 3 : 1) void rsa_bwd_dkdv(BwdPar
             dv[db][r] = 0.0f;
         }
 
-    const int ntq = (p.L + kKT - 1) / kKT;
+    // Query tiles in ring delivery order. Causal with chunk-aligned tiles:
+    // rows before this workgroup's first key see none of its keys, and in
+    // delivery order (query chunk c, c + 1, ..., N - 1, 0, ..., c - 1) the
+    // visible rows form one run, from the tile holding row key0 to the end
+    // of chunk N - 1. Otherwise every tile is visited.
+    int tbeg = 0, ntq = (p.L + kKT - 1) / kKT;
+    if (CONTIG && CAUSAL) {
+        tbeg = (key0 - c * p.Lc) / kKT;
+        ntq = (p.N - c) * (p.Lc / kKT);
+    }
+    const int key_last = min(key0 + 127, p.L - 1);
     // The K and V fragments have landed (waited for here, so that the
     // compiler keeps no wait for them inside the tile loop).
     __builtin_amdgcn_s_waitcnt(0);
@@ -415,6 +447,10 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 3 : 1) void rsa_bwd_dkdv(BwdPar
         const float* nDs = reinterpret_cast<const float*>(gb + T::BYTES);
         const float* nLs = nDs + kKT;
         if (t + 2 < ntq) load(t + 2, FB);
+        // causal: does some row of this tile come before some key of the
+        // workgroup (then rows are masked per element)?
+        const int pos0c = (CAUSAL && CONTIG) ? ring_pos_rev(t * kKT, c, p.N, p.Lc) : 0;
+        const bool cmask = CAUSAL && (!CONTIG || pos0c < key_last);
         // two 32-query halves in turn, to bound the live registers
 #pragma unroll
         for (int qb2 = 0; qb2 < 2; ++qb2) {
@@ -449,6 +485,21 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 3 : 1) void rsa_bwd_dkdv(BwdPar
                     qtf[hs][db] = T::tfrag(qb, 32 * qb2 + 16 * hs, 32 * db);
                     gtf[hs][db] = T::tfrag(gb, 32 * qb2 + 16 * hs, 32 * db);
                 }
+            if (cmask) {   // causal: rows before this lane's key see nothing of it
+                const int rel = key - pos0c - 32 * qb2 - 4 * h;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int u = 8 * (r >> 2) + (r & 3);   // row 32 qb2 + 4 h + u of the tile
+                    bool hide;
+                    if constexpr (CONTIG) {
+                        hide = rel > u;
+                    } else {
+                        const int uu = t * kKT + 32 * qb2 + 4 * h + u;
+                        hide = uu < p.L && key > ring_pos_rev(uu, c, p.N, p.Lc);
+                    }
+                    if (hide) s[r] = -INFINITY;
+                }
+            }
             uint32_t pp[8], pd[8];
 #pragma unroll
             for (int r4 = 0; r4 < 4; ++r4) {
@@ -488,20 +539,20 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 3 : 1) void rsa_bwd_dkdv(BwdPar
         return false;
     };
 
-    load(0, 0);
-    if (ntq > 1) {
-        load(1, 1);
+    load(tbeg, 0);
+    if (ntq > tbeg + 1) {
+        load(tbeg + 1, 1);
         wait_tile_copies_but_one();
     } else {
         vm_wait<0>();
     }
-    fix_tail(0, 0);
+    fix_tail(tbeg, 0);
     bare_barrier();
     {
         using C0 = std::integral_constant<int, 0>;
         using C1 = std::integral_constant<int, 1>;
         using C2 = std::integral_constant<int, 2>;
-        int t = 0;
+        int t = tbeg;
         while (true) {
             if (body(C0{}, t++)) break;
             if (body(C1{}, t++)) break;
@@ -554,6 +605,7 @@ BwdParams make_params(const BackwardCall& c) {
     p.BH = c.B * c.H;
     p.nt = (c.L + 127) / 128;
     p.scale = (float)(1.0 / __builtin_sqrt((double)c.d));
+    p.causal = c.causal ? 1 : 0;
     p.sl2 = (float)(1.4426950408889634 / __builtin_sqrt((double)c.d));
     return p;
 }
@@ -572,18 +624,26 @@ hipError_t launch_t(const BackwardCall& c, int stages, hipStream_t stream) {
     }
     const unsigned blocks = (unsigned)((long long)p.nt * p.BH);
     if (stages & kBwdStageDq) {
-        if (contig)
-            hipLaunchKernelGGL((rsa_bwd_dq<D, true>), dim3(blocks), dim3(kThreads), 0, stream, p);
+        if (contig && !p.causal)
+            hipLaunchKernelGGL((rsa_bwd_dq<D, true, false>), dim3(blocks), dim3(kThreads), 0, stream, p);
+        else if (!p.causal)
+            hipLaunchKernelGGL((rsa_bwd_dq<D, false, false>), dim3(blocks), dim3(kThreads), 0, stream, p);
+        else if (contig)
+            hipLaunchKernelGGL((rsa_bwd_dq<D, true, true>), dim3(blocks), dim3(kThreads), 0, stream, p);
         else
-            hipLaunchKernelGGL((rsa_bwd_dq<D, false>), dim3(blocks), dim3(kThreads), 0, stream, p);
+            hipLaunchKernelGGL((rsa_bwd_dq<D, false, true>), dim3(blocks), dim3(kThreads), 0, stream, p);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
     if (stages & kBwdStageDkDv) {
-        if (contig)
-            hipLaunchKernelGGL((rsa_bwd_dkdv<D, true>), dim3(blocks), dim3(kThreads), 0, stream, p);
+        if (contig && !p.causal)
+            hipLaunchKernelGGL((rsa_bwd_dkdv<D, true, false>), dim3(blocks), dim3(kThreads), 0, stream, p);
+        else if (!p.causal)
+            hipLaunchKernelGGL((rsa_bwd_dkdv<D, false, false>), dim3(blocks), dim3(kThreads), 0, stream, p);
+        else if (contig)
+            hipLaunchKernelGGL((rsa_bwd_dkdv<D, true, true>), dim3(blocks), dim3(kThreads), 0, stream, p);
         else
-            hipLaunchKernelGGL((rsa_bwd_dkdv<D, false>), dim3(blocks), dim3(kThreads), 0, stream, p);
+            hipLaunchKernelGGL((rsa_bwd_dkdv<D, false, true>), dim3(blocks), dim3(kThreads), 0, stream, p);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }

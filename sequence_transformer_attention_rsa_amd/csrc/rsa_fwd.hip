@@ -66,6 +66,7 @@ struct FwdParams {
     float sl2;        // log2(e) / sqrt(d)
     float tau_raw;    // lazy-rescale threshold in raw score units (8 / sl2)
     int contiguous;   // Lc % kKT == 0: a tile never straddles two chunks
+    int causal;       // the query at position i sees keys at positions <= i only
 };
 
 // fp32 forward (fp32 inputs and output): the same ring-ordered online
@@ -116,7 +117,12 @@ __global__ __launch_bounds__(kThreads) void rsa_fwd_f32(FwdParams p) {
     if (ntile > kFwdMaxTiles) return;   // the host never launches such a range
     const bool contig = p.contiguous != 0;
 
-    tflag.build(ntile, kThreads, [&](int t) { return key_tile_flags(mrow, n, p.N, p.Lc, contig, vbeg + t * kKT, vend); });
+    const int qlo = p.q_pos0 + row0, qhi = p.q_pos0 + min(row0 + 4 * kQW, p.Lq) - 1;
+    tflag.build(ntile, kThreads, [&](int t) {
+        const int v0 = vbeg + t * kKT;
+        const uint32_t f = key_tile_flags(mrow, n, p.N, p.Lc, contig, v0, vend);
+        return p.causal ? f & causal_tile_class(v0, min(kKT, vend - v0), n, p.N, p.Lc, contig, qlo, qhi) : f;
+    });
 
     // Q^T fragments (B operand of S^T = K Q^T): lane (j, h) holds Q[row][2 ks + h]
     float qf[D / 2];
@@ -198,6 +204,16 @@ __global__ __launch_bounds__(kThreads) void rsa_fwd_f32(FwdParams p) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r)
                     if (!((bits >> (32 * kb + acc_row(r, h))) & 1ull)) s[kb][r] = -INFINITY;
+            if (p.causal) {   // keys after this lane's query position
+                const int qpos = p.q_pos0 + row;
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int vk = v0 + 32 * kb + acc_row(r, h);
+                        if (vk < vend && ring_pos(vk, n, p.N, p.Lc) > qpos) s[kb][r] = -INFINITY;
+                    }
+            }
         }
         float mx = s[0][0];
 #pragma unroll
@@ -276,7 +292,7 @@ __global__ __launch_bounds__(kThreads) void rsa_fwd_f32(FwdParams p) {
 // the vector ALU. (A variant that overlapped the next tile's score MFMAs
 // with this tile's softmax inside one wave needed more registers, ran at
 // fewer waves per SIMD and was slower; so was three buffers at three waves.)
-template <int D, bool CONTIG, int QB>
+template <int D, bool CONTIG, int QB, bool CAUSAL>
 __global__ __launch_bounds__(256 / QB, (D == 64 && QB == 1) ? 4 : 2)
 void rsa_fwd_bf16(FwdParams p) {
     // QB 32-row query blocks per wave; 128 query rows per workgroup either
@@ -318,7 +334,12 @@ void rsa_fwd_bf16(FwdParams p) {
     const uint8_t* mrow = p.mask ? p.mask + (size_t)b * p.L : nullptr;
     if (ntile > kFwdMaxTiles) return;   // the host never launches such a range
 
-    tflag.build(ntile, NTH, [&](int t) { return key_tile_flags(mrow, n, p.N, p.Lc, CONTIG, vbeg + t * kKT, vend); });
+    const int qlo = p.q_pos0 + row0, qhi = p.q_pos0 + min(row0 + ROWS, p.Lq) - 1;
+    tflag.build(ntile, NTH, [&](int t) {
+        const int v0 = vbeg + t * kKT;
+        const uint32_t f = key_tile_flags(mrow, n, p.N, p.Lc, CONTIG, v0, vend);
+        return CAUSAL ? f & causal_tile_class(v0, min(kKT, vend - v0), n, p.N, p.Lc, CONTIG, qlo, qhi) : f;
+    });
 
     u32x4 qf[QB][D / 16];
 #pragma unroll
@@ -423,6 +444,32 @@ void rsa_fwd_bf16(FwdParams p) {
 #pragma unroll
                         for (int qb = 0; qb < QB; ++qb) s[qb][kb][r] = -INFINITY;
                     }
+            if constexpr (CAUSAL) {
+                // keys after this lane's query position; within a chunk-aligned
+                // tile key 32 kb + acc_row(r, h) sits at position kp0 plus that,
+                // so one offset per lane leaves constant comparisons
+                const int v0 = vbeg + t * kKT;
+                const int kp0 = CONTIG ? ring_pos(v0, n, p.N, p.Lc) : 0;
+#pragma unroll
+                for (int qb = 0; qb < QB; ++qb) {
+                    const int qpos = p.q_pos0 + wrow0 + 32 * qb + j;
+                    const int rel = qpos - kp0 - 4 * h;
+#pragma unroll
+                    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) {
+                            const int i = 32 * kb + 8 * (r >> 2) + (r & 3);
+                            bool hide;
+                            if constexpr (CONTIG) {
+                                hide = i > rel;
+                            } else {
+                                const int vk = v0 + i + 4 * h;
+                                hide = vk < vend && ring_pos(vk, n, p.N, p.Lc) > qpos;
+                            }
+                            if (hide) s[qb][kb][r] = -INFINITY;
+                        }
+                }
+            }
         }
         // ---- online softmax (base 2). The weights are formed against the
         // running base first; only when some lane's tile sum exceeds
@@ -613,6 +660,7 @@ hipError_t launch_t(const ForwardCall& c, hipStream_t stream) {
     p.sl2 = (float)sl2;
     p.tau_raw = (float)(8.0 / sl2);
     p.contiguous = (p.Lc % kKT) == 0;
+    p.causal = c.causal ? 1 : 0;
     if (c.groups > 1) {
         p.part_o = c.part;
         p.part_ml = c.part + (size_t)c.groups * p.BH * c.Lq * D;
@@ -625,10 +673,14 @@ hipError_t launch_t(const ForwardCall& c, hipStream_t stream) {
         // measured 12% slower at d = 64.
         constexpr int QB = 1;
         const dim3 block(kWave * 4 / QB);
-        if (p.contiguous)
-            hipLaunchKernelGGL((rsa_fwd_bf16<D, true, QB>), dim3((unsigned)total), block, 0, stream, p);
+        if (p.contiguous && !p.causal)
+            hipLaunchKernelGGL((rsa_fwd_bf16<D, true, QB, false>), dim3((unsigned)total), block, 0, stream, p);
+        else if (!p.causal)
+            hipLaunchKernelGGL((rsa_fwd_bf16<D, false, QB, false>), dim3((unsigned)total), block, 0, stream, p);
+        else if (p.contiguous)
+            hipLaunchKernelGGL((rsa_fwd_bf16<D, true, QB, true>), dim3((unsigned)total), block, 0, stream, p);
         else
-            hipLaunchKernelGGL((rsa_fwd_bf16<D, false, QB>), dim3((unsigned)total), block, 0, stream, p);
+            hipLaunchKernelGGL((rsa_fwd_bf16<D, false, QB, true>), dim3((unsigned)total), block, 0, stream, p);
     } else {
         hipLaunchKernelGGL((rsa_fwd_f32<D>), dim3((unsigned)total), dim3(kThreads), 0, stream, p);
     }

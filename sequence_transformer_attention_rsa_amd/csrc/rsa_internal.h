@@ -27,6 +27,7 @@ struct ForwardCall {
     int q_pos0;             // sequence position of q's row 0
     int groups;             // ring-step groups computed in parallel (1 = no split)
     bool bf16;
+    bool causal;            // the query at position i sees keys at positions <= i only
 };
 
 // Bytes of split partials for `groups` ring-step groups.
@@ -58,6 +59,7 @@ struct BackwardCall {
     void* dk;
     void* dv;
     int B, H, L, d, N;
+    bool causal;
 };
 
 size_t backward_workspace_bytes(int B, int H, int L, int d);

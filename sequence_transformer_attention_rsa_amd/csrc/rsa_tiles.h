@@ -45,6 +45,34 @@ __device__ __forceinline__ uint8_t key_tile_flags(const uint8_t* mrow, int n, in
     return (any ? 1 : 0) | (all ? 2 : 0);
 }
 
+// Causal visibility of a key tile (ring indices v0 .. v0 + cnt - 1 of rank n)
+// to the query positions [qlo, qhi]: 0 = every key lies after every query
+// (hidden), 3 = every key at or before every query (visible), 1 = mixed.
+// The causal variant is not on the pages: the query at position i sees key
+// j only if j <= i (the standard autoregressive mask). Within one chunk the
+// ring indices map to consecutive positions, so a tile is split into at most
+// a few chunk segments.
+__device__ __forceinline__ uint32_t causal_tile_class(int v0, int cnt, int n, int N, int Lc, bool contiguous, int qlo,
+                                                      int qhi) {
+    int kmin, kmax;
+    if (contiguous) {
+        kmin = ring_pos(v0, n, N, Lc);
+        kmax = kmin + cnt - 1;
+    } else {
+        kmin = 0x7fffffff;
+        kmax = -1;
+        for (int v = v0; v < v0 + cnt;) {
+            const int seg_end = min(v0 + cnt, (v / Lc + 1) * Lc);
+            const int a = ring_pos(v, n, N, Lc);
+            kmin = min(kmin, a);
+            kmax = max(kmax, a + (seg_end - 1 - v));
+            v = seg_end;
+        }
+    }
+    if (kmin > qhi) return 0u;
+    return kmax <= qlo ? 3u : 1u;
+}
+
 // Occupancy table of a workgroup's key tiles in LDS: the two bits of
 // key_tile_flags per tile, four tiles per byte. build() is called by all
 // `nthreads` threads and must be followed by a barrier before get().

@@ -194,3 +194,17 @@ def test_layer_forward_validation(lib):
     assert call(ws_bytes=ws - 2) == EWS
     w.b_ff1 = P + 4
     assert call() == EALIGN
+
+
+def test_flag_validation(lib):
+    """The *_ex entry points accept RSA_CAUSAL and reject other flag bits."""
+    assert lib.rsa_forward_ex(P, P, P, None, 1, 2, 256, 64, 4, BF16, 2, None, P, None) == EUNSUP
+    assert lib.rsa_forward_ex(None, P, P, None, 1, 2, 256, 64, 4, BF16, 1, None, P, None) == ENULL
+    assert lib.rsa_forward_ex(P, P, P, None, 1, 2, 255, 64, 4, BF16, 1, None, P, None) == ESHAPE
+    ws = lib.rsa_forward_rank_workspace_bytes(1, 16, 32768, 128, 64)
+    assert lib.rsa_forward_rank_ex(P, P, P, None, 1, 16, 32768, 128, 64, 0, BF16, 4, P, ws, None, P, None) == EUNSUP
+    assert lib.rsa_forward_rank_ex(P, P, P, None, 1, 16, 32768, 128, 64, 64, BF16, 1, P, ws, None, P, None) == ESHAPE
+    bws = lib.rsa_backward_workspace_bytes(1, 2, 256, 64, 4, BF16)
+    assert lib.rsa_backward_ex(P, P, P, P, P, P, None, 1, 2, 256, 64, 4, BF16, 8, P, bws, None, P, P, P) == EUNSUP
+    assert lib.rsa_backward_ex(P, P, P, P, P, P, None, 1, 2, 256, 64, 4, F32, 1, P, bws, None, P, P, P) == EUNSUP
+    assert lib.rsa_backward_ex(P, P, P, P, P, P, None, 1, 2, 256, 64, 4, BF16, 1, None, bws, None, P, P, P) == EWS
