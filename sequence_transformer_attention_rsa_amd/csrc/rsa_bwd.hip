@@ -118,7 +118,9 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 3 : 1) void rsa_bwd_dq(BwdParam
     const TileTable tflag{tflag_bytes};
 
     const int lid = xcd_remap(blockIdx.x, p.nt * p.BH);
-    const int qt = lid % p.nt, bh = lid / p.nt, b = bh / p.H;
+    // causal: the last query tiles see the most keys; dispatch them first
+    const int qt = CAUSAL ? p.nt - 1 - lid % p.nt : lid % p.nt;
+    const int bh = lid / p.nt, b = bh / p.H;
     const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
     const int j = lane & 31, h = lane >> 5;
     const int row0 = qt * 128;
@@ -324,8 +326,11 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 3 : 1) void rsa_bwd_dq(BwdParam
 // dO V^T (lane <-> key, registers <-> query rows), P and dS elementwise, then
 // dV^T += dO^T P and dK^T += Q^T dS, with Q^T and dO^T from the transposing
 // read of the same Q and dO tiles.
+// (The causal instance runs at two waves per SIMD: its per-element mask of
+// the diagonal tiles pushes three waves' worth of registers into spills,
+// which measured 21% slower.)
 template <int D, bool CONTIG, bool CAUSAL>
-__global__ __launch_bounds__(kThreads, D == 64 ? 3 : 1) void rsa_bwd_dkdv(BwdParams p) {
+__global__ __launch_bounds__(kThreads, D == 64 ? (CAUSAL ? 2 : 3) : 1) void rsa_bwd_dkdv(BwdParams p) {
     using T = DirectTile<D>;
     constexpr int NBUF = 3;
     constexpr int ROWV = 2 * kKT * 4;             // -D and -lse*log2(e) for 64 rows

@@ -311,7 +311,9 @@ void rsa_fwd_bf16(FwdParams p) {
 
     const int total = p.nqt * p.BH * p.groups;
     const int lid = xcd_remap(blockIdx.x, total);
-    const int qt = lid % p.nqt;
+    // causal: the last query tiles of a head see the most keys; dispatch them
+    // first so that the light ones fill the tail
+    const int qt = CAUSAL ? p.nqt - 1 - lid % p.nqt : lid % p.nqt;
     const int rest = lid / p.nqt;
     const int g = rest % p.groups;
     const int bh = rest / p.groups;
