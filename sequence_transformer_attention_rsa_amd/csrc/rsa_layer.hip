@@ -237,9 +237,6 @@ constexpr int kBT = 256;
 using BTile = DirectTile<64, 8>;                 // one copy instruction per wave per 64-row tile
 constexpr int kBigStage = 8 * BTile::BYTES;      // A: tiles 0-3, W: tiles 4-7
 constexpr int kBigLds = 2 * kBigStage;           // 128 KB; the epilogue reuses it
-#ifndef RSA_GEMM_REGSTAGE
-#define RSA_GEMM_REGSTAGE 0
-#endif
 
 template <int PRO, int EPI>
 __global__ __launch_bounds__(kBigThreads) void rsa_gemm_bf16_256(GemmParams p) {
@@ -304,7 +301,9 @@ __global__ __launch_bounds__(kBigThreads) void rsa_gemm_bf16_256(GemmParams p) {
             for (int mi = 0; mi < 4; ++mi)
                 af[slot][mi] = BTile::chunk(sb + (2 * wm + (mi >> 1)) * BTile::BYTES, 32 * (mi & 1) + j, 2 * ks + h);
 #pragma unroll
-            for (int ni = 0; ni < 2; ++ni) wf[slot][ni] = BTile::chunk(wt, 32 * ni + j, 2 * ks + h);
+            for (int ni = 0; ni < 2; ++ni) {
+                wf[slot][ni] = BTile::chunk(wt, 32 * ni + j, 2 * ks + h);
+            }
         };
         frags(0, 0);
 #pragma unroll
@@ -317,52 +316,6 @@ __global__ __launch_bounds__(kBigThreads) void rsa_gemm_bf16_256(GemmParams p) {
                     acc[ni][mi] = mfma_32x32x16_bf16(wf[ks & 1][ni], af[ks & 1][mi], acc[ni][mi]);
         }
     };
-#if RSA_GEMM_REGSTAGE
-    // Register-staged copies: step s + 2 is loaded into registers while step
-    // s is computed from LDS, and written to LDS (the same placement as the
-    // direct copy) once step s is done; two LDS buffers, two register sets.
-    auto gload = [&](int s, u32x4 (&r)[8]) {
-        const uint8_t* abase;
-        if constexpr (PRO == kProRows) {
-            abase = reinterpret_cast<const uint8_t*>(p.a + (size_t)m0 * p.K + (size_t)s * kGK);
-        } else {
-            const int k0 = s * kGK, hh = k0 / p.d;
-            abase = reinterpret_cast<const uint8_t*>(p.a + (size_t)hh * p.L * p.d + (k0 - hh * p.d));
-        }
-        const uint8_t* wbase = reinterpret_cast<const uint8_t*>(p.w + (size_t)n0 * p.K + (size_t)s * kGK);
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            r[t] = *reinterpret_cast<const u32x4*>(abase + va[t]);
-            r[4 + t] = *reinterpret_cast<const u32x4*>(wbase + vw[t]);
-        }
-    };
-    auto lwrite = [&](const u32x4 (&r)[8], int bi) {
-        uint8_t* d = smem + bi * kBigStage + wave * 1024 + lane * 16;
-#pragma unroll
-        for (int t = 0; t < 8; ++t) *reinterpret_cast<u32x4*>(d + t * BTile::BYTES) = r[t];
-    };
-    auto lds_sync = [&]() {
-        __builtin_amdgcn_s_waitcnt(0xC07F);   // this wave's LDS writes done (lgkmcnt(0) only)
-        bare_barrier();
-    };
-    u32x4 ra[8], rb[8];
-    gload(0, ra);
-    if (nk > 1) gload(1, rb);
-    lwrite(ra, 0);
-    lds_sync();
-    for (int s = 0; s < nk; s += 2) {
-        if (s + 2 < nk) gload(s + 2, ra);
-        compute(0);
-        if (s + 1 >= nk) break;
-        lwrite(rb, 1);
-        lds_sync();
-        if (s + 3 < nk) gload(s + 3, rb);
-        compute(1);
-        if (s + 2 >= nk) break;
-        lwrite(ra, 0);
-        lds_sync();
-    }
-#else
     load(0, 0);
     for (int s = 0; s < nk; ++s) {
         vm_wait<0>();   // step s landed
@@ -370,7 +323,6 @@ __global__ __launch_bounds__(kBigThreads) void rsa_gemm_bf16_256(GemmParams p) {
         if (s + 1 < nk) load(s + 1, (s + 1) & 1);
         compute(s & 1);
     }
-#endif
     bare_barrier();   // every wave's last reads of the stage buffers are done
 
     uint8_t* st = smem + wave * (128 * 128);     // this wave's 128 x 64 bf16 strip
