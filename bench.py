@@ -78,6 +78,7 @@ KERNEL_SOURCES = {
     "bwd_dq": ("rsa_bwd.hip", "rsa_tiles.h", "rsa_device.h"),
     "bwd_dkdv": ("rsa_bwd.hip", "rsa_tiles.h", "rsa_device.h"),
     "forward_twopass": ("rsa_twopass.hip", "rsa_tiles.h", "rsa_device.h"),
+    "ff1_gelu": ("rsa_layer.hip", "rsa_tiles.h", "rsa_device.h"),
 }
 
 
@@ -272,6 +273,13 @@ def layer_bench(args):
         keep["y"] = rsa.layernorm(a2, w["ln2_gamma"], w["ln2_beta"])
         mark(7)
 
+    if args.copy_calibration_mib > 0:
+        n = args.copy_calibration_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -320,9 +328,11 @@ def layer_bench(args):
         "products_share_of_step": gemm_ms / ms_per_step,
         "chain_equals_rsa_layer_forward": same,
         "kernels": per,
-        "roofline": {"kernel": f"rsa_gemm_bf16 ({dom})", "bound": "mfma",
+        "roofline": {"kernel": f"rsa_gemm_bf16_256 ({dom})", "bound": "mfma",
                      "achieved": per[dom]["tflops"], "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": per[dom]["tflops"] / PEAK_BF16_TFLOPS, "traffic": None,
+                     "frac": per[dom]["tflops"] / PEAK_BF16_TFLOPS,
+                     "traffic": recorded_traffic(shp.name, dom),
+                     "traffic_unit": "bytes per launch (calibrated FETCH_SIZE + WRITE_SIZE)",
                      "avg_ms": per[dom]["avg_ms"], "flops_per_launch": flops[dom]},
         "gpu": torch.cuda.get_device_name(dev),
     }
