@@ -144,3 +144,36 @@ def test_causal_backward_workload_two_heads(oracle_lib):
                                    causal=True)
         for name, a, ref in zip(("dq", "dk", "dv"), got, want):
             assert_parity(a[sl], ref, "bf16", f"causal workload {name} b={b} h={h}", grad=True)
+
+
+def test_causal_longest_key_range(oracle_lib):
+    """L = 1048576 with the causal mask: the tile table of a workgroup near
+    the end of the sequence classifies 16384 tiles; sampled rows of every
+    part of the sequence, key padding at the end."""
+    dev = device()
+    L, N, d = 64 * 16384, 64, 64
+    x = inputs(1, 1, L, d, seed=77, dtype="bf16", valid_range=(L - 3000, L - 1000))
+    say("causal longest key range", "valid", x["valid_len"])
+    out, lse = gpu_forward(x, "bf16", N, dev)
+    rows = sample_rows(L, 14, seed=78)
+    want, want_lse = oracle_lib.forward(x["q"][:, :, rows], x["k"], x["v"], x["mask"], N=N, qpos=rows, causal=True)
+    assert_parity(out[0, 0, rows], want[0, 0], "bf16", f"causal L={L}")
+    check_lse(lse[0, 0, rows], want_lse[0, 0], "bf16", f"causal L={L}")
+
+
+def test_causal_backward_every_ring_size(oracle_lib):
+    """The causal backward does not depend on N (every divisor of L = 256,
+    including one token per chunk)."""
+    dev = device()
+    L, d = 256, 64
+    x = inputs(1, 2, L, d, seed=79, dtype="bf16", valid_range=(200, 200), with_dout=True)
+    q, k, v, g = (to_dev(x[n], "bf16", dev) for n in ("q", "k", "v", "dout"))
+    m = mask_dev(x["mask"], dev)
+    want = oracle_lib.backward(x["q"], x["k"], x["v"], x["dout"], x["mask"], N=1, causal=True)
+    for N in (1, 2, 4, 16, 64, 256):
+        say("causal backward ring size", N)
+        out, lse = rsa.forward(q, k, v, m, N=N, return_lse=True, causal=True)
+        dq, dk, dv = rsa.backward(q, k, v, out, g, lse, m, N=N, causal=True)
+        torch.cuda.synchronize()
+        for name, a, b in zip(("dq", "dk", "dv"), (dq, dk, dv), want):
+            assert_parity(from_dev(a), b, "bf16", f"causal N={N} {name}", grad=True)
