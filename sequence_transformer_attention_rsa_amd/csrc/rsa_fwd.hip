@@ -20,9 +20,13 @@
 //     plus one exchange between wave halves, and the accumulator is the B
 //     operand of O^T = V^T P^T unchanged;
 //   * online softmax in base 2 (scale and log2(e) folded into one FMA), with
-//     a lazy rescale: the running base only moves when a tile's maximum
-//     exceeds it by more than 8 (weights stay <= 2^8), which is exact after
-//     the final normalisation;
+//     a lazy rescale: the weights are formed against the running base, and
+//     only when some lane's sum of its 32 weights of the tile exceeds 2^12
+//     does the wave take the row maximum, move the base and form them again
+//     (the fp32 kernel moves the base when a tile's maximum exceeds it by
+//     more than 8 in log2 units); exact after the final normalisation;
+//   * tiles are dropped from the occupancy table when the causal variant
+//     hides all their keys, and masked per element on the diagonal;
 //   * P is rounded to bf16 for the MFMA and the row sum adds those same
 //     rounded values, so sum_j P_ij = 1 holds for the weights actually used;
 //   * tiles whose keys are all padding are skipped (a per-workgroup
