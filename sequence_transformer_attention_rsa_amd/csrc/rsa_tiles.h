@@ -163,11 +163,19 @@ __device__ __forceinline__ void bare_barrier() {
 // global_load_lds (16 bytes per lane, no registers, no VALU): each
 // wave-instruction fills one contiguous 1 KB block, so rows are unpadded and
 // the 16-byte chunk c of row r is stored at r * 2D + 16 * (c ^ swz(r)) bytes;
-// the XOR is chosen through each lane's source address. With
-// swz(r) = 2(r & 3) + ((r >> 2) & 1), eight consecutive rows read at the same
-// chunk (16-byte fragment reads) and four consecutive rows read at a chunk
-// pair (the transposing ds_read_b64_tr_b16) both hit eight different bank
-// groups, so one copy of a tile serves both operand orientations.
+// the XOR is chosen through each lane's source address. LDS has 64 banks of
+// 4 bytes; a 16-byte read is served 16 lanes per cycle, an 8-byte read 32
+// lanes per cycle. The fragment reads put 16 consecutive rows (lanes) on one
+// logical chunk, the transposing ds_read_b64_tr_b16 puts four consecutive
+// rows on four consecutive chunks (eight 8-byte pieces per row over 32
+// lanes). swz(r) is chosen so that both touch 64 different banks:
+//   D = 64 (two rows per 256 bytes): rows of one parity among 16 consecutive
+//     rows get eight different swz values, and the two rows of one parity in
+//     an aligned group of four differ in swz bit 2 (disjoint aligned chunk
+//     quads);
+//   D = 128 (one row per 256 bytes): 16 consecutive rows get 16 different
+//     swz values, four consecutive rows four different swz bits 2-3.
+// One copy of a tile then serves both operand orientations.
 template <int D, int WAVES = 4>
 struct DirectTile {
     static constexpr int ROW_BYTES = 2 * D;
@@ -177,7 +185,13 @@ struct DirectTile {
     static constexpr int IPW = kTileRows / RPI / WAVES;   // instructions per wave
     static_assert(IPW * RPI * WAVES == kTileRows, "tile copy split");
 
-    __device__ __forceinline__ static constexpr int swz(int r) { return 2 * (r & 3) + ((r >> 2) & 1); }
+    __device__ __forceinline__ static constexpr int swz(int r) {
+        if constexpr (CPR == 8)
+            return (((r >> 1) & 1) << 2) | (((r >> 2) & 1) << 1) | ((r ^ (r >> 3)) & 1);
+        else
+            return ((r & 3) << 2) | ((r >> 2) & 3);
+    }
+    static_assert(CPR == 8 || CPR == 16, "tile rows of 64 or 128 bf16");
 
     // Issue the copies; rowptr(r) must return a readable row for every r
     // (callers point rows outside the range at any valid row).
