@@ -192,9 +192,11 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 3 : 1) void rsa_bwd_dq(BwdParam
         return t;
     };
 
-    // Three LDS buffers at d = 64: the copy of tile t+2 is issued right after
-    // the barrier that opens tile t and may stay in flight until t+1 opens
-    // (two buffers at d = 128: the copy of t+1 lands while t is computed).
+    // Two LDS buffers (RSA_DQ_NBUF): the copy of tile t+1 is issued right after
+    // the barrier that opens tile t and lands while t is computed. Three
+    // buffers (the copy of t+2 in flight until t+1 opens) need 100 KB of LDS
+    // per workgroup at d = 64, leave one workgroup per CU and measured 3.7x
+    // slower.
     int t = next_tile(-1);
     int t1 = t < ntile ? next_tile(t) : ntile;
     auto body = [&](auto cb_c) -> bool {
