@@ -70,6 +70,7 @@ struct FwdParams {
     float sl2;        // log2(e) / sqrt(d)
     float tau_raw;    // lazy-rescale threshold in raw score units (8 / sl2)
     int contiguous;   // Lc % kKT == 0: a tile never straddles two chunks
+    int strided;      // bf16, groups > 1, contiguous: group g takes ring steps g, g + groups, ...
     int causal;       // the query at position i sees keys at positions <= i only
 };
 
@@ -332,7 +333,17 @@ void rsa_fwd_bf16(FwdParams p) {
     const int step0 = g * p.spg;
     const int step1 = min(p.N, step0 + p.spg);
     const int vbeg = step0 * p.Lc, vend = step1 * p.Lc;
-    const int ntile = (vend - vbeg + kKT - 1) / kKT;
+    // Ring indices of this workgroup's key tiles. One group, or tiles that
+    // straddle chunks: the ring steps [step0, step1) in order. Several groups
+    // on chunk-aligned tiles: group g takes every groups-th ring step (g,
+    // g + groups, ...), so the padded chunks, which a rank meets one after
+    // another, spread evenly over the groups (the merge is exact for any
+    // grouping of the steps).
+    const bool strided = CONTIG && p.strided;
+    const int tpc = p.Lc / kKT;   // tiles per chunk (chunk-aligned tiles)
+    const int ntile = strided ? (p.N - g + p.groups - 1) / p.groups * tpc : (vend - vbeg + kKT - 1) / kKT;
+    auto tile_v0 = [&](int t) { return strided ? (g + p.groups * (t / tpc)) * p.Lc + (t % tpc) * kKT : vbeg + t * kKT; };
+    auto tile_end = [&](int v0) { return strided ? v0 + kKT : vend; };
 
     const uint16_t* qh = static_cast<const uint16_t*>(p.q) + (size_t)bh * p.Lq * D;
     const uint16_t* kh = static_cast<const uint16_t*>(p.k) + (size_t)bh * p.L * D;
@@ -342,9 +353,9 @@ void rsa_fwd_bf16(FwdParams p) {
 
     const int qlo = p.q_pos0 + row0, qhi = p.q_pos0 + min(row0 + ROWS, p.Lq) - 1;
     tflag.build(ntile, NTH, [&](int t) {
-        const int v0 = vbeg + t * kKT;
-        const uint32_t f = key_tile_flags(mrow, n, p.N, p.Lc, CONTIG, v0, vend);
-        return CAUSAL ? f & causal_tile_class(v0, min(kKT, vend - v0), n, p.N, p.Lc, CONTIG, qlo, qhi) : f;
+        const int v0 = tile_v0(t), ve = tile_end(v0);
+        const uint32_t f = key_tile_flags(mrow, n, p.N, p.Lc, CONTIG, v0, ve);
+        return CAUSAL ? f & causal_tile_class(v0, min(kKT, ve - v0), n, p.N, p.Lc, CONTIG, qlo, qhi) : f;
     });
 
     u32x4 qf[QB][D / 16];
@@ -379,7 +390,7 @@ void rsa_fwd_bf16(FwdParams p) {
     uint32_t voff[KTile::IPW];
     KTile::row_offsets(voff);
     auto load = [&](int t, int bi) {
-        const int v0 = vbeg + t * kKT;
+        const int v0 = tile_v0(t);
         uint8_t* kbuf = smem + bi * BUF;
         uint8_t* vbuf = kbuf + KTile::BYTES;
         if constexpr (CONTIG) {
@@ -441,7 +452,8 @@ void rsa_fwd_bf16(FwdParams p) {
             // key acc_row(r, h) = 8 (r / 4) + 4 h + r % 4 of block kb: after one
             // shift by 4 h every bit position is a constant (no per-register
             // masks held in registers)
-            const uint64_t bits = key_tile_bits(mrow, n, p.N, p.Lc, CONTIG, vbeg + t * kKT, vend) >> (4 * h);
+            const int tv0 = tile_v0(t);
+            const uint64_t bits = key_tile_bits(mrow, n, p.N, p.Lc, CONTIG, tv0, tile_end(tv0)) >> (4 * h);
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -454,7 +466,7 @@ void rsa_fwd_bf16(FwdParams p) {
                 // keys after this lane's query position; within a chunk-aligned
                 // tile key 32 kb + acc_row(r, h) sits at position kp0 plus that,
                 // so one offset per lane leaves constant comparisons
-                const int v0 = vbeg + t * kKT;
+                const int v0 = tile_v0(t);
                 const int kp0 = CONTIG ? ring_pos(v0, n, p.N, p.Lc) : 0;
 #pragma unroll
                 for (int qb = 0; qb < QB; ++qb) {
@@ -666,6 +678,7 @@ hipError_t launch_t(const ForwardCall& c, hipStream_t stream) {
     p.sl2 = (float)sl2;
     p.tau_raw = (float)(8.0 / sl2);
     p.contiguous = (p.Lc % kKT) == 0;
+    p.strided = (BF16 && c.groups > 1 && p.contiguous) ? 1 : 0;
     p.causal = c.causal ? 1 : 0;
     if (c.groups > 1) {
         p.part_o = c.part;

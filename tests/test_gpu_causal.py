@@ -65,7 +65,8 @@ def test_causal_first_row_copies_first_value_and_n_independence(oracle_lib):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-@pytest.mark.parametrize("L,N,d", [(1024, 8, 64), (600, 6, 128), (96, 96, 64)])
+@pytest.mark.parametrize("L,N,d", [(1024, 8, 64), (600, 6, 128), (96, 96, 64),
+                                   (1536, 12, 128)])   # 8 ring-step groups of two or one steps
 def test_causal_rank_share(oracle_lib, dtype, L, N, d):
     """One rank's share: ranks after the first meet chunks that hide nothing
     (before their own), their own chunk (the diagonal) and chunks that hide

@@ -204,7 +204,10 @@ def test_rank_share_sampled_rows(oracle_lib, rank):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-@pytest.mark.parametrize("L,N,d", [(256, 4, 64), (1024, 32, 128), (600, 6, 64), (96, 96, 128)])
+@pytest.mark.parametrize("L,N,d", [(256, 4, 64), (1024, 32, 128), (600, 6, 64), (96, 96, 128),
+                                   # 12 chunks of 128 in 8 ring-step groups: groups take every 8th
+                                   # step, so four of them hold two steps and four hold one
+                                   (1536, 12, 64), (1536, 12, 128)])
 def test_rank_share_matches_oracle_small(oracle_lib, dtype, L, N, d):
     dev = device()
     x = inputs(2, 2, L, d, seed=L + N, dtype=dtype, valid_range=(L // 3, L))
