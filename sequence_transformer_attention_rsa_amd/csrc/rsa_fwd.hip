@@ -297,9 +297,13 @@ __global__ __launch_bounds__(kThreads) void rsa_fwd_f32(FwdParams p) {
 // the vector ALU. (A variant that overlapped the next tile's score MFMAs
 // with this tile's softmax inside one wave needed more registers, ran at
 // fewer waves per SIMD and was slower; so was three buffers at three waves.)
-template <int D, bool CONTIG, int QB, bool CAUSAL>
+// FULL: no key mask, no causal mask and chunk-aligned tiles, so every key
+// tile of the range is whole and visible: the occupancy table is not built
+// and the loop takes every tile without looking it up.
+template <int D, bool CONTIG, int QB, bool CAUSAL, bool FULL = false>
 __global__ __launch_bounds__(256 / QB, (D == 64 && QB == 1) ? 4 : 2)
 void rsa_fwd_bf16(FwdParams p) {
+    static_assert(!FULL || (CONTIG && !CAUSAL), "whole tiles need chunk-aligned, non-causal ranges");
     // QB 32-row query blocks per wave; 128 query rows per workgroup either
     // way (4 waves x 32 rows, or 2 waves x 64 rows: each K and V^T fragment
     // read from LDS then feeds two MFMAs).
@@ -311,7 +315,7 @@ void rsa_fwd_bf16(FwdParams p) {
     constexpr int NBUF = 2;   // 4 x (2 x 16 KB + 4 KB) of LDS per CU at d = 64
     constexpr int ROWS = 4 * 32;
     __shared__ __attribute__((aligned(1024))) uint8_t smem[NBUF * BUF];
-    __shared__ uint8_t tflag_bytes[kFwdMaxTiles / 4];
+    __shared__ uint8_t tflag_bytes[FULL ? 4 : kFwdMaxTiles / 4];
     const TileTable tflag{tflag_bytes};
 
     const int total = p.nqt * p.BH * p.groups;
@@ -352,11 +356,13 @@ void rsa_fwd_bf16(FwdParams p) {
     if (ntile > kFwdMaxTiles) return;   // the host never launches such a range
 
     const int qlo = p.q_pos0 + row0, qhi = p.q_pos0 + min(row0 + ROWS, p.Lq) - 1;
-    tflag.build(ntile, NTH, [&](int t) {
-        const int v0 = tile_v0(t), ve = tile_end(v0);
-        const uint32_t f = key_tile_flags(mrow, n, p.N, p.Lc, CONTIG, v0, ve);
-        return CAUSAL ? f & causal_tile_class(v0, min(kKT, ve - v0), n, p.N, p.Lc, CONTIG, qlo, qhi) : f;
-    });
+    if constexpr (!FULL) {
+        tflag.build(ntile, NTH, [&](int t) {
+            const int v0 = tile_v0(t), ve = tile_end(v0);
+            const uint32_t f = key_tile_flags(mrow, n, p.N, p.Lc, CONTIG, v0, ve);
+            return CAUSAL ? f & causal_tile_class(v0, min(kKT, ve - v0), n, p.N, p.Lc, CONTIG, qlo, qhi) : f;
+        });
+    }
 
     u32x4 qf[QB][D / 16];
 #pragma unroll
@@ -408,7 +414,8 @@ void rsa_fwd_bf16(FwdParams p) {
     };
     auto next_tile = [&](int t) {
         ++t;
-        while (t < ntile && !(tflag.get(t) & 1)) ++t;
+        if constexpr (!FULL)
+            while (t < ntile && !(tflag.get(t) & 1)) ++t;
         return t;
     };
 
@@ -448,7 +455,7 @@ void rsa_fwd_bf16(FwdParams p) {
                         s[qb][kb] = mfma_32x32x16_bf16(kf[kb][kq], qf[qb][kq], s[qb][kb]);
         }
         // ---- key mask and range tail (tiles not fully valid)
-        if (!(tflag.get(t) & 2)) {
+        if (!FULL && !(tflag.get(t) & 2)) {
             // key acc_row(r, h) = 8 (r / 4) + 4 h + r % 4 of block kb: after one
             // shift by 4 h every bit position is a constant (no per-register
             // masks held in registers)
@@ -692,7 +699,9 @@ hipError_t launch_t(const ForwardCall& c, hipStream_t stream) {
         // measured 12% slower at d = 64.
         constexpr int QB = 1;
         const dim3 block(kWave * 4 / QB);
-        if (p.contiguous && !p.causal)
+        if (p.contiguous && !p.causal && p.mask == nullptr)
+            hipLaunchKernelGGL((rsa_fwd_bf16<D, true, QB, false, true>), dim3((unsigned)total), block, 0, stream, p);
+        else if (p.contiguous && !p.causal)
             hipLaunchKernelGGL((rsa_fwd_bf16<D, true, QB, false>), dim3((unsigned)total), block, 0, stream, p);
         else if (!p.causal)
             hipLaunchKernelGGL((rsa_fwd_bf16<D, false, QB, false>), dim3((unsigned)total), block, 0, stream, p);
