@@ -376,7 +376,10 @@ void rsa_fwd_bf16(FwdParams p) {
         }
     }
     f32x16 o[QB][D / 32];
-    float m_b[QB], l0[QB], l1[QB];
+    // running base m_b (raw score units) and nb = -m_b * log2(e)/sqrt(d);
+    // running row sums l0, l1 (two dot-product chains); lim = l0 + l1 +
+    // kMaxTileSum, the sum beyond which a tile's weights are too large
+    float m_b[QB], nb[QB], l0[QB], l1[QB], lim[QB];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
 #pragma unroll
@@ -384,8 +387,10 @@ void rsa_fwd_bf16(FwdParams p) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) o[qb][db][r] = 0.0f;
         m_b[qb] = kNoBase;
+        nb[qb] = -kNoBase * p.sl2;
         l0[qb] = 0.0f;
         l1[qb] = 0.0f;
+        lim[qb] = kMaxTileSum;
     }
 
     // The Q fragments have landed (waited for here, so that the compiler
@@ -395,14 +400,15 @@ void rsa_fwd_bf16(FwdParams p) {
 
     uint32_t voff[KTile::IPW];
     KTile::row_offsets(voff);
+    const uint32_t wave_lds = KTile::wave_lds_offset();
     auto load = [&](int t, int bi) {
         const int v0 = tile_v0(t);
         uint8_t* kbuf = smem + bi * BUF;
         uint8_t* vbuf = kbuf + KTile::BYTES;
         if constexpr (CONTIG) {
             const int pos0 = ring_pos(v0, n, p.N, p.Lc);
-            KTile::load_rows(kbuf, kh + (size_t)pos0 * D, voff);
-            VTile::load_rows(vbuf, vh + (size_t)pos0 * D, voff);
+            KTile::load_rows(kbuf, kh + (size_t)pos0 * D, voff, wave_lds);
+            VTile::load_rows(vbuf, vh + (size_t)pos0 * D, voff, wave_lds);
         } else {
             auto rowoff = [&](int r) -> size_t {
                 const int vk = v0 + r;
@@ -500,19 +506,20 @@ void rsa_fwd_bf16(FwdParams p) {
         // running base first; only when some lane's tile sum exceeds
         // kMaxTileSum (always, while the base is still kNoBase) does the wave
         // take the row maximum, move the base up, rescale and form them again.
+        // the row sums after this tile: the dot-product chains continue from
+        // l0 and l1, and the tile's weights were too large if the sum passed lim
         uint32_t pk[QB][2][8];
-        float tl0[QB], tl1[QB];
+        float tl0[QB], tl1[QB], tsum[QB];
         auto weights = [&](int qb) {
-            const float nbase = -m_b[qb] * p.sl2;
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
                 for (int i = 0; i < 8; ++i) {
-                    const float p0 = fast_exp2(fmaf(s[qb][kb][2 * i], p.sl2, nbase));
-                    const float p1 = fast_exp2(fmaf(s[qb][kb][2 * i + 1], p.sl2, nbase));
+                    const float p0 = fast_exp2(fmaf(s[qb][kb][2 * i], p.sl2, nb[qb]));
+                    const float p1 = fast_exp2(fmaf(s[qb][kb][2 * i + 1], p.sl2, nb[qb]));
                     pk[qb][kb][i] = pack_bf16x2(p0, p1);
                 }
-            float a0 = 0.0f, a1 = 0.0f;
+            float a0 = l0[qb], a1 = l1[qb];
 #pragma unroll
             for (int i = 0; i < 8; i += 2) {
                 a0 = add_bf16x2(pk[qb][0][i], a0);
@@ -522,12 +529,13 @@ void rsa_fwd_bf16(FwdParams p) {
             }
             tl0[qb] = a0;
             tl1[qb] = a1;
+            tsum[qb] = a0 + a1;
         };
         bool over = false;
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
             weights(qb);
-            over |= tl0[qb] + tl1[qb] > kMaxTileSum;
+            over |= tsum[qb] > lim[qb];
         }
         if (wave_any(over)) {
 #pragma unroll
@@ -540,6 +548,7 @@ void rsa_fwd_bf16(FwdParams p) {
                 const float m_new = fmaxf(m_b[qb], fmaxf(a, shfl_xor32(a)));
                 const float alpha = fast_exp2((m_b[qb] - m_new) * p.sl2);
                 m_b[qb] = m_new;
+                nb[qb] = -m_new * p.sl2;
                 l0[qb] *= alpha;
                 l1[qb] *= alpha;
 #pragma unroll
@@ -551,8 +560,9 @@ void rsa_fwd_bf16(FwdParams p) {
         }
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
-            l0[qb] += tl0[qb];
-            l1[qb] += tl1[qb];
+            l0[qb] = tl0[qb];
+            l1[qb] = tl1[qb];
+            lim[qb] = tsum[qb] + kMaxTileSum;
         }
         // ---- O^T += V^T P^T, four 16-key steps
 #pragma unroll

@@ -224,7 +224,18 @@ struct DirectTile {
     // Untracked copy of 64 contiguous rows starting at `base` (wave-uniform);
     // IPW copies per wave, waited for with vm_wait.
     __device__ __forceinline__ static void load_rows(uint8_t* lds, const uint16_t* base, const uint32_t (&voff)[IPW]) {
-        const uint32_t l0 = lds_addr(lds) + (uint32_t)(__builtin_amdgcn_readfirstlane(threadIdx.x / kWave) * IPW * 1024);
+        load_rows(lds, base, voff, wave_lds_offset());
+    }
+
+    // Byte offset of this wave's blocks within a tile (wave-uniform), for
+    // callers that compute it once outside their tile loop.
+    __device__ __forceinline__ static uint32_t wave_lds_offset() {
+        return (uint32_t)(__builtin_amdgcn_readfirstlane(threadIdx.x / kWave) * IPW * 1024);
+    }
+
+    __device__ __forceinline__ static void load_rows(uint8_t* lds, const uint16_t* base, const uint32_t (&voff)[IPW],
+                                                     uint32_t wave_lds) {
+        const uint32_t l0 = lds_addr(lds) + wave_lds;
 #pragma unroll
         for (int u = 0; u < IPW; ++u) dma_copy16(base, voff[u], l0 + (uint32_t)(u * 1024));
     }
