@@ -203,6 +203,31 @@ def test_rank_share_sampled_rows(oracle_lib, rank):
         check_lse(lse[0, h, rows], want_lse[0, 0], "bf16", f"rank {rank}")
 
 
+@pytest.mark.parametrize("d", [64, 128])
+def test_unmasked_matches_all_ones_mask_bitwise(d):
+    """Without a key mask (chunk-aligned tiles, not causal) the forward runs an
+    instance that builds no tile table; with an all-ones mask every tile is
+    whole, so the general instance must give the same bits: full forward and
+    one rank's share (split over ring-step groups)."""
+    dev = device()
+    B, H, L, N = 2, 3, 1024, 8
+    x = inputs(B, H, L, d, seed=90 + d, dtype="bf16")
+    q, k, v = (to_dev(x[n], "bf16", dev) for n in ("q", "k", "v"))
+    ones = torch.ones(B, L, dtype=torch.uint8, device=dev)
+    say("unmasked vs all-ones mask", d)
+    a, la = rsa.forward(q, k, v, None, N=N, return_lse=True)
+    b, lb = rsa.forward(q, k, v, ones, N=N, return_lse=True)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b) and torch.equal(la, lb)
+    Lc = L // N
+    for rank in (0, N - 1):
+        ql = q[:, :, rank * Lc:(rank + 1) * Lc].contiguous()
+        a, la = rsa.forward_rank(ql, k, v, None, N=N, rank=rank, return_lse=True)
+        b, lb = rsa.forward_rank(ql, k, v, ones, N=N, rank=rank, return_lse=True)
+        torch.cuda.synchronize()
+        assert torch.equal(a, b) and torch.equal(la, lb), rank
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("L,N,d", [(256, 4, 64), (1024, 32, 128), (600, 6, 64), (96, 96, 128),
                                    # 12 chunks of 128 in 8 ring-step groups: groups take every 8th
