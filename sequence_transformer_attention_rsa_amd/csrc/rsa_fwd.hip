@@ -22,7 +22,8 @@
 //   * online softmax in base 2 (scale and log2(e) folded into one FMA), with
 //     a lazy rescale: the weights are formed against the running base, and
 //     only when some lane's sum of its 32 weights of the tile exceeds 2^12
-//     does the wave take the row maximum, move the base and form them again
+//     (its running row sum grew by more than that) does the wave take the
+//     row maximum, move the base and form them again
 //     (the fp32 kernel moves the base when a tile's maximum exceeds it by
 //     more than 8 in log2 units); exact after the final normalisation;
 //   * tiles are dropped from the occupancy table when the causal variant
@@ -30,10 +31,12 @@
 //   * P is rounded to bf16 for the MFMA and the row sum adds those same
 //     rounded values, so sum_j P_ij = 1 holds for the weights actually used;
 //   * tiles whose keys are all padding are skipped (a per-workgroup
-//     occupancy table built in LDS), so masked chunks cost nothing;
-//   * in split mode (one rank's share), each workgroup covers a contiguous
-//     group of ring steps and writes unnormalised partials that a merge
-//     kernel combines exactly.
+//     occupancy table built in LDS), so masked chunks cost nothing; launches
+//     without any mask on chunk-aligned tiles build no table at all;
+//   * in split mode (one rank's share), each workgroup covers a group of
+//     ring steps (every G-th step on chunk-aligned bf16 tiles, so padded
+//     chunks spread over the groups; a contiguous run otherwise) and writes
+//     unnormalised partials that a merge kernel combines exactly.
 // fp32 inputs use a simpler kernel of the same structure on the 32x32x2
 // fp32 MFMA.
 
