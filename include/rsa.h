@@ -91,9 +91,12 @@ int rsa_forward_ex(const void* q, const void* k, const void* v, const uint8_t* k
  * One rank's share, as one device of the ring computes it (ABSTRACT: no
  * device holds the whole sequence's queries): q_local holds rank `rank`'s
  * L/N query rows, k and v hold all L keys, visited in the ring order of that
- * rank. The ring steps are split into groups processed in parallel; each
+ * rank. The ring steps are split into groups processed in parallel (with
+ * bf16 and L/N a multiple of 64, group g takes every G-th step, so that
+ * padded chunks, met one after another, spread over the groups); each
  * group's unnormalised output and softmax statistics go to `workspace` and
- * are merged exactly (log-sum-exp combination) into out_local.
+ * are merged exactly (log-sum-exp combination) into out_local. Within a
+ * group the steps keep ring order; the grouping changes rounding only.
  *   q_local   [B,H,L/N,d] of dtype (input)
  *   k, v      [B,H,L,d] of dtype (inputs)
  *   workspace device buffer of at least rsa_forward_rank_workspace_bytes()
