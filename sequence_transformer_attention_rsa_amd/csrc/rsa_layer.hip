@@ -222,34 +222,60 @@ __global__ __launch_bounds__(kThreads) void rsa_gemm_bf16(GemmParams p) {
     }
 }
 
-// ---- 256x256 tiles, eight waves ------------------------------------------
-// The same product with twice the tile edge: each contraction step copies
-// (256 + 256) x 64 bf16 for 2 x 256 x 256 x 64 flops, half the L2-to-LDS
-// bytes per flop of the 128x128 tile, and each wave (a 128 x 64 strip, 4x2
-// MFMA blocks) reads 6 fragments per 8 MFMAs instead of 4 per 4. Two stage
-// buffers fill 128 KB of LDS (one workgroup per CU, two waves per SIMD).
+// ---- 256-row tiles, eight waves ------------------------------------------
+// The same product with 256 rows and NT = 256 or 192 columns per tile. At
+// NT = 256 each contraction step copies (256 + 256) x 64 bf16 for
+// 2 x 256 x 256 x 64 flops, half the L2-to-LDS bytes per flop of the
+// 128x128 tile, and each wave (a 128 x 64 strip, 4x2 MFMA blocks) reads 6
+// fragments per 8 MFMAs instead of 4 per 4. NT = 192 (waves of 64 x 96,
+// 2x3 blocks, 5 fragments per 6 MFMAs) exists for the widths that 256
+// columns divide into a poor number of workgroups: N = 768 gives 256
+// workgroups of 256 x 192 for 256 CUs, where 256 x 256 tiles would leave a
+// quarter of the CUs idle. Two stage buffers fill 128 or 112 KB of LDS
+// (one workgroup per CU, two waves per SIMD).
 // The epilogue finishes each value in registers (bias, GeLU, residual read
 // as 8-byte pieces), rounds once to bf16 and stages each wave's strip in
-// its own 16 KB of LDS (16-byte chunks XOR-swizzled by row), from which the
-// wave stores whole 128-byte row segments.
+// its own part of LDS (NT = 256: 128-byte rows with 16-byte chunks
+// XOR-swizzled by row; NT = 192: 192-byte rows at a 208-byte pitch), from
+// which the wave stores whole row segments.
 constexpr int kBigThreads = 512;
 constexpr int kBT = 256;
 using BTile = DirectTile<64, 8>;                 // one copy instruction per wave per 64-row tile
-constexpr int kBigStage = 8 * BTile::BYTES;      // A: tiles 0-3, W: tiles 4-7
-constexpr int kBigLds = 2 * kBigStage;           // 128 KB; the epilogue reuses it
 
-template <int PRO, int EPI>
+template <int NT>
+struct BigShape {
+    static_assert(NT == 256 || NT == 192, "256 or 192 columns");
+    static constexpr int WTILES = NT / 64;                        // W tiles per stage
+    static constexpr int STAGE = (4 + WTILES) * BTile::BYTES;     // A: tiles 0-3, W: tiles 4 ..
+    static constexpr int WM = NT == 256 ? 128 : 64;               // wave strip rows
+    static constexpr int WN = NT == 256 ? 64 : 96;                // wave strip columns
+    static constexpr int MWAVES = kBT / WM;                       // waves along the rows
+    static constexpr int MI = WM / 32, NI = WN / 32;              // MFMA blocks per wave
+    static constexpr int CW = WN / 8;                             // 16-byte chunks per strip row
+    static constexpr int PITCH = NT == 256 ? 128 : 208;           // strip row pitch, bytes
+    static constexpr int LDS = 2 * STAGE;
+    static_assert(MWAVES * (NT / WN) == kBigThreads / kWave, "wave grid");
+    static_assert(8 * WM * PITCH <= LDS, "epilogue strips fit in the stage buffers");
+    static_assert(WM * CW % kWave == 0, "whole store iterations");
+    // byte offset of 16-byte chunk c of strip row ml
+    __device__ __forceinline__ static int pos(int ml, int c) {
+        return NT == 256 ? ml * PITCH + 16 * (c ^ (ml & 7)) : ml * PITCH + 16 * c;
+    }
+};
+
+template <int PRO, int EPI, int NT>
 __global__ __launch_bounds__(kBigThreads) void rsa_gemm_bf16_256(GemmParams p) {
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[kBigLds];
+    using S = BigShape<NT>;
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[S::LDS];
 
     const int lid = xcd_remap(blockIdx.x, p.mt * p.nt);
-    const int m0 = (lid / p.nt) * kBT, n0 = (lid % p.nt) * kBT;
+    const int m0 = (lid / p.nt) * kBT, n0 = (lid % p.nt) * NT;
     const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
     const int j = lane & 31, h = lane >> 5;
-    const int wm = wave & 1, wn = wave >> 1;     // rows 128 wm .., columns 64 wn ..
+    const int wm = wave % S::MWAVES, wn = wave / S::MWAVES;   // rows WM wm .., columns WN wn ..
     const int nk = p.K / kGK;
 
-    uint32_t va[4], vw[4];
+    uint32_t va[4], vw[S::WTILES];
     {
         const int r = wave * BTile::RPI + lane / BTile::CPR;   // tile row this lane copies
         const uint32_t sw = 16u * (uint32_t)((lane % BTile::CPR) ^ BTile::swz(r));
@@ -262,11 +288,11 @@ __global__ __launch_bounds__(kBigThreads) void rsa_gemm_bf16_256(GemmParams p) {
                 const int b = m / p.L, l = m - b * p.L;
                 va[t] = ((uint32_t)(b * p.H) * (uint32_t)p.L + (uint32_t)l) * (uint32_t)(2 * p.d) + sw;
             }
-            vw[t] = (uint32_t)(64 * t + r) * (uint32_t)(2 * p.K) + sw;
+            if (t < S::WTILES) vw[t] = (uint32_t)(64 * t + r) * (uint32_t)(2 * p.K) + sw;
         }
     }
     auto load = [&](int s, int bi) {
-        uint8_t* sb = smem + bi * kBigStage;
+        uint8_t* sb = smem + bi * S::STAGE;
         const uint16_t* abase;
         if constexpr (PRO == kProRows) {
             abase = p.a + (size_t)m0 * p.K + (size_t)s * kGK;
@@ -277,32 +303,34 @@ __global__ __launch_bounds__(kBigThreads) void rsa_gemm_bf16_256(GemmParams p) {
         const uint16_t* wbase = p.w + (size_t)n0 * p.K + (size_t)s * kGK;
         const uint32_t l0 = lds_addr(sb) + (uint32_t)(__builtin_amdgcn_readfirstlane(wave) * 1024);
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            dma_copy16(abase, va[t], l0 + (uint32_t)(t * BTile::BYTES));
-            dma_copy16(wbase, vw[t], l0 + (uint32_t)((4 + t) * BTile::BYTES));
-        }
+        for (int t = 0; t < 4; ++t) dma_copy16(abase, va[t], l0 + (uint32_t)(t * BTile::BYTES));
+#pragma unroll
+        for (int t = 0; t < S::WTILES; ++t) dma_copy16(wbase, vw[t], l0 + (uint32_t)((4 + t) * BTile::BYTES));
     };
 
-    f32x16 acc[2][4];
+    f32x16 acc[S::NI][S::MI];
 #pragma unroll
-    for (int ni = 0; ni < 2; ++ni)
+    for (int ni = 0; ni < S::NI; ++ni)
 #pragma unroll
-        for (int mi = 0; mi < 4; ++mi)
+        for (int mi = 0; mi < S::MI; ++mi)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[ni][mi][r] = 0.0f;
 
     auto compute = [&](int bi) {
-        const uint8_t* sb = smem + bi * kBigStage;
-        const uint8_t* wt = sb + (4 + wn) * BTile::BYTES;
+        const uint8_t* sb = smem + bi * S::STAGE;
+        const uint8_t* wt = sb + 4 * BTile::BYTES;
         // fragments of sub-step ks + 1 are read while the MFMAs of ks run
-        u32x4 af[2][4], wf[2][2];
+        u32x4 af[2][S::MI], wf[2][S::NI];
         auto frags = [&](int ks, int slot) {
 #pragma unroll
-            for (int mi = 0; mi < 4; ++mi)
-                af[slot][mi] = BTile::chunk(sb + (2 * wm + (mi >> 1)) * BTile::BYTES, 32 * (mi & 1) + j, 2 * ks + h);
+            for (int mi = 0; mi < S::MI; ++mi) {
+                const int r = S::WM * wm + 32 * mi;     // tile row of this block
+                af[slot][mi] = BTile::chunk(sb + (r >> 6) * BTile::BYTES, (r & 63) + j, 2 * ks + h);
+            }
 #pragma unroll
-            for (int ni = 0; ni < 2; ++ni) {
-                wf[slot][ni] = BTile::chunk(wt, 32 * ni + j, 2 * ks + h);
+            for (int ni = 0; ni < S::NI; ++ni) {
+                const int c = S::WN * wn + 32 * ni;     // tile column of this block
+                wf[slot][ni] = BTile::chunk(wt + (c >> 6) * BTile::BYTES, (c & 63) + j, 2 * ks + h);
             }
         };
         frags(0, 0);
@@ -310,9 +338,9 @@ __global__ __launch_bounds__(kBigThreads) void rsa_gemm_bf16_256(GemmParams p) {
         for (int ks = 0; ks < kGK / 16; ++ks) {
             if (ks + 1 < kGK / 16) frags(ks + 1, (ks + 1) & 1);
 #pragma unroll
-            for (int ni = 0; ni < 2; ++ni)
+            for (int ni = 0; ni < S::NI; ++ni)
 #pragma unroll
-                for (int mi = 0; mi < 4; ++mi)
+                for (int mi = 0; mi < S::MI; ++mi)
                     acc[ni][mi] = mfma_32x32x16_bf16(wf[ks & 1][ni], af[ks & 1][mi], acc[ni][mi]);
         }
     };
@@ -325,19 +353,19 @@ __global__ __launch_bounds__(kBigThreads) void rsa_gemm_bf16_256(GemmParams p) {
     }
     bare_barrier();   // every wave's last reads of the stage buffers are done
 
-    uint8_t* st = smem + wave * (128 * 128);     // this wave's 128 x 64 bf16 strip
+    uint8_t* st = smem + wave * (S::WM * S::PITCH);   // this wave's WM x WN bf16 strip
 #pragma unroll
-    for (int ni = 0; ni < 2; ++ni)
+    for (int ni = 0; ni < S::NI; ++ni)
 #pragma unroll
         for (int r4 = 0; r4 < 4; ++r4) {
             const int nl = 32 * ni + 8 * r4 + 4 * h;             // strip column of 4
-            const int n = n0 + 64 * wn + nl;
+            const int n = n0 + S::WN * wn + nl;
             f32x4 bv = {0.0f, 0.0f, 0.0f, 0.0f};
             if (p.bias) bv = *reinterpret_cast<const f32x4*>(p.bias + n);
 #pragma unroll
-            for (int mi = 0; mi < 4; ++mi) {
+            for (int mi = 0; mi < S::MI; ++mi) {
                 const int ml = 32 * mi + j;                       // strip row
-                const int m = m0 + 128 * wm + ml;
+                const int m = m0 + S::WM * wm + ml;
                 float o[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
@@ -352,26 +380,25 @@ __global__ __launch_bounds__(kBigThreads) void rsa_gemm_bf16_256(GemmParams p) {
                     o[3] += bf16_hi(rv[1]);
                 }
                 const u32x2 pk = {pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
-                const int c = nl >> 3;                            // 16-byte chunk of the row
-                *reinterpret_cast<u32x2*>(st + ml * 128 + 16 * (c ^ (ml & 7)) + 8 * h) = pk;
+                *reinterpret_cast<u32x2*>(st + S::pos(ml, nl >> 3) + 8 * h) = pk;
             }
         }
     __syncthreads();
 
     uint16_t* dst = p.out0;
-    int ncol0 = n0 + 64 * wn;
+    int ncol0 = n0 + S::WN * wn;
     if constexpr (EPI == kEpiQkv) {
-        const int which = n0 / p.E;   // a 256-column tile never straddles Q, K and V (E % 256 == 0)
+        const int which = n0 / p.E;   // a tile never straddles Q, K and V (E % NT == 0)
         dst = which == 0 ? p.out0 : (which == 1 ? p.out1 : p.out2);
         ncol0 -= which * p.E;
     }
-    const int c = lane & 7;
 #pragma unroll 4
-    for (int it = 0; it < 16; ++it) {
-        const int ml = 8 * it + (lane >> 3);
-        const int m = m0 + 128 * wm + ml;
+    for (int it = 0; it < S::WM * S::CW / kWave; ++it) {
+        const int idx = kWave * it + lane;
+        const int ml = idx / S::CW, c = idx % S::CW;      // strip row, 16-byte chunk
+        const int m = m0 + S::WM * wm + ml;
         if (m >= p.M) continue;
-        const u32x4 v = *reinterpret_cast<const u32x4*>(st + ml * 128 + 16 * (c ^ (ml & 7)));
+        const u32x4 v = *reinterpret_cast<const u32x4*>(st + S::pos(ml, c));
         size_t off;
         if constexpr (EPI == kEpiQkv) {
             const int nn = ncol0 + 8 * c, hh = nn / p.d, dd = nn - hh * p.d;
@@ -455,17 +482,41 @@ __global__ __launch_bounds__(kThreads) void rsa_layernorm_bf16(const uint16_t* _
 #define RSA_GEMM_BIG 1
 #endif
 
+// Compute units of the current device (cached per device).
+int device_cus() {
+    static int cus[64] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cus[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cus[dev] = n;
+    }
+    return cus[dev];
+}
+
 template <int PRO, int EPI>
 hipError_t launch_gemm_t(const GemmParams& p0, hipStream_t stream) {
     GemmParams p = p0;
-    // 256x256 tiles where the widths allow them (a Q/K/V block must not
-    // straddle a 256-column tile), else 128x128
-    const bool big = RSA_GEMM_BIG && p.N % kBT == 0 && (EPI != kEpiQkv || p.E % kBT == 0);
-    if (big) {
-        p.mt = (p.M + kBT - 1) / kBT;
-        p.nt = p.N / kBT;
-        hipLaunchKernelGGL((rsa_gemm_bf16_256<PRO, EPI>), dim3((unsigned)(p.mt * p.nt)), dim3(kBigThreads), 0,
-                           stream, p);
+    // 256-row tiles where the widths allow them (a Q/K/V block must not
+    // straddle a tile), else 128x128. Between 256 and 192 columns, the one
+    // with the shorter schedule: rounds of one workgroup per CU times the
+    // tile's share of a 256x256 tile's work (ties go to 256).
+    auto fits = [&](int nt) { return RSA_GEMM_BIG && p.N % nt == 0 && (EPI != kEpiQkv || p.E % nt == 0); };
+    const long long mt = (p.M + kBT - 1) / kBT, cus = device_cus();
+    auto cost = [&](int nt) { return (mt * (p.N / nt) + cus - 1) / cus * nt; };
+    int nt = 0;
+    if (fits(256)) nt = 256;
+    if (fits(192) && (nt == 0 || cost(192) < cost(256))) nt = 192;
+    if (nt != 0) {
+        p.mt = (int)mt;
+        p.nt = p.N / nt;
+        if (nt == 256)
+            hipLaunchKernelGGL((rsa_gemm_bf16_256<PRO, EPI, 256>), dim3((unsigned)(p.mt * p.nt)), dim3(kBigThreads),
+                               0, stream, p);
+        else
+            hipLaunchKernelGGL((rsa_gemm_bf16_256<PRO, EPI, 192>), dim3((unsigned)(p.mt * p.nt)), dim3(kBigThreads),
+                               0, stream, p);
     } else {
         p.mt = (p.M + kGT - 1) / kGT;
         p.nt = p.N / kGT;

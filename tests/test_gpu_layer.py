@@ -67,7 +67,8 @@ def check_norm(got, want, what):
     (200, 256, 192, "gelu", True, False),     # ragged M, three steps
     (1, 384, 768, "none", True, True),        # a single row
     (129, 128, 128, "gelu", True, True),      # ragged by one row, two steps
-    (1000, 768, 3072, "none", True, True),    # the second MLP product's width
+    (1000, 768, 3072, "none", True, True),    # the second MLP product's width (256 x 192 tiles)
+    (300, 1152, 256, "gelu", True, True),     # 192-column tiles, ragged M, GeLU
 ])
 def test_linear_parity(oracle_lib, M, N, K, act, bias, res):
     from oracle import layer as OL
@@ -92,10 +93,11 @@ def test_linear_parity(oracle_lib, M, N, K, act, bias, res):
 
 
 @pytest.mark.parametrize("B,L,E,H", [
-    (2, 96, 256, 4),      # 256-column tiles (E % 256 == 0)
+    (2, 96, 256, 4),      # 256-column tiles (E % 256 == 0, E % 192 != 0)
     (1, 130, 512, 4),     # d = 128, ragged rows
-    (3, 64, 768, 12),     # BERT-base widths
-    (2, 80, 384, 6),      # 128-column tiles (E % 256 != 0)
+    (3, 64, 768, 12),     # BERT-base widths (192-column tiles)
+    (2, 80, 384, 6),      # 192-column tiles (E % 256 != 0)
+    (2, 70, 640, 10),     # 128-column tiles (E divisible by neither 256 nor 192)
 ])
 def test_qkv_and_output_projection(oracle_lib, B, L, E, H):
     from oracle import layer as OL
