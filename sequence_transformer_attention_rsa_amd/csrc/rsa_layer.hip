@@ -46,14 +46,37 @@ struct GemmParams {
     uint16_t* out1;         // K
     uint16_t* out2;         // V
     int M, N, K;
-    int act;                // 0: none, 1: GeLU (before the residual sum)
     int L, H, d, E;         // token/head layout of the head variants
     int mt, nt;             // tile counts
 };
 
+// erfc(x) from the Chebyshev fit published in Press, Teukolsky, Vetterling
+// and Flannery, Numerical Recipes (section 6.2, the routine erfcc): with
+// t = 1 / (1 + |x|/2), erfc(|x|) = t exp(-x^2 + P(t)) for a degree-9
+// polynomial P, fractional error below 1.2e-7 for every x, and
+// erfc(-|x|) = 2 - erfc(|x|). Branch-free, so one code path serves every
+// lane; in fp32 the rounding of x^2 adds up to ~1.6e-5 relative error at
+// |x| ~ 9, far below the bf16 rounding of the output.
+__device__ __forceinline__ float erfc_fit(float x) {
+    const float ax = fabsf(x);
+    const float t = __builtin_amdgcn_rcpf(fmaf(0.5f, ax, 1.0f));
+    float q = 0.17087277f;
+    q = fmaf(q, t, -0.82215223f);
+    q = fmaf(q, t, 1.48851587f);
+    q = fmaf(q, t, -1.13520398f);
+    q = fmaf(q, t, 0.27886807f);
+    q = fmaf(q, t, -0.18628806f);
+    q = fmaf(q, t, 0.09678418f);
+    q = fmaf(q, t, 0.37409196f);
+    q = fmaf(q, t, 1.00002368f);
+    q = fmaf(q, t, -1.26551223f);
+    const float r = t * __builtin_amdgcn_exp2f(fmaf(-ax, ax, q) * 1.44269504088896341f);
+    return x >= 0.0f ? r : 2.0f - r;
+}
+
 // GeLU(z) = z Phi(z) = z/2 erfc(-z / sqrt 2): the complementary form keeps
 // full fp32 accuracy for negative z, where 1 + erf(z / sqrt 2) would cancel.
-__device__ __forceinline__ float gelu(float z) { return 0.5f * z * erfcf(-z * 0.70710678118654752f); }
+__device__ __forceinline__ float gelu(float z) { return 0.5f * z * erfc_fit(-z * 0.70710678118654752f); }
 
 // out = act(A W^T + bias) + res for one 128x128 tile. Four waves, each a
 // 64x64 quarter as 2x2 MFMA blocks. The MFMA computes the transposed block
@@ -61,7 +84,9 @@ __device__ __forceinline__ float gelu(float z) { return 0.5f * z * erfcf(-z * 0.
 // registers run along the columns: the epilogue then writes four
 // consecutive fp32 columns per lane into an LDS staging tile, from which
 // the whole workgroup stores 16-byte chunks of rows.
-template <int PRO, int EPI>
+// GELU: apply GeLU before the residual sum (a template argument, so that
+// the products without it carry none of its code or registers).
+template <int PRO, int EPI, bool GELU>
 __global__ __launch_bounds__(kThreads) void rsa_gemm_bf16(GemmParams p) {
     __shared__ __attribute__((aligned(1024))) uint8_t smem[kGemmLds];
 
@@ -174,7 +199,7 @@ __global__ __launch_bounds__(kThreads) void rsa_gemm_bf16(GemmParams p) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const float z = acc[ni][mi][4 * r4 + e] + bv[e];
-                    o[e] = p.act ? gelu(z) : z;
+                    o[e] = GELU ? gelu(z) : z;
                 }
                 const int ml = 64 * wm + 32 * mi + j;
                 *reinterpret_cast<f32x4*>(smem + ml * kStagePitch + nl * 4) = o;
@@ -263,7 +288,7 @@ struct BigShape {
     }
 };
 
-template <int PRO, int EPI, int NT>
+template <int PRO, int EPI, int NT, bool GELU>
 __global__ __launch_bounds__(kBigThreads) void rsa_gemm_bf16_256(GemmParams p) {
     using S = BigShape<NT>;
     __shared__ __attribute__((aligned(1024))) uint8_t smem[S::LDS];
@@ -370,7 +395,7 @@ __global__ __launch_bounds__(kBigThreads) void rsa_gemm_bf16_256(GemmParams p) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const float z = acc[ni][mi][4 * r4 + e] + bv[e];
-                    o[e] = p.act ? gelu(z) : z;
+                    o[e] = GELU ? gelu(z) : z;
                 }
                 if (p.res && m < p.M) {
                     const u32x2 rv = *reinterpret_cast<const u32x2*>(p.res + (size_t)m * p.N + n);
@@ -495,7 +520,7 @@ int device_cus() {
     return cus[dev];
 }
 
-template <int PRO, int EPI>
+template <int PRO, int EPI, bool GELU>
 hipError_t launch_gemm_t(const GemmParams& p0, hipStream_t stream) {
     GemmParams p = p0;
     // 256-row tiles where the widths allow them (a Q/K/V block must not
@@ -512,15 +537,15 @@ hipError_t launch_gemm_t(const GemmParams& p0, hipStream_t stream) {
         p.mt = (int)mt;
         p.nt = p.N / nt;
         if (nt == 256)
-            hipLaunchKernelGGL((rsa_gemm_bf16_256<PRO, EPI, 256>), dim3((unsigned)(p.mt * p.nt)), dim3(kBigThreads),
+            hipLaunchKernelGGL((rsa_gemm_bf16_256<PRO, EPI, 256, GELU>), dim3((unsigned)(p.mt * p.nt)), dim3(kBigThreads),
                                0, stream, p);
         else
-            hipLaunchKernelGGL((rsa_gemm_bf16_256<PRO, EPI, 192>), dim3((unsigned)(p.mt * p.nt)), dim3(kBigThreads),
+            hipLaunchKernelGGL((rsa_gemm_bf16_256<PRO, EPI, 192, GELU>), dim3((unsigned)(p.mt * p.nt)), dim3(kBigThreads),
                                0, stream, p);
     } else {
         p.mt = (p.M + kGT - 1) / kGT;
         p.nt = p.N / kGT;
-        hipLaunchKernelGGL((rsa_gemm_bf16<PRO, EPI>), dim3((unsigned)(p.mt * p.nt)), dim3(kThreads), 0, stream,
+        hipLaunchKernelGGL((rsa_gemm_bf16<PRO, EPI, GELU>), dim3((unsigned)(p.mt * p.nt)), dim3(kThreads), 0, stream,
                            p);
     }
     return hipGetLastError();
@@ -540,14 +565,16 @@ hipError_t launch_linear(const LinearCall& c, hipStream_t stream) {
     p.M = c.M;
     p.N = c.N;
     p.K = c.K;
-    p.act = c.act;
     p.L = c.L;
     p.H = c.H;
     p.d = c.d;
     p.E = c.N / 3;
-    if (c.layout == kLinearQkv) return launch_gemm_t<kProRows, kEpiQkv>(p, stream);
-    if (c.layout == kLinearHeadsIn) return launch_gemm_t<kProHeads, kEpiRows>(p, stream);
-    return launch_gemm_t<kProRows, kEpiRows>(p, stream);
+    // GeLU is offered on the row layout only (the first MLP product)
+    if (c.layout != kLinearRows && c.act) return hipErrorInvalidValue;
+    if (c.layout == kLinearQkv) return launch_gemm_t<kProRows, kEpiQkv, false>(p, stream);
+    if (c.layout == kLinearHeadsIn) return launch_gemm_t<kProHeads, kEpiRows, false>(p, stream);
+    if (c.act) return launch_gemm_t<kProRows, kEpiRows, true>(p, stream);
+    return launch_gemm_t<kProRows, kEpiRows, false>(p, stream);
 }
 
 hipError_t launch_layernorm(const void* x, const float* gamma, const float* beta, int rows, int E, float eps,
