@@ -443,47 +443,62 @@ __device__ __forceinline__ float wave_sum(float x) {
 }
 
 // y = (x - mean) / sqrt(var + eps) * gamma + beta over each row of E bf16
-// values; one wave per row, CPL 16-byte chunks per lane, statistics in fp32
-// (the mean first, then the mean squared deviation from it).
-template <int CPL>
+// values; one wave per RPW consecutive rows (all their loads issued before
+// the first reduction, gamma and beta read once per wave), CPL 16-byte
+// chunks per lane and row, statistics in fp32 (the mean first, then the
+// mean squared deviation from it).
+template <int CPL, int RPW>
 __global__ __launch_bounds__(kThreads) void rsa_layernorm_bf16(const uint16_t* __restrict__ x,
                                                                const float* __restrict__ gamma,
                                                                const float* __restrict__ beta,
                                                                uint16_t* __restrict__ y, int rows, int E,
                                                                float eps) {
     const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
-    const long long row = (long long)blockIdx.x * (kThreads / kWave) + wave;
-    if (row >= rows) return;
+    const long long row0 = ((long long)blockIdx.x * (kThreads / kWave) + wave) * RPW;
+    if (row0 >= rows) return;
     const int nch = E / 8;
-    const uint16_t* xr = x + row * E;
-    float v[CPL][8];
-    float s = 0.0f;
+    float v[RPW][CPL][8];
+    float mean[RPW], rstd[RPW];
 #pragma unroll
-    for (int c = 0; c < CPL; ++c) {
-        const int ch = lane + kWave * c;
-        u32x4 w = {0u, 0u, 0u, 0u};
-        if (ch < nch) w = *reinterpret_cast<const u32x4*>(xr + 8 * ch);
+    for (int i = 0; i < RPW; ++i) {
+        const bool ok = row0 + i < rows;   // rows past the end: zeros, never stored
+        const uint16_t* xr = x + (row0 + i) * E;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            v[c][2 * e] = bf16_lo(w[e]);
-            v[c][2 * e + 1] = bf16_hi(w[e]);
-            s += v[c][2 * e] + v[c][2 * e + 1];
-        }
-    }
-    const float mean = wave_sum(s) / (float)E;
-    float q = 0.0f;
+        for (int c = 0; c < CPL; ++c) {
+            const int ch = lane + kWave * c;
+            u32x4 w = {0u, 0u, 0u, 0u};
+            if (ok && ch < nch) w = *reinterpret_cast<const u32x4*>(xr + 8 * ch);
 #pragma unroll
-    for (int c = 0; c < CPL; ++c) {
-        if (lane + kWave * c < nch) {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float dv = v[c][e] - mean;
-                q += dv * dv;
+            for (int e = 0; e < 4; ++e) {
+                v[i][c][2 * e] = bf16_lo(w[e]);
+                v[i][c][2 * e + 1] = bf16_hi(w[e]);
             }
         }
     }
-    const float rstd = 1.0f / sqrtf(wave_sum(q) / (float)E + eps);
-    uint16_t* yr = y + row * E;
+#pragma unroll
+    for (int i = 0; i < RPW; ++i) {
+        float s = 0.0f;
+#pragma unroll
+        for (int c = 0; c < CPL; ++c)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) s += v[i][c][2 * e] + v[i][c][2 * e + 1];
+        mean[i] = wave_sum(s) / (float)E;
+    }
+#pragma unroll
+    for (int i = 0; i < RPW; ++i) {
+        float q = 0.0f;
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) {
+            if (lane + kWave * c < nch) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float dv = v[i][c][e] - mean[i];
+                    q += dv * dv;
+                }
+            }
+        }
+        rstd[i] = 1.0f / sqrtf(wave_sum(q) / (float)E + eps);
+    }
 #pragma unroll
     for (int c = 0; c < CPL; ++c) {
         const int ch = lane + kWave * c;
@@ -494,12 +509,16 @@ __global__ __launch_bounds__(kThreads) void rsa_layernorm_bf16(const uint16_t* _
         const f32x4 b1 = *reinterpret_cast<const f32x4*>(beta + 8 * ch + 4);
         const float g[8] = {g0[0], g0[1], g0[2], g0[3], g1[0], g1[1], g1[2], g1[3]};
         const float b[8] = {b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
-        u32x4 o;
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-            o[e] = pack_bf16x2((v[c][2 * e] - mean) * rstd * g[2 * e] + b[2 * e],
-                               (v[c][2 * e + 1] - mean) * rstd * g[2 * e + 1] + b[2 * e + 1]);
-        *reinterpret_cast<u32x4*>(yr + 8 * ch) = o;
+        for (int i = 0; i < RPW; ++i) {
+            if (row0 + i >= rows) continue;
+            u32x4 o;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                o[e] = pack_bf16x2((v[i][c][2 * e] - mean[i]) * rstd[i] * g[2 * e] + b[2 * e],
+                                   (v[i][c][2 * e + 1] - mean[i]) * rstd[i] * g[2 * e + 1] + b[2 * e + 1]);
+            *reinterpret_cast<u32x4*>(y + (row0 + i) * E + 8 * ch) = o;
+        }
     }
 }
 
@@ -579,22 +598,23 @@ hipError_t launch_linear(const LinearCall& c, hipStream_t stream) {
 
 hipError_t launch_layernorm(const void* x, const float* gamma, const float* beta, int rows, int E, float eps,
                             void* y, hipStream_t stream) {
-    const unsigned blocks = (unsigned)((rows + 3) / 4);
     const uint16_t* xi = static_cast<const uint16_t*>(x);
     uint16_t* yo = static_cast<uint16_t*>(y);
     const int cpl = (E / 8 + kWave - 1) / kWave;
+    // rows per wave so that each lane holds 64 values of x
+    auto blocks = [&](int rpw) { return (unsigned)((rows + 4 * rpw - 1) / (4 * rpw)); };
     if (cpl <= 1)
-        hipLaunchKernelGGL((rsa_layernorm_bf16<1>), dim3(blocks), dim3(kThreads), 0, stream, xi, gamma, beta, yo,
-                           rows, E, eps);
+        hipLaunchKernelGGL((rsa_layernorm_bf16<1, 8>), dim3(blocks(8)), dim3(kThreads), 0, stream, xi, gamma, beta,
+                           yo, rows, E, eps);
     else if (cpl <= 2)
-        hipLaunchKernelGGL((rsa_layernorm_bf16<2>), dim3(blocks), dim3(kThreads), 0, stream, xi, gamma, beta, yo,
-                           rows, E, eps);
+        hipLaunchKernelGGL((rsa_layernorm_bf16<2, 4>), dim3(blocks(4)), dim3(kThreads), 0, stream, xi, gamma, beta,
+                           yo, rows, E, eps);
     else if (cpl <= 4)
-        hipLaunchKernelGGL((rsa_layernorm_bf16<4>), dim3(blocks), dim3(kThreads), 0, stream, xi, gamma, beta, yo,
-                           rows, E, eps);
+        hipLaunchKernelGGL((rsa_layernorm_bf16<4, 2>), dim3(blocks(2)), dim3(kThreads), 0, stream, xi, gamma, beta,
+                           yo, rows, E, eps);
     else
-        hipLaunchKernelGGL((rsa_layernorm_bf16<8>), dim3(blocks), dim3(kThreads), 0, stream, xi, gamma, beta, yo,
-                           rows, E, eps);
+        hipLaunchKernelGGL((rsa_layernorm_bf16<8, 1>), dim3(blocks(1)), dim3(kThreads), 0, stream, xi, gamma, beta,
+                           yo, rows, E, eps);
     return hipGetLastError();
 }
 
