@@ -218,7 +218,8 @@ int rsa_backward_dkdv(const void* q, const void* k, const void* v, const void* d
 
 /*
  * out[M,N] = act(a[M,K] w[N,K]^T + bias[N]) + residual[M,N]
- *   activation  0: none, 1: GeLU (exact erf form) applied before the residual
+ *   activation  0: none, 1: GeLU in its erf form, z Phi(z) (not the tanh approximation;
+ *               erfc to 1.2e-7 relative), applied before the residual
  *   bias, residual  may be NULL
  */
 int rsa_linear(const void* a, const void* w, const float* bias, const void* residual, int M, int N, int K,
