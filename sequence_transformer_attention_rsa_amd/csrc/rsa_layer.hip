@@ -11,6 +11,8 @@
 // (2) and (3)) describes the two fully connected layers with GeLU and the
 // independent attention heads.
 
+#include <atomic>
+
 #include "rsa_internal.h"
 #include "rsa_tiles.h"
 
@@ -526,17 +528,18 @@ __global__ __launch_bounds__(kThreads) void rsa_layernorm_bf16(const uint16_t* _
 #define RSA_GEMM_BIG 1
 #endif
 
-// Compute units of the current device (cached per device).
+// Compute units of the current device (cached per device; threads that
+// race on the first call store the same value).
 int device_cus() {
-    static int cus[64] = {};
+    static std::atomic<int> cus[64];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    if (cus[dev] == 0) {
-        int n = 0;
+    int n = cus[dev].load(std::memory_order_relaxed);
+    if (n == 0) {
         if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-        cus[dev] = n;
+        cus[dev].store(n, std::memory_order_relaxed);
     }
-    return cus[dev];
+    return n;
 }
 
 template <int PRO, int EPI, bool GELU>
