@@ -52,9 +52,11 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kKT = kFwdKeyTile;   // keys per tile
 constexpr int kQW = 32;            // query rows per wave
-// Initial running base (raw score units) of the bf16 kernel: finite and far
-// below any score, so that every valid weight formed against it overflows to
-// +inf and forces the first rescale, while padded keys (-inf) give weight 0.
+// Initial running base (raw score units) of both kernels: finite and far
+// below any score, so that a row's first visible key forces a rescale (in the
+// bf16 kernel every valid weight formed against it overflows to +inf), padded
+// keys (-inf) give weight 0, and a rescale of a row that has seen no key yet
+// keeps a factor of exactly 1.
 constexpr float kNoBase = -1.0e30f;
 // Largest sum of one lane's 32 weights of a tile before the running base is
 // moved up (each weight then stays <= 2^12, far from fp32 and bf16 limits).
@@ -142,7 +144,10 @@ __global__ __launch_bounds__(kThreads) void rsa_fwd_f32(FwdParams p) {
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
         for (int r = 0; r < 16; ++r) o[db][r] = 0.0f;
-    float m_b = -INFINITY;   // running base, raw score units
+    // running base (raw score units): the finite sentinel kNoBase until the
+    // row meets a visible key, so that a rescale forced by another lane of
+    // the wave never forms -inf - (-inf) for a row that has seen none yet
+    float m_b = kNoBase;
     float l = 0.0f;          // running row sum over this lane half's keys
 
     __syncthreads();   // tile flags visible

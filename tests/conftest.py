@@ -22,3 +22,15 @@ def oracle_lib():
     if not os.path.exists(os.path.join(ROOT, "oracle", "liboracle.so")):
         oracle.build()
     return oracle
+
+
+def pytest_terminal_summary(terminalreporter):
+    """Print the full-size parity results (max-abs and relative Frobenius error
+    against the fp64 oracle) that the GPU tests recorded."""
+    mod = sys.modules.get("gpu_util")
+    rows = getattr(mod, "PARITY_REPORT", None) if mod else None
+    if not rows:
+        return
+    terminalreporter.write_sep("-", "parity vs fp64 oracle (full-size workloads)")
+    for what, max_abs, rel in rows:
+        terminalreporter.write_line(f"{what:<44} max-abs {max_abs:.3e}  rel-fro {rel:.3e}")

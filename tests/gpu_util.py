@@ -24,6 +24,15 @@ def say(*args):
     sys.stdout.flush()
 
 
+PARITY_REPORT = []
+
+
+def report(what: str, e: dict):
+    """Record a parity result (errors() dict) for the end-of-run summary."""
+    PARITY_REPORT.append((what, e["max_abs"], e["rel_fro"]))
+    say(what, f"max-abs {e['max_abs']:.3e} rel-fro {e['rel_fro']:.3e}")
+
+
 def to_dev(x: np.ndarray, dtype: str, dev) -> torch.Tensor:
     """Exact upload: fp32 values (bf16-representable for "bf16")."""
     t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))

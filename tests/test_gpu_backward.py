@@ -9,7 +9,7 @@ import torch
 import rsa_inputs
 import sequence_transformer_attention_rsa_amd as rsa
 from gates import assert_parity
-from gpu_util import device, from_dev, inputs, mask_dev, say, to_dev
+from gpu_util import device, report, from_dev, inputs, mask_dev, say, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -110,19 +110,47 @@ def test_backward_invariants():
     assert np.abs(dv.sum(axis=2) - gsum).max() <= 2e-2 * np.abs(gsum).max() + 0.05
 
 
-def test_backward_workload_sampled_heads(oracle_lib):
-    """B=4, H=12, L=4096, d=64, N=8, key padding: the full launch, checked
-    element by element on two heads (the oracle computes each head alone)."""
+def test_backward_workload_full_parity(oracle_lib):
+    """B=4, H=12, L=4096, d=64, N=8, key padding: dQ, dK and dV of all 48
+    heads element by element, each head also on its own."""
     w = rsa_inputs.WORKLOADS["backward"]
     dev = device()
     x = rsa_inputs.workload_inputs(w)
-    say("workload backward")
-    dq, dk, dv = gpu_fwd_bwd(x, w.N, dev)
-    for b, h in ((0, 0), (3, 7)):
-        sl = (slice(b, b + 1), slice(h, h + 1))
-        want = oracle_lib.backward(x["q"][sl], x["k"][sl], x["v"][sl], x["dout"][sl],
-                                   x["mask"][b:b + 1], N=w.N)
-        check_grads((dq[sl], dk[sl], dv[sl]), want, f"backward b={b} h={h}")
+    say("workload backward, all heads")
+    got = gpu_fwd_bwd(x, w.N, dev)
+    want = oracle_lib.backward(x["q"], x["k"], x["v"], x["dout"], x["mask"], N=w.N)
+    for name, a, b in zip(("dq", "dk", "dv"), got, want):
+        report(f"backward {name} (48 heads)", assert_parity(a, b, "bf16", f"backward {name}", grad=True))
+    for bb in range(w.B):
+        for h in range(w.H):
+            sl = (bb, h)
+            check_grads([g[sl] for g in got], [g[sl] for g in want], f"backward b={bb} h={h}")
+
+
+def test_backward_long_sequence_four_heads(oracle_lib):
+    """The bench's own step at B=2, H=12, L=8192, d=64, N=16, no mask: the
+    forward and the three backward stages exactly as the bench launches them
+    (preprocess, dQ, dK/dV), and the gradients of the first and last head of
+    both batch rows against the oracle, element by element."""
+    w = rsa_inputs.WORKLOADS["long_seq"]
+    dev = device()
+    x = rsa_inputs.make_inputs(w.B, w.H, w.L, w.d, w.seed, w.dtype, w.scale, w.valid_range, with_dout=True)
+    q, k, v, g = (to_dev(x[n], "bf16", dev) for n in ("q", "k", "v", "dout"))
+    say("long_seq backward stages")
+    out, lse = rsa.forward(q, k, v, None, N=w.N, return_lse=True)
+    stats = rsa.backward_preprocess(out, g, lse)
+    dq = rsa.backward_dq(q, k, v, g, stats, None, N=w.N)
+    dk, dv = rsa.backward_dkdv(q, k, v, g, stats, None, N=w.N)
+    torch.cuda.synchronize()
+    got = [from_dev(t) for t in (dq, dk, dv)]
+    heads = ((0, 0), (0, w.H - 1), (1, 0), (1, w.H - 1))
+    sel = lambda a: np.stack([a[b, h] for b, h in heads])[None]
+    want = oracle_lib.backward(sel(x["q"]), sel(x["k"]), sel(x["v"]), sel(x["dout"]), None, N=w.N)
+    for name, a, b in zip(("dq", "dk", "dv"), got, want):
+        report(f"long_seq backward {name} (4 heads)",
+               assert_parity(sel(a), b, "bf16", f"long_seq {name}", grad=True))
+        for i, (bb, h) in enumerate(heads):
+            assert_parity(a[bb, h], b[0, i], "bf16", f"long_seq {name} b={bb} h={h}", grad=True)
 
 
 def test_backward_longest_key_range():

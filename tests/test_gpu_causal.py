@@ -9,12 +9,11 @@ import torch
 
 import rsa_inputs
 import sequence_transformer_attention_rsa_amd as rsa
-from gates import assert_parity
+from gates import LSE_TOL, assert_parity
 from gpu_util import device, from_dev, inputs, mask_dev, sample_rows, say, to_dev
 
 pytestmark = pytest.mark.gpu
 
-LSE_TOL = {"f32": 1e-5, "bf16": 2e-3}
 
 
 def check_lse(got, want, dtype, what):
@@ -178,3 +177,58 @@ def test_causal_backward_every_ring_size(oracle_lib):
         torch.cuda.synchronize()
         for name, a, b in zip(("dq", "dk", "dv"), (dq, dk, dv), want):
             assert_parity(from_dev(a), b, "bf16", f"causal N={N} {name}", grad=True)
+
+
+def padded_mask(B, L, N, kind):
+    """Key masks that leave early query rows without any visible key under the
+    causal mask: "left" pads the first keys of the sequence, "hole" pads the
+    first keys of every chunk (every other chunk entirely in its first half)."""
+    Lc = L // N
+    m = np.ones((B, L), np.uint8)
+    if kind == "left":
+        m[0, :37] = 0
+        m[1, :Lc + 5] = 0
+    else:
+        for c in range(N):
+            m[0, c * Lc:c * Lc + min(3, Lc)] = 0
+            if c % 2 == 1:
+                m[1, c * Lc:c * Lc + max(1, Lc // 2)] = 0
+        m[1, :1] = 0
+    return m
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("L,N,kind", [(256, 4, "left"), (512, 8, "hole"), (200, 5, "left"), (200, 5, "hole"),
+                                      (384, 3, "hole")])
+def test_causal_padding_before_visible_keys(oracle_lib, dtype, d, L, N, kind):
+    """Causal mask plus key padding at the start of the sequence or of each
+    chunk: the first rows see no key at all (output 0, lse -inf), and within
+    one wave some rows meet their first visible key while others have seen
+    none yet, so a rescale must leave the latter untouched (never NaN). The
+    full forward and one rank's share (ring-step groups + merge)."""
+    dev = device()
+    x = inputs(2, 2, L, d, seed=L + 3 * N + d + (kind == "hole"), dtype=dtype)
+    x["mask"] = padded_mask(2, L, N, kind)
+    say("causal padded", dtype, d, L, N, kind)
+    out, lse = gpu_forward(x, dtype, N, dev)
+    want, want_lse = oracle_lib.forward(x["q"], x["k"], x["v"], x["mask"], N=N, causal=True)
+    assert np.all(np.isfinite(out)), "non-finite output"
+    empty = np.isneginf(want_lse)
+    assert empty.any()
+    assert np.all(out[empty] == 0.0) and np.all(np.isneginf(lse[empty]))
+    assert_parity(out, want, dtype, f"causal padded {kind} {dtype} d={d} L={L} N={N}")
+    check_lse(lse, want_lse, dtype, "causal padded lse")
+    Lc = L // N
+    k, v = to_dev(x["k"], dtype, dev), to_dev(x["v"], dtype, dev)
+    m = mask_dev(x["mask"], dev)
+    for rank in sorted({0, 1, N - 1}):
+        rows = np.arange(rank * Lc, (rank + 1) * Lc)
+        ql = to_dev(x["q"][:, :, rows], dtype, dev)
+        say("causal padded rank share", dtype, d, L, N, kind, rank)
+        o, ls = rsa.forward_rank(ql, k, v, m, N=N, rank=rank, return_lse=True, causal=True)
+        torch.cuda.synchronize()
+        o, ls = from_dev(o), ls.cpu().numpy().astype(np.float64)
+        assert np.all(np.isfinite(o)), f"rank {rank}: non-finite output"
+        assert_parity(o, want[:, :, rows], dtype, f"causal padded rank {rank}")
+        check_lse(ls, want_lse[:, :, rows], dtype, f"causal padded rank {rank}")

@@ -8,12 +8,12 @@ import torch
 
 import rsa_inputs
 import sequence_transformer_attention_rsa_amd as rsa
-from gates import MAX_ABS, assert_parity
+from gates import LSE_TOL as _LSE_TOL, MAX_ABS, assert_parity
 from gpu_util import device, from_dev, inputs, mask_dev, sample_rows, say, to_dev
 
 pytestmark = pytest.mark.gpu
 
-LSE_TOL = 2e-3
+LSE_TOL = _LSE_TOL["bf16"]
 
 
 def run(x, N, dev, fused=False):

@@ -167,3 +167,69 @@ def test_bf16_store_mode_rounds_every_kept_activation():
     # nine rounding points of relative size 2^-9 each, through O(1) layer gains
     assert np.abs(r["y"] - exact).max() < 0.1
     assert np.linalg.norm(r["y"] - exact) / np.linalg.norm(exact) < 2e-2
+
+
+# ------------------------------------------------- bf16 store mode, exactly ---
+
+POINTS = ("q", "k", "v", "o", "a1", "h1", "f1", "a2", "y")
+
+
+def torch_layer_bf16(inp, H, drop=(), move=None):
+    """The layer written independently with torch fp64 operations (linear,
+    scaled_dot_product_attention with a boolean key mask, layer_norm, exact
+    GeLU), rounding to bf16 with torch's own conversion at the nine points
+    where a bf16 implementation stores an activation: Q, K, V, O, A1, h1, F1,
+    A2, y. `drop` removes roundings; `move` places one elsewhere:
+      "gelu_in"   F1 rounded before the GeLU instead of after it,
+      "a1_prod"   A1's product rounded before the residual sum instead of after,
+      "a2_prod"   the same for A2,
+      "a1_twice"  A1's product rounded before the residual sum and A1 after it,
+      "a2_twice"  the same for A2."""
+    f = torch.nn.functional
+    T = lambda a: torch.from_numpy(np.asarray(a, np.float64))
+    bf = lambda t: t.to(torch.bfloat16).to(torch.float64)
+    r = lambda name, t: t if name in drop else bf(t)
+    x = T(inp["x"])
+    B, Ls, E = x.shape
+    d = E // H
+    t = f.linear(x, T(inp["w_qkv"]), T(inp["b_qkv"]))
+    heads = lambda u: u.reshape(B, Ls, H, d).transpose(1, 2)
+    q, k, v = (r(n, heads(t[..., i * E:(i + 1) * E])) for i, n in enumerate(("q", "k", "v")))
+    mask = None if inp["mask"] is None else T(inp["mask"]).bool()[:, None, None, :]
+    o = r("o", f.scaled_dot_product_attention(q, k, v, attn_mask=mask))
+    z1 = f.linear(o.transpose(1, 2).reshape(B, Ls, E), T(inp["w_o"]), T(inp["b_o"]))
+    if move in ("a1_prod", "a1_twice"):
+        z1 = bf(z1)
+    a1 = z1 + x if move == "a1_prod" else r("a1", z1 + x)
+    h1 = r("h1", f.layer_norm(a1, (E,), T(inp["ln1_gamma"]), T(inp["ln1_beta"]), eps=1e-12))
+    z = f.linear(h1, T(inp["w_ff1"]), T(inp["b_ff1"]))
+    f1 = f.gelu(bf(z)) if move == "gelu_in" else r("f1", f.gelu(z))
+    z2 = f.linear(f1, T(inp["w_ff2"]), T(inp["b_ff2"]))
+    if move in ("a2_prod", "a2_twice"):
+        z2 = bf(z2)
+    a2 = z2 + h1 if move == "a2_prod" else r("a2", z2 + h1)
+    y = r("y", f.layer_norm(a2, (E,), T(inp["ln2_gamma"]), T(inp["ln2_beta"]), eps=1e-12))
+    return {"q": q, "k": k, "v": v, "o": o, "a1": a1, "h1": h1, "f1": f1, "a2": a2, "y": y}
+
+
+def test_bf16_store_mode_equals_torch_at_the_nine_points():
+    """The oracle's bf16 store mode equals, value for value, an independent
+    torch evaluation that rounds with torch's bf16 conversion at exactly the
+    nine kept activations; every plausible misplacement of a rounding (one
+    left out, one moved before the GeLU or before a residual sum, one applied
+    twice around a residual sum) changes the result, so the equality pins
+    the placement."""
+    inp = small_inputs(seed=8, valid=(6, 12))
+    got = L.layer_forward(inp, H=2, N=3, store="bf16")
+    want = torch_layer_bf16(inp, 2)
+    for name in POINTS:
+        w = want[name].numpy()
+        if name in ("q", "k", "v", "o"):
+            w = np.ascontiguousarray(w)
+        assert np.array_equal(got[name], w), name
+    variants = [dict(drop=(p,)) for p in POINTS] + [dict(move=m) for m in
+                                                    ("gelu_in", "a1_prod", "a2_prod", "a1_twice", "a2_twice")]
+    for var in variants:
+        alt = torch_layer_bf16(inp, 2, **var)
+        diff = [n for n in POINTS if not np.array_equal(got[n], alt[n].numpy())]
+        assert "y" in diff, f"{var}: the misplaced rounding leaves y unchanged"
