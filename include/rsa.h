@@ -54,7 +54,8 @@ typedef enum rsa_status {
     RSA_ERR_UNSUPPORTED = 3, /* d not in {64, 128}, unknown dtype, or a size beyond the kernels' range */
     RSA_ERR_ALIGN = 4,       /* a tensor pointer is not 16-byte aligned */
     RSA_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than the query function returns */
-    RSA_ERR_HIP = 6          /* the HIP runtime reported an error at launch */
+    RSA_ERR_HIP = 6,         /* the HIP runtime reported an error at launch */
+    RSA_ERR_SCRATCH = 7      /* rsa_backward_noalloc: the sizes need more than its static scratch */
 } rsa_status;
 
 typedef enum rsa_dtype { RSA_F32 = 0, RSA_BF16 = 1 } rsa_dtype;
@@ -169,6 +170,28 @@ int rsa_backward_ex(const void* q, const void* k, const void* v, const void* out
 
 /* Workspace bytes rsa_backward needs for these sizes (0 if they are invalid). */
 size_t rsa_backward_workspace_bytes(int B, int H, int L, int d, int N, int dtype);
+
+/*
+ * rsa_backward_ex for callers that cannot allocate device memory where they
+ * call it: code under HIP graph capture, serving loops that must not
+ * allocate, harnesses that forbid hipMalloc. Same arguments, results and
+ * validation as rsa_backward_ex without the workspace: the row statistics go
+ * to a static array in device memory of RSA_NOALLOC_SCRATCH_BYTES (16 MiB),
+ * which each GPU the library runs on holds until the process ends. Limit:
+ * rsa_backward_workspace_bytes() <= RSA_NOALLOC_SCRATCH_BYTES, i.e.
+ * B * H * L <= 2097152 query rows; larger sizes return RSA_ERR_SCRATCH
+ * before any HIP call. The first call on a device resolves the array's
+ * address there (hipGetSymbolAddress; no allocation): make one call before
+ * capturing a graph. Every call on one GPU shares the array, so calls that
+ * overlap on one GPU (several streams or threads) race; the caller
+ * serialises them. The array needs no clearing: the backward's first stage
+ * writes every value its later stages read.
+ */
+#define RSA_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+int rsa_backward_noalloc(const void* q, const void* k, const void* v, const void* out, const void* dout,
+                         const float* lse, const uint8_t* key_mask,
+                         int B, int H, int L, int d, int N, int dtype, int flags,
+                         void* stream, void* dq, void* dk, void* dv);
 
 /*
  * The three stages rsa_backward runs, for callers that schedule them

@@ -32,12 +32,14 @@ __all__ = [
     "forward_rank_workspace_bytes", "forward_twopass_workspace_bytes", "backward_workspace_bytes",
     "status_string", "linear", "qkv_projection", "output_projection", "layernorm", "layer_forward",
     "layer_forward_workspace_bytes", "LAYER_WEIGHTS",
+    "backward_noalloc", "NOALLOC_SCRATCH_BYTES",
     "RSA_F32", "RSA_BF16",
 ]
 
 RSA_F32 = 0
 RSA_BF16 = 1
 RSA_CAUSAL = 1
+NOALLOC_SCRATCH_BYTES = 16 << 20   # RSA_NOALLOC_SCRATCH_BYTES
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "librsa.so")
@@ -62,6 +64,8 @@ SIGNATURES = {
     "rsa_backward_ex": (_ci, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _ci, _ci, _ci, _ci, _ci, _ci, _ci,
                               _vp, _sz, _vp, _vp, _vp, _vp]),
     "rsa_backward_workspace_bytes": (_sz, [_ci, _ci, _ci, _ci, _ci, _ci]),
+    "rsa_backward_noalloc": (_ci, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _ci, _ci, _ci, _ci, _ci, _ci, _ci,
+                                   _vp, _vp, _vp, _vp]),
     "rsa_backward_preprocess": (_ci, [_vp, _vp, _vp, _ci, _ci, _ci, _ci, _ci, _vp, _vp]),
     "rsa_backward_dq": (_ci, [_vp, _vp, _vp, _vp, _vp, _vp, _ci, _ci, _ci, _ci, _ci, _ci, _vp, _vp]),
     "rsa_backward_dkdv": (_ci, [_vp, _vp, _vp, _vp, _vp, _vp, _ci, _ci, _ci, _ci, _ci, _ci, _vp, _vp, _vp]),
@@ -341,6 +345,30 @@ def backward(q, k, v, out, dout, lse, key_mask=None, N: int = 1, dq=None, dk=Non
                                  _ptr(dq), _ptr(dk), _ptr(dv))
     if st != 0:
         raise RSAError(st, "rsa_backward")
+    return dq, dk, dv
+
+
+def backward_noalloc(q, k, v, out, dout, lse, key_mask=None, N: int = 1, dq=None, dk=None, dv=None,
+                     causal: bool = False):
+    """backward() without a workspace: the library keeps the row statistics in
+    its static device array (at most B*H*L = 2097152 rows; calls that overlap
+    on one GPU race). Pass dq, dk and dv to allocate nothing at all."""
+    B, H, L, d = q.shape
+    dev = q.device
+    for name, t in (("q", q), ("k", k), ("v", v), ("out", out), ("dout", dout)):
+        _need(t, name, (B, H, L, d), q.dtype, dev)
+    _need(lse, "lse", (B, H, L), torch.float32, dev)
+    m = _mask(key_mask, B, L, dev)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(q) if dk is None else dk
+    dv = torch.empty_like(q) if dv is None else dv
+    for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+        _need(t, name, (B, H, L, d), q.dtype, dev)
+    st = load().rsa_backward_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(lse), _ptr(m),
+                                     B, H, L, d, int(N), _dtype_code(q), RSA_CAUSAL if causal else 0,
+                                     _stream(dev), _ptr(dq), _ptr(dk), _ptr(dv))
+    if st != 0:
+        raise RSAError(st, "rsa_backward_noalloc")
     return dq, dk, dv
 
 

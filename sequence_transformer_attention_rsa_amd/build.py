@@ -22,7 +22,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "librsa.so")
 
-SOURCES = ["rsa_fwd.hip", "rsa_twopass.hip", "rsa_bwd.hip", "rsa_layer.hip", "rsa_api.cpp"]
+SOURCES = ["rsa_fwd.hip", "rsa_twopass.hip", "rsa_bwd.hip", "rsa_layer.hip", "rsa_static.hip", "rsa_api.cpp"]
 ARCH = "gfx950"
 
 

@@ -85,6 +85,23 @@ size_t layer_workspace(int B, int L, int E, int F) {
 
 }  // namespace
 
+namespace rsa {
+
+int check_backward_call(const void* q, const void* k, const void* v, const void* out, const void* dout,
+                        const float* lse, const uint8_t* key_mask, int B, int H, int L, int d, int N, int dtype,
+                        int flags, const void* dq, const void* dk, const void* dv) {
+    if (!q || !k || !v || !out || !dout || !lse || !dq || !dk || !dv) return RSA_ERR_NULL;
+    int st = check_backward(B, H, L, d, N, dtype);
+    if (st != RSA_OK) return st;
+    if (flags & ~RSA_CAUSAL) return RSA_ERR_UNSUPPORTED;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) || !aligned(dout, 16) ||
+        !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) || !aligned(key_mask, 16) || !aligned(lse, 4))
+        return RSA_ERR_ALIGN;
+    return RSA_OK;
+}
+
+}  // namespace rsa
+
 extern "C" {
 
 int rsa_forward(const void* q, const void* k, const void* v, const uint8_t* key_mask,
@@ -234,14 +251,9 @@ int rsa_backward_ex(const void* q, const void* k, const void* v, const void* out
                     int B, int H, int L, int d, int N, int dtype, int flags,
                     void* workspace, size_t workspace_bytes,
                     void* stream, void* dq, void* dk, void* dv) {
-    if (!q || !k || !v || !out || !dout || !lse || !dq || !dk || !dv) return RSA_ERR_NULL;
-    int st = check_backward(B, H, L, d, N, dtype);
+    int st = rsa::check_backward_call(q, k, v, out, dout, lse, key_mask, B, H, L, d, N, dtype, flags, dq, dk, dv);
     if (st != RSA_OK) return st;
-    if (flags & ~RSA_CAUSAL) return RSA_ERR_UNSUPPORTED;
-    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) || !aligned(dout, 16) ||
-        !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) || !aligned(key_mask, 16) ||
-        !aligned(lse, 4) || !aligned(workspace, 16))
-        return RSA_ERR_ALIGN;
+    if (!aligned(workspace, 16)) return RSA_ERR_ALIGN;
     if (!workspace || workspace_bytes < rsa::backward_workspace_bytes(B, H, L, d)) return RSA_ERR_WORKSPACE;
     rsa::BackwardCall c = backward_call(q, k, v, out, dout, lse, key_mask, B, H, L, d, N);
     c.stats = static_cast<float*>(workspace);
@@ -488,6 +500,9 @@ const char* rsa_status_string(int status) {
         case RSA_ERR_ALIGN: return "RSA_ERR_ALIGN: tensor pointers must be 16-byte aligned (lse 4-byte)";
         case RSA_ERR_WORKSPACE: return "RSA_ERR_WORKSPACE: workspace missing or too small";
         case RSA_ERR_HIP: return "RSA_ERR_HIP: the HIP runtime reported a launch error";
+        case RSA_ERR_SCRATCH:
+            return "RSA_ERR_SCRATCH: rsa_backward_noalloc holds the row statistics of at most 2097152 query rows "
+                   "(B * H * L) in its 16 MiB static scratch";
         default: return "unknown rsa_status";
     }
 }

@@ -64,6 +64,13 @@ struct BackwardCall {
 
 size_t backward_workspace_bytes(int B, int H, int L, int d);
 
+// Every check of rsa_backward_ex except the workspace's: NULL pointers,
+// sizes, dtype, flags and alignment, before any HIP call. Returns an
+// rsa_status.
+int check_backward_call(const void* q, const void* k, const void* v, const void* out, const void* dout,
+                        const float* lse, const uint8_t* key_mask, int B, int H, int L, int d, int N, int dtype,
+                        int flags, const void* dq, const void* dk, const void* dv);
+
 // Backward stages (bit mask): row statistics; dq; dk and dv.
 constexpr int kBwdStagePre = 1;
 constexpr int kBwdStageDq = 2;

@@ -42,7 +42,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_status_strings(lib):
-    for code in range(7):
+    for code in range(8):
         assert rsa.status_string(code).startswith("RSA_")
     assert "unknown" in rsa.status_string(99)
 
@@ -208,3 +208,24 @@ def test_flag_validation(lib):
     assert lib.rsa_backward_ex(P, P, P, P, P, P, None, 1, 2, 256, 64, 4, BF16, 8, P, bws, None, P, P, P) == EUNSUP
     assert lib.rsa_backward_ex(P, P, P, P, P, P, None, 1, 2, 256, 64, 4, F32, 1, P, bws, None, P, P, P) == EUNSUP
     assert lib.rsa_backward_ex(P, P, P, P, P, P, None, 1, 2, 256, 64, 4, BF16, 1, None, bws, None, P, P, P) == EWS
+
+
+def test_backward_noalloc_validation(lib):
+    """The no-allocation backward validates like rsa_backward_ex and rejects
+    sizes beyond its static scratch (RSA_ERR_SCRATCH), all before any HIP
+    call."""
+    ESCRATCH = 7
+
+    def call(B=1, H=2, L=256, N=4, dtype=BF16, flags=0, lse=P, dq=P):
+        return lib.rsa_backward_noalloc(P, P, P, P, P, lse, None, B, H, L, 64, N, dtype, flags, None, dq, P, P)
+
+    assert call(lse=None) == ENULL
+    assert call(dq=None) == ENULL
+    assert call(L=255) == ESHAPE
+    assert call(flags=8) == EUNSUP
+    assert call(dq=P + 2) == EALIGN
+    # 2 * 4 bytes per query row in a 16 MiB array: 2097152 rows fit, one more does not
+    assert lib.rsa_backward_workspace_bytes(1, 2, 1048576, 64, 64, BF16) == rsa.NOALLOC_SCRATCH_BYTES
+    assert call(B=1, H=3, L=1048576, N=64) == ESCRATCH
+    assert call(B=4, H=1, L=524288 + 64, N=64) == ESCRATCH
+    assert "static scratch" in rsa.status_string(ESCRATCH)
