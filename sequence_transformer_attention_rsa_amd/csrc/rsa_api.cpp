@@ -87,6 +87,34 @@ size_t layer_workspace(int B, int L, int E, int F) {
 
 namespace rsa {
 
+// ---- host-side sizing (no device code) ----
+
+size_t forward_partial_bytes(int B, int H, int Lq, int d, int groups) {
+    if (groups <= 1) return 0;
+    return (size_t)groups * B * H * Lq * (size_t)(d + 2) * sizeof(float);
+}
+
+int forward_rank_groups(int B, int H, int L, int d, int N) {
+    // Enough workgroups to cover the 256 CUs about twice, while keeping the
+    // partials small next to K and V: at most 8 groups, and each group's key
+    // range within the occupancy table.
+    const int Lc = L / N;
+    const long long qtiles = (long long)B * H * ((Lc + kFwdQueryTile - 1) / kFwdQueryTile);
+    int g = 1;
+    while (g < 8 && g < N && qtiles * g < 512) g *= 2;
+    g = g < N ? g : N;
+    while (((long long)((N + g - 1) / g) * Lc + kFwdKeyTile - 1) / kFwdKeyTile > kFwdMaxTiles && g < N) ++g;
+    (void)d;
+    return g;
+}
+
+size_t backward_workspace_bytes(int B, int H, int L, int d) {
+    (void)d;
+    return 2 * (size_t)B * H * L * sizeof(float);
+}
+
+size_t twopass_workspace_bytes(int B, int H, int L) { return (size_t)B * H * L * (size_t)L * sizeof(float); }
+
 int check_backward_call(const void* q, const void* k, const void* v, const void* out, const void* dout,
                         const float* lse, const uint8_t* key_mask, int B, int H, int L, int d, int N, int dtype,
                         int flags, const void* dq, const void* dk, const void* dv) {

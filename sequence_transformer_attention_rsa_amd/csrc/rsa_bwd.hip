@@ -659,11 +659,6 @@ hipError_t launch_t(const BackwardCall& c, int stages, hipStream_t stream) {
 
 }  // namespace
 
-size_t backward_workspace_bytes(int B, int H, int L, int d) {
-    (void)d;
-    return 2 * (size_t)B * H * L * sizeof(float);
-}
-
 hipError_t launch_backward(const BackwardCall& c, int stages, hipStream_t stream) {
     if (c.d == 64) return launch_t<64>(c, stages, stream);
     return launch_t<128>(c, stages, stream);

@@ -52,6 +52,7 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kKT = kFwdKeyTile;   // keys per tile
 constexpr int kQW = 32;            // query rows per wave
+static_assert(4 * kQW == kFwdQueryTile, "query rows per workgroup");
 // Initial running base (raw score units) of both kernels: finite and far
 // below any score, so that a row's first visible key forces a rescale (in the
 // bf16 kernel every valid weight formed against it overflows to +inf), padded
@@ -740,25 +741,6 @@ hipError_t launch_t(const ForwardCall& c, hipStream_t stream) {
 }
 
 }  // namespace
-
-size_t forward_partial_bytes(int B, int H, int Lq, int d, int groups) {
-    if (groups <= 1) return 0;
-    return (size_t)groups * B * H * Lq * (size_t)(d + 2) * sizeof(float);
-}
-
-int forward_rank_groups(int B, int H, int L, int d, int N) {
-    // Enough workgroups to cover the 256 CUs about twice, while keeping the
-    // partials small next to K and V: at most 8 groups, and each group's key
-    // range within the occupancy table.
-    const int Lc = L / N;
-    const long long qtiles = (long long)B * H * ((Lc + 4 * kQW - 1) / (4 * kQW));
-    int g = 1;
-    while (g < 8 && g < N && qtiles * g < 512) g *= 2;
-    g = g < N ? g : N;
-    while (((long long)((N + g - 1) / g) * Lc + kKT - 1) / kKT > kFwdMaxTiles && g < N) ++g;
-    (void)d;
-    return g;
-}
 
 hipError_t launch_forward(const ForwardCall& c, hipStream_t stream) {
     if (c.bf16) {

@@ -13,6 +13,8 @@ namespace rsa {
 // tile: 4 KB for 16384 tiles = 1048576 keys).
 constexpr int kFwdKeyTile = 64;
 constexpr int kFwdMaxTiles = 16384;
+// Query rows per forward workgroup (4 waves x 32 rows).
+constexpr int kFwdQueryTile = 128;
 
 struct ForwardCall {
     const void* q;          // [B,H,Lq,d]

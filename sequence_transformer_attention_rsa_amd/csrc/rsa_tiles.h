@@ -126,7 +126,9 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 
 // m0 is reserved to the compiler, which ignores it in a clobber list (and
 // warns); the kernels that issue these copies have no compiler-generated use
-// of m0, and none may be added to them (e.g. the builtin copy).
+// of m0, and none may be added to them (e.g. the builtin copy). The build
+// checks this on the device assembly of every kernel (build.py,
+// m0_violations) and fails if such a use appears.
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
 __device__ __forceinline__ void dma_copy16(const void* sbase, uint32_t voff, uint32_t lds) {

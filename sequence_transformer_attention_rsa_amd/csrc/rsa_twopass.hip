@@ -265,7 +265,6 @@ hipError_t launch_t(const ForwardCall& c, hipStream_t stream) {
 
 }  // namespace
 
-size_t twopass_workspace_bytes(int B, int H, int L) { return (size_t)B * H * L * (size_t)L * sizeof(float); }
 
 hipError_t launch_forward_twopass(const ForwardCall& c, hipStream_t stream) {
     if (c.d == 64) return launch_t<64>(c, stream);
