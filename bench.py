@@ -55,6 +55,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default="long_seq", choices=sorted(rsa_inputs.WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
+    ap.add_argument("--cpu-threads", type=int, default=0,
+                    help="oracle threads for the CPU baseline (default: OMP_NUM_THREADS if set, else every "
+                         "core of the process's affinity)")
     ap.add_argument("--forward-only", action="store_true", help="time the forward alone")
     ap.add_argument("--forward-variant", default="fused", choices=("fused", "twopass"),
                     help="fused online-softmax kernel, or the two-stage form with score rows in HBM "
@@ -123,31 +126,44 @@ def pair_count(w, x, causal):
     return float(sum(np.minimum(pos + 1, vl).sum() for vl in vls))
 
 
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.lower().startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(w, x, threads, causal=False):
-    """fp64 oracle, forward (+ backward) on `threads` heads of batch row 0
-    (full sequence length), timed once."""
+    """fp64 oracle, forward (+ backward) on the first `threads` heads of the
+    workload (batch row 0 first, then row 1, ...; full sequence length),
+    timed once. One head per thread keeps every thread busy in the backward,
+    which the oracle parallelises over heads (the forward over rows)."""
     import oracle
 
-    heads = max(1, min(threads, w.H))
-    sl = (slice(0, 1), slice(0, heads))
-    m = None if x["mask"] is None else x["mask"][0:1]
-    q, k, v = x["q"][sl], x["k"][sl], x["v"][sl]
-    vl = w.L if x["mask"] is None else int(x["valid_len"][0])
-    t0 = time.perf_counter()
+    heads = max(1, min(threads, w.B * w.H))
+    picks = [(b, h) for b in range(w.B) for h in range(w.H)][:heads]
     rows = np.arange(w.Lq) + (w.rank * w.Lc if w.rank is not None else 0)
-    pairs = float(np.minimum(rows + 1, vl).sum()) if causal else float(w.Lq * vl)
-    if w.rank is not None:
-        oracle.forward(q, k, v, m, N=w.N, qpos=rows, causal=causal)
-        flops = 4.0 * heads * pairs * w.d
-        what = "forward"
-    else:
-        oracle.forward(q, k, v, m, N=w.N, causal=causal)
-        flops = 4.0 * heads * pairs * w.d
-        what = "forward"
-        if x.get("dout") is not None:
-            g = x["dout"][sl]
-            oracle.backward(q, k, v, g, m, N=w.N, causal=causal)
-            flops += 8.0 * heads * pairs * w.d
+    flops = 0.0
+    what = "forward"
+    t0 = time.perf_counter()
+    for b in sorted({b for b, _ in picks}):
+        hs = [h for bb, h in picks if bb == b]
+        sl = (slice(b, b + 1), hs)
+        m = None if x["mask"] is None else x["mask"][b:b + 1]
+        q, k, v = (np.ascontiguousarray(x[n][sl]) for n in ("q", "k", "v"))
+        vl = w.L if x["mask"] is None else int(x["valid_len"][b])
+        pairs = float(np.minimum(rows + 1, vl).sum()) if causal else float(w.Lq * vl)
+        if w.rank is not None:
+            oracle.forward(q, k, v, m, N=w.N, qpos=rows, causal=causal)
+        else:
+            oracle.forward(q, k, v, m, N=w.N, causal=causal)
+        flops += 4.0 * len(hs) * pairs * w.d
+        if w.rank is None and x.get("dout") is not None:
+            oracle.backward(q, k, v, np.ascontiguousarray(x["dout"][sl]), m, N=w.N, causal=causal)
+            flops += 8.0 * len(hs) * pairs * w.d
             what = "forward+backward"
     if causal:
         what = "causal " + what
@@ -157,9 +173,11 @@ def cpu_baseline(w, x, threads, causal=False):
         "unit": "TFLOP/s",
         "cores": oracle.num_threads(),
         "kind": "oracle",
-        "sample": f"fp64 oracle {what} of {heads} head(s) of batch row 0 at full length "
+        "sample": f"fp64 oracle {what} of {heads} of the {w.B * w.H} heads at full length "
                   f"({w.name}: L={w.L}, d={w.d}, N={w.N}); {dt:.1f} s wall",
         "seconds": dt,
+        "cpu_model": cpu_model(),
+        "affinity_cores": len(os.sched_getaffinity(0)),
     }
 
 
@@ -554,9 +572,12 @@ def main():
         "gpu": torch.cuda.get_device_name(dev),
     }
     if not args.no_cpu_baseline:
-        threads = len(os.sched_getaffinity(0))
-        os.environ.setdefault("OMP_NUM_THREADS", str(min(threads, 16)))
-        line["cpu_baseline"] = cpu_baseline(w, x, int(os.environ["OMP_NUM_THREADS"]), causal)
+        # every core of the process's affinity, unless the environment
+        # (OMP_NUM_THREADS, which the GPU hosts set to their CPU share) or
+        # --cpu-threads says fewer
+        threads = args.cpu_threads or int(os.environ.get("OMP_NUM_THREADS", 0)) or len(os.sched_getaffinity(0))
+        os.environ["OMP_NUM_THREADS"] = str(threads)
+        line["cpu_baseline"] = cpu_baseline(w, x, threads, causal)
     else:
         line["cpu_baseline"] = None
     print(json.dumps(line), flush=True)

@@ -60,3 +60,20 @@ def test_more_than_one_gpu_is_refused():
                        text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+def test_cpu_baseline_reports_cores_model_and_work():
+    """The CPU baseline times the oracle on one head per thread across batch
+    rows and reports the threads used, the affinity and the CPU model."""
+    w = rsa_inputs.Workload("tiny", B=2, H=2, L=64, d=64, N=4, dtype="bf16", seed=4, valid_range=(40, 64),
+                            backward=True)
+    x = rsa_inputs.workload_inputs(w)
+    r = bench.cpu_baseline(w, x, threads=3)
+    assert r["kind"] == "oracle" and r["unit"] == "TFLOP/s" and r["value"] > 0
+    assert r["cores"] >= 1 and r["affinity_cores"] == len(os.sched_getaffinity(0))
+    assert isinstance(r["cpu_model"], str) and r["cpu_model"]
+    assert "3 of the 4 heads" in r["sample"] and "forward+backward" in r["sample"]
+    # the credited work: 12 d flops per visible pair, heads (0,0), (0,1) of row 0 and (1,0) of row 1
+    vl = [int(v) for v in x["valid_len"]]
+    flops = 12.0 * w.d * w.L * (2 * vl[0] + vl[1])
+    assert abs(r["value"] * 1e12 * r["seconds"] - flops) <= 1e-6 * flops
