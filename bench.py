@@ -146,25 +146,25 @@ def cpu_baseline(w, x, threads, causal=False):
     heads = max(1, min(threads, w.B * w.H))
     picks = [(b, h) for b in range(w.B) for h in range(w.H)][:heads]
     rows = np.arange(w.Lq) + (w.rank * w.Lc if w.rank is not None else 0)
-    flops = 0.0
+    # the sampled heads as a batch of single-head rows, each with its own
+    # batch row's key mask, so that one oracle call spreads them over threads
+    bs = [b for b, _ in picks]
+    q, k, v = (np.ascontiguousarray(np.stack([x[n][b, h] for b, h in picks])[:, None]) for n in ("q", "k", "v"))
+    m = None if x["mask"] is None else np.ascontiguousarray(x["mask"][bs])
+    vls = [w.L] * heads if x["mask"] is None else [int(x["valid_len"][b]) for b in bs]
+    pairs = sum(float(np.minimum(rows + 1, vl).sum()) if causal else float(w.Lq * vl) for vl in vls)
     what = "forward"
     t0 = time.perf_counter()
-    for b in sorted({b for b, _ in picks}):
-        hs = [h for bb, h in picks if bb == b]
-        sl = (slice(b, b + 1), hs)
-        m = None if x["mask"] is None else x["mask"][b:b + 1]
-        q, k, v = (np.ascontiguousarray(x[n][sl]) for n in ("q", "k", "v"))
-        vl = w.L if x["mask"] is None else int(x["valid_len"][b])
-        pairs = float(np.minimum(rows + 1, vl).sum()) if causal else float(w.Lq * vl)
-        if w.rank is not None:
-            oracle.forward(q, k, v, m, N=w.N, qpos=rows, causal=causal)
-        else:
-            oracle.forward(q, k, v, m, N=w.N, causal=causal)
-        flops += 4.0 * len(hs) * pairs * w.d
-        if w.rank is None and x.get("dout") is not None:
-            oracle.backward(q, k, v, np.ascontiguousarray(x["dout"][sl]), m, N=w.N, causal=causal)
-            flops += 8.0 * len(hs) * pairs * w.d
-            what = "forward+backward"
+    if w.rank is not None:
+        oracle.forward(q, k, v, m, N=w.N, qpos=rows, causal=causal)
+    else:
+        oracle.forward(q, k, v, m, N=w.N, causal=causal)
+    flops = 4.0 * pairs * w.d
+    if w.rank is None and x.get("dout") is not None:
+        g = np.ascontiguousarray(np.stack([x["dout"][b, h] for b, h in picks])[:, None])
+        oracle.backward(q, k, v, g, m, N=w.N, causal=causal)
+        flops += 8.0 * pairs * w.d
+        what = "forward+backward"
     if causal:
         what = "causal " + what
     dt = time.perf_counter() - t0

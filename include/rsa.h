@@ -152,7 +152,8 @@ size_t rsa_forward_twopass_workspace_bytes(int B, int H, int L, int d, int N);
  *   workspace          at least rsa_backward_workspace_bytes() (holds the
  *                      row statistics of stage 1 below)
  *   dq, dk, dv         [B,H,L,d] of dtype (outputs)
- * Only RSA_BF16 is supported (RSA_ERR_UNSUPPORTED for RSA_F32).
+ * RSA_BF16 (bf16 P and dS operands, fp32 accumulation) and RSA_F32 (every
+ * product and element in fp32).
  */
 int rsa_backward(const void* q, const void* k, const void* v, const void* out, const void* dout,
                  const float* lse, const uint8_t* key_mask,

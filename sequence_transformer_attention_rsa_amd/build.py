@@ -24,7 +24,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "librsa.so")
 
-SOURCES = ["rsa_fwd.hip", "rsa_twopass.hip", "rsa_bwd.hip", "rsa_layer.hip", "rsa_static.hip", "rsa_api.cpp"]
+SOURCES = ["rsa_fwd.hip", "rsa_twopass.hip", "rsa_bwd.hip", "rsa_bwd_f32.hip", "rsa_layer.hip", "rsa_static.hip",
+           "rsa_api.cpp"]
 ARCH = "gfx950"
 # Sources whose kernels issue HBM->LDS copies from inline assembly that sets
 # m0 (rsa_tiles.h: dma_copy16, dma_copy4). The compiler does not know the
@@ -129,7 +130,8 @@ def build(verbose: bool = False, extra=()) -> str:
         objs = list(ex.map(lambda s: _compile(s, extra), SOURCES))
         guard.result()
     tmp = LIB + ".tmp"
-    cmd = [hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp, *objs]
+    # every symbol resolved at link time: a kernel source missing from SOURCES fails here
+    cmd = [hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", "-Wl,--no-undefined", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"linking librsa.so failed:\n{r.stdout}\n{r.stderr}")

@@ -28,14 +28,15 @@ int launch_status(hipError_t e) { return e == hipSuccess ? RSA_OK : RSA_ERR_HIP;
 int check_backward(int B, int H, int L, int d, int N, int dtype) {
     int st = check_sizes(B, H, L, d, N, dtype);
     if (st != RSA_OK) return st;
-    if (dtype != RSA_BF16) return RSA_ERR_UNSUPPORTED;
     if (L > kMaxL) return RSA_ERR_UNSUPPORTED;
     return RSA_OK;
 }
 
 rsa::BackwardCall backward_call(const void* q, const void* k, const void* v, const void* out, const void* dout,
-                                const float* lse, const uint8_t* mask, int B, int H, int L, int d, int N) {
+                                const float* lse, const uint8_t* mask, int B, int H, int L, int d, int N,
+                                int dtype) {
     rsa::BackwardCall c{};
+    c.bf16 = dtype == RSA_BF16;
     c.q = q;
     c.k = k;
     c.v = v;
@@ -283,7 +284,7 @@ int rsa_backward_ex(const void* q, const void* k, const void* v, const void* out
     if (st != RSA_OK) return st;
     if (!aligned(workspace, 16)) return RSA_ERR_ALIGN;
     if (!workspace || workspace_bytes < rsa::backward_workspace_bytes(B, H, L, d)) return RSA_ERR_WORKSPACE;
-    rsa::BackwardCall c = backward_call(q, k, v, out, dout, lse, key_mask, B, H, L, d, N);
+    rsa::BackwardCall c = backward_call(q, k, v, out, dout, lse, key_mask, B, H, L, d, N, dtype);
     c.stats = static_cast<float*>(workspace);
     c.dq = dq;
     c.dk = dk;
@@ -298,7 +299,7 @@ int rsa_backward_preprocess(const void* out, const void* dout, const float* lse,
     int st = check_backward(B, H, L, d, 1, dtype);
     if (st != RSA_OK) return st;
     if (!aligned(out, 16) || !aligned(dout, 16) || !aligned(lse, 4) || !aligned(rowstats, 4)) return RSA_ERR_ALIGN;
-    rsa::BackwardCall c = backward_call(nullptr, nullptr, nullptr, out, dout, lse, nullptr, B, H, L, d, 1);
+    rsa::BackwardCall c = backward_call(nullptr, nullptr, nullptr, out, dout, lse, nullptr, B, H, L, d, 1, dtype);
     c.stats = rowstats;
     return launch_status(rsa::launch_backward(c, rsa::kBwdStagePre, static_cast<hipStream_t>(stream)));
 }
@@ -312,7 +313,7 @@ int rsa_backward_dq(const void* q, const void* k, const void* v, const void* dou
     if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(dout, 16) || !aligned(dq, 16) ||
         !aligned(key_mask, 16) || !aligned(rowstats, 4))
         return RSA_ERR_ALIGN;
-    rsa::BackwardCall c = backward_call(q, k, v, nullptr, dout, nullptr, key_mask, B, H, L, d, N);
+    rsa::BackwardCall c = backward_call(q, k, v, nullptr, dout, nullptr, key_mask, B, H, L, d, N, dtype);
     c.stats = const_cast<float*>(rowstats);
     c.dq = dq;
     return launch_status(rsa::launch_backward(c, rsa::kBwdStageDq, static_cast<hipStream_t>(stream)));
@@ -327,7 +328,7 @@ int rsa_backward_dkdv(const void* q, const void* k, const void* v, const void* d
     if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(dout, 16) || !aligned(dk, 16) ||
         !aligned(dv, 16) || !aligned(key_mask, 16) || !aligned(rowstats, 4))
         return RSA_ERR_ALIGN;
-    rsa::BackwardCall c = backward_call(q, k, v, nullptr, dout, nullptr, key_mask, B, H, L, d, N);
+    rsa::BackwardCall c = backward_call(q, k, v, nullptr, dout, nullptr, key_mask, B, H, L, d, N, dtype);
     c.stats = const_cast<float*>(rowstats);
     c.dk = dk;
     c.dv = dv;

@@ -660,6 +660,7 @@ hipError_t launch_t(const BackwardCall& c, int stages, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_backward(const BackwardCall& c, int stages, hipStream_t stream) {
+    if (!c.bf16) return launch_backward_f32(c, stages, stream);
     if (c.d == 64) return launch_t<64>(c, stages, stream);
     return launch_t<128>(c, stages, stream);
 }

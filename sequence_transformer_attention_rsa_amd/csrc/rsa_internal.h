@@ -61,6 +61,7 @@ struct BackwardCall {
     void* dk;
     void* dv;
     int B, H, L, d, N;
+    bool bf16;              // bf16 tensors; fp32 otherwise
     bool causal;
 };
 
@@ -80,6 +81,8 @@ constexpr int kBwdStageDkDv = 4;
 constexpr int kBwdStageAll = kBwdStagePre | kBwdStageDq | kBwdStageDkDv;
 
 hipError_t launch_backward(const BackwardCall& c, int stages, hipStream_t stream);
+// fp32 tensors (rsa_bwd_f32.hip); launch_backward dispatches to it.
+hipError_t launch_backward_f32(const BackwardCall& c, int stages, hipStream_t stream);
 
 // Token-local steps of the layer around the attention (rsa_layer.hip).
 // Matrix product out = act(a w^T + bias) + residual, bf16 operands, fp32

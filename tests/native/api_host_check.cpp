@@ -155,7 +155,10 @@ void backward_checks() {
     g_ws = {W, W + ws};
     CHECK(rsa_backward(cp(P), cp(P), cp(P), cp(P), cp(P), fp(P), nullptr, B, H, L, d, N, RSA_BF16, vp(W), ws,
                        nullptr, vp(P), vp(P), vp(P)) == RSA_OK);
-    CHECK(g_last_stages == rsa::kBwdStageAll && g_last_bwd.stats == fp(W));
+    CHECK(g_last_stages == rsa::kBwdStageAll && g_last_bwd.stats == fp(W) && g_last_bwd.bf16);
+    CHECK(rsa_backward(cp(P), cp(P), cp(P), cp(P), cp(P), fp(P), nullptr, B, H, L, d, N, RSA_F32, vp(W), ws,
+                       nullptr, vp(P), vp(P), vp(P)) == RSA_OK);
+    CHECK(!g_last_bwd.bf16);
     CHECK(rsa_backward(cp(P), cp(P), cp(P), cp(P), cp(P), fp(P), nullptr, B, H, L, d, N, RSA_BF16, vp(W), ws - 4,
                        nullptr, vp(P), vp(P), vp(P)) == RSA_ERR_WORKSPACE);
     CHECK(rsa_backward_ex(cp(P), cp(P), cp(P), cp(P), cp(P), fp(P), nullptr, B, H, L, d, N, RSA_BF16, 8, vp(W), ws,

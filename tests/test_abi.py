@@ -98,7 +98,8 @@ def test_backward_validation(lib):
     assert call(lse=None) == ENULL
     assert call(dq=None) == ENULL
     assert call(L_=4095) == ESHAPE
-    assert call(dtype=F32) == EUNSUP
+    assert call(dtype=7) == EUNSUP
+    assert call(dtype=F32, ws_ptr=None) == EWS      # fp32 is supported: it gets as far as the workspace
     assert call(ws_ptr=None) == EWS
     assert call(ws_bytes=ws - 4) == EWS
     assert call(dq=P + 2) == EALIGN
@@ -206,7 +207,7 @@ def test_flag_validation(lib):
     assert lib.rsa_forward_rank_ex(P, P, P, None, 1, 16, 32768, 128, 64, 64, BF16, 1, P, ws, None, P, None) == ESHAPE
     bws = lib.rsa_backward_workspace_bytes(1, 2, 256, 64, 4, BF16)
     assert lib.rsa_backward_ex(P, P, P, P, P, P, None, 1, 2, 256, 64, 4, BF16, 8, P, bws, None, P, P, P) == EUNSUP
-    assert lib.rsa_backward_ex(P, P, P, P, P, P, None, 1, 2, 256, 64, 4, F32, 1, P, bws, None, P, P, P) == EUNSUP
+    assert lib.rsa_backward_ex(P, P, P, P, P, P, None, 1, 2, 256, 64, 4, F32, 2, P, bws, None, P, P, P) == EUNSUP
     assert lib.rsa_backward_ex(P, P, P, P, P, P, None, 1, 2, 256, 64, 4, BF16, 1, None, bws, None, P, P, P) == EWS
 
 

@@ -173,3 +173,63 @@ def test_backward_longest_key_range():
     gsum = x["dout"].astype(np.float64).sum(axis=2)
     assert np.abs(dv.sum(axis=2) - gsum).max() <= 2e-2 * np.abs(gsum).max() + 0.05
     assert np.abs(dq).max() > 0
+
+
+# ------------------------------------------------------------- fp32 ---
+
+def gpu_fwd_bwd_f32(x, N, dev, causal=False):
+    q, k, v, g = (to_dev(x[n], "f32", dev) for n in ("q", "k", "v", "dout"))
+    m = mask_dev(x["mask"], dev)
+    out, lse = rsa.forward(q, k, v, m, N=N, return_lse=True, causal=causal)
+    dq, dk, dv = rsa.backward(q, k, v, out, g, lse, m, N=N, causal=causal)
+    torch.cuda.synchronize()
+    return from_dev(dq), from_dev(dk), from_dev(dv)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("L,N,valid,causal", [
+    (256, 4, None, False),          # the fp32 workload's shape
+    (256, 4, (150, 256), True),
+    (200, 5, (120, 200), False),    # chunks of 40: tiles straddle chunks, ragged tails
+    (130, 13, (60, 130), True),     # chunks of 10, one 128-row tile + 2 rows
+    (64, 64, None, False),          # one token per chunk
+    (32, 8, (24, 32), False),       # the finite-difference slice's shape
+])
+def test_backward_f32_parity(oracle_lib, d, L, N, valid, causal):
+    """fp32 in, fp32 out: dQ, dK, dV against the fp64 oracle at the fp32
+    gates (max-abs 1e-4, relative Frobenius 1e-5)."""
+    dev = device()
+    x = inputs(2, 2, L, d, seed=L * 3 + N + d + causal, dtype="f32", valid_range=valid, with_dout=True)
+    say("backward f32", d, L, N, valid, causal)
+    got = gpu_fwd_bwd_f32(x, N, dev, causal)
+    want = oracle_lib.backward(x["q"], x["k"], x["v"], x["dout"], x["mask"], N=N, causal=causal)
+    for name, a, b in zip(("dq", "dk", "dv"), got, want):
+        assert_parity(a, b, "f32", f"f32 {name} d={d} L={L} N={N}", grad=True)
+    if x["mask"] is not None:
+        for b, vl in enumerate(x["valid_len"]):
+            assert np.all(got[1][b, :, vl:] == 0) and np.all(got[2][b, :, vl:] == 0)
+
+
+def test_backward_f32_workload_and_stages(oracle_lib):
+    """The fp32 workload's shape (B=1 H=2 L=256 d=64 N=4) with an upstream
+    gradient: the one-call backward equals its three stages bit for bit,
+    does not depend on N, and meets the fp32 gates."""
+    w = rsa_inputs.WORKLOADS["fp32_small"]
+    dev = device()
+    x = rsa_inputs.make_inputs(w.B, w.H, w.L, w.d, w.seed, "f32", with_dout=True)
+    q, k, v, g = (to_dev(x[n], "f32", dev) for n in ("q", "k", "v", "dout"))
+    say("backward f32 workload")
+    out, lse = rsa.forward(q, k, v, None, N=w.N, return_lse=True)
+    full = rsa.backward(q, k, v, out, g, lse, None, N=w.N)
+    stats = rsa.backward_preprocess(out, g, lse)
+    dq = rsa.backward_dq(q, k, v, g, stats, None, N=w.N)
+    dk, dv = rsa.backward_dkdv(q, k, v, g, stats, None, N=w.N)
+    torch.cuda.synchronize()
+    for a, b in zip(full, (dq, dk, dv)):
+        assert torch.equal(a, b)
+    want = oracle_lib.backward(x["q"], x["k"], x["v"], x["dout"], None, N=w.N)
+    for name, a, b in zip(("dq", "dk", "dv"), full, want):
+        report(f"fp32_small backward {name}", assert_parity(from_dev(a), b, "f32", f"f32 {name}", grad=True))
+    for N in (1, 2, 16, 256):
+        for name, a, b in zip(("dq", "dk", "dv"), gpu_fwd_bwd_f32(x, N, dev), want):
+            assert_parity(a, b, "f32", f"f32 N={N} {name}", grad=True)
