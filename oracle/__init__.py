@@ -49,10 +49,18 @@ def _load():
         u8p = ctypes.POINTER(ctypes.c_uint8)
         i64p = ctypes.POINTER(ctypes.c_int64)
         ci = ctypes.c_int
-        lib.oracle_forward.argtypes = [dp, dp, dp, u8p, ci, ci, ci, ci, ci, ci, i64p, ci, dp, dp]
+        u64, u32 = ctypes.c_uint64, ctypes.c_uint32
+        lib.oracle_forward.argtypes = [dp, dp, dp, u8p, ci, ci, ci, ci, ci, ci, i64p, ci, ci, u64, u32, dp, dp]
         lib.oracle_forward.restype = ci
-        lib.oracle_backward.argtypes = [dp, dp, dp, dp, u8p, ci, ci, ci, ci, ci, ci, dp, dp, dp]
+        lib.oracle_backward.argtypes = [dp, dp, dp, dp, u8p, ci, ci, ci, ci, ci, ci, ci, u64, u32, dp, dp, dp]
         lib.oracle_backward.restype = ci
+        lib.oracle_philox4x32_10.argtypes = [ctypes.POINTER(u32), ctypes.POINTER(u32), ctypes.POINTER(u32)]
+        lib.oracle_philox4x32_10.restype = None
+        lib.oracle_philox4x64_10.argtypes = [ctypes.POINTER(u64), ctypes.POINTER(u64), ctypes.POINTER(u64)]
+        lib.oracle_philox4x64_10.restype = None
+        lib.oracle_dropout_keep.argtypes = [ci, u64, u32, ctypes.c_int64, ctypes.c_int64, ci, ctypes.c_int64, ci,
+                                            u8p]
+        lib.oracle_dropout_keep.restype = None
         lib.oracle_num_threads.argtypes = []
         lib.oracle_num_threads.restype = ci
         _lib = lib
@@ -74,13 +82,67 @@ def num_threads() -> int:
     return int(_load().oracle_num_threads())
 
 
-def forward(q, k, v, mask=None, N: int = 1, qpos=None, causal: bool = False) -> Tuple[np.ndarray, np.ndarray]:
+def dropout_p8(p: float) -> int:
+    """The dropout probability quantised to 1/256 steps: p is taken as fp32,
+    p8 = floor(256 p + 1/2), and the weights are dropped with probability
+    p8 / 256. p8 must lie in [0, 256)."""
+    p32 = float(np.float32(p))
+    p8 = int(np.floor(p32 * 256.0 + 0.5))
+    if not (0 <= p8 < 256):
+        raise ValueError(f"dropout probability {p} outside [0, 1 - 1/512)")
+    return p8
+
+
+def _dropout_args(dropout):
+    """(p8, seed, offset) from None or (p, seed[, offset])."""
+    if dropout is None:
+        return 0, 0, 0
+    p, seed = dropout[0], int(dropout[1])
+    offset = int(dropout[2]) if len(dropout) > 2 else 0
+    return dropout_p8(p), seed & (2 ** 64 - 1), offset & (2 ** 32 - 1)
+
+
+def philox4x32_10(counter, key) -> np.ndarray:
+    """Philox-4x32-10 of a 4-word counter and a 2-word key (uint32 words)."""
+    c = np.ascontiguousarray(counter, dtype=np.uint32)
+    k = np.ascontiguousarray(key, dtype=np.uint32)
+    out = np.empty(4, dtype=np.uint32)
+    u32p = ctypes.POINTER(ctypes.c_uint32)
+    _load().oracle_philox4x32_10(c.ctypes.data_as(u32p), k.ctypes.data_as(u32p), out.ctypes.data_as(u32p))
+    return out
+
+
+def philox4x64_10(counter, key) -> np.ndarray:
+    """Philox-4x64-10 of a 4-word counter and a 2-word key (uint64 words)."""
+    c = np.ascontiguousarray(counter, dtype=np.uint64)
+    k = np.ascontiguousarray(key, dtype=np.uint64)
+    out = np.empty(4, dtype=np.uint64)
+    u64p = ctypes.POINTER(ctypes.c_uint64)
+    _load().oracle_philox4x64_10(c.ctypes.data_as(u64p), k.ctypes.data_as(u64p), out.ctypes.data_as(u64p))
+    return out
+
+
+def dropout_keep(dropout, bh: int, i0: int, ni: int, j0: int, nj: int) -> np.ndarray:
+    """Keep decisions [ni, nj] (1 = kept) of the weights of query positions
+    i0.. and key positions j0.. of head bh = b * H + h; dropout = (p, seed[,
+    offset])."""
+    p8, seed, offset = _dropout_args(dropout)
+    out = np.empty((ni, nj), dtype=np.uint8)
+    _load().oracle_dropout_keep(p8, seed, offset, bh, i0, ni, j0, nj, _ptr(out, ctypes.c_uint8))
+    return out
+
+
+def forward(q, k, v, mask=None, N: int = 1, qpos=None, causal: bool = False,
+            dropout=None) -> Tuple[np.ndarray, np.ndarray]:
     """fp64 attention output and natural-log lse through RSA's ring stages.
 
     q: [B,H,Lq,d]; k, v: [B,H,L,d]; mask: [B,L] (nonzero = valid) or None;
     qpos: absolute positions of q's rows (default 0..Lq-1), which fix each
     row's rank and so its ring order; causal: the row at position i sees
-    keys j <= i only. Returns (out [B,H,Lq,d], lse [B,H,Lq]).
+    keys j <= i only; dropout: None or (p, seed[, offset]) -- the softmax
+    weights of head b*H + h are dropped as oracle.c's dropout_keep() decides
+    (the heads' indices come from q's [B,H] layout). Returns
+    (out [B,H,Lq,d], lse [B,H,Lq]).
     """
     q, k, v = _f64(q), _f64(k), _f64(v)
     B, H, Lq, d = q.shape
@@ -102,14 +164,16 @@ def forward(q, k, v, mask=None, N: int = 1, qpos=None, causal: bool = False) -> 
     st = _load().oracle_forward(_ptr(q, ctypes.c_double), _ptr(k, ctypes.c_double),
                                 _ptr(v, ctypes.c_double), _ptr(m, ctypes.c_uint8),
                                 B, H, L, d, N, Lq, _ptr(pos, ctypes.c_int64), int(bool(causal)),
-                                _ptr(out, ctypes.c_double), _ptr(lse, ctypes.c_double))
+                                *_dropout_args(dropout), _ptr(out, ctypes.c_double), _ptr(lse, ctypes.c_double))
     if st != 0:
         raise ValueError(f"oracle_forward failed with status {st}")
     return out, lse
 
 
-def backward(q, k, v, dout, mask=None, N: int = 1, causal: bool = False) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
-    """fp64 gradients (dQ, dK, dV) of <O, dO>, all [B,H,L,d] (causal as in forward)."""
+def backward(q, k, v, dout, mask=None, N: int = 1, causal: bool = False,
+             dropout=None) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """fp64 gradients (dQ, dK, dV) of <O, dO>, all [B,H,L,d] (causal and
+    dropout as in forward)."""
     q, k, v, g = _f64(q), _f64(k), _f64(v), _f64(dout)
     B, H, L, d = q.shape
     for name, a in (("k", k), ("v", v), ("dout", g)):
@@ -124,7 +188,7 @@ def backward(q, k, v, dout, mask=None, N: int = 1, causal: bool = False) -> Tupl
     st = _load().oracle_backward(_ptr(q, ctypes.c_double), _ptr(k, ctypes.c_double),
                                  _ptr(v, ctypes.c_double), _ptr(g, ctypes.c_double),
                                  _ptr(m, ctypes.c_uint8), B, H, L, d, N, int(bool(causal)),
-                                 _ptr(dq, ctypes.c_double), _ptr(dk, ctypes.c_double),
+                                 *_dropout_args(dropout), _ptr(dq, ctypes.c_double), _ptr(dk, ctypes.c_double),
                                  _ptr(dv, ctypes.c_double))
     if st != 0:
         raise ValueError(f"oracle_backward failed with status {st}")

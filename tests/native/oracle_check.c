@@ -4,8 +4,8 @@
  * (tests/test_host_sanitizers.py builds it). Cases: every ring size of a
  * short sequence, key padding with fully masked rows, chunks shorter than
  * one key, one rank's rows through qpos, the causal variant, and the
- * backward. Each result is checked for finiteness and for the two facts
- * that hold whatever the inputs: a row without a visible key gives zeros
+ * backward, each without and with dropout. Each result is checked for
+ * finiteness and for the two facts that hold whatever the inputs: a row without a visible key gives zeros
  * (lse -inf), and the forward does not depend on N.
  */
 #include <math.h>
@@ -14,9 +14,16 @@
 #include <stdlib.h>
 
 int oracle_forward(const double* q, const double* k, const double* v, const uint8_t* mask, int B, int H, int L,
-                   int d, int N, int Lq, const int64_t* qpos, int causal, double* out, double* lse);
+                   int d, int N, int Lq, const int64_t* qpos, int causal, int drop_p8, uint64_t drop_seed,
+                   uint32_t drop_offset, double* out, double* lse);
 int oracle_backward(const double* q, const double* k, const double* v, const double* dout, const uint8_t* mask,
-                    int B, int H, int L, int d, int N, int causal, double* dq, double* dk, double* dv);
+                    int B, int H, int L, int d, int N, int causal, int drop_p8, uint64_t drop_seed,
+                    uint32_t drop_offset, double* dq, double* dk, double* dv);
+
+/* the dropout settings every case runs with (p8 = 0: none) */
+static int P8 = 0;
+static const uint64_t SEED = 0x0123456789ABCDEFull;
+#define DROP P8, SEED, 7u
 
 static int failures = 0;
 #define CHECK(c) do { if (!(c)) { fprintf(stderr, "%s:%d: check failed: %s\n", __FILE__, __LINE__, #c); ++failures; } } while (0)
@@ -38,10 +45,10 @@ static void run_case(int B, int H, int L, int d, int causal, const uint8_t* mask
     double *q = fill(n), *k = fill(n), *v = fill(n), *g = fill(n);
     double *o1 = malloc(n * sizeof(double)), *oN = malloc(n * sizeof(double));
     double *l1 = malloc((size_t)B * H * L * sizeof(double)), *lN = malloc((size_t)B * H * L * sizeof(double));
-    CHECK(oracle_forward(q, k, v, mask, B, H, L, d, 1, L, NULL, causal, o1, l1) == 0);
+    CHECK(oracle_forward(q, k, v, mask, B, H, L, d, 1, L, NULL, causal, DROP, o1, l1) == 0);
     for (int N = 1; N <= L; ++N) {
         if (L % N) continue;
-        CHECK(oracle_forward(q, k, v, mask, B, H, L, d, N, L, NULL, causal, oN, lN) == 0);
+        CHECK(oracle_forward(q, k, v, mask, B, H, L, d, N, L, NULL, causal, DROP, oN, lN) == 0);
         for (size_t i = 0; i < n; ++i) CHECK(isfinite(oN[i]) && fabs(oN[i] - o1[i]) < 1e-12);
         for (size_t r = 0; r < (size_t)B * H * L; ++r) {
             CHECK(lN[r] == l1[r] || fabs(lN[r] - l1[r]) < 1e-12);
@@ -57,18 +64,18 @@ static void run_case(int B, int H, int L, int d, int causal, const uint8_t* mask
             for (int i = 0; i < Lc; ++i)
                 for (int x = 0; x < d; ++x)
                     ql[((size_t)bh * Lc + i) * d + x] = q[((size_t)bh * L + pos[i]) * d + x];
-        CHECK(oracle_forward(ql, k, v, mask, B, H, L, d, N, Lc, pos, causal, ol, NULL) == 0);
+        CHECK(oracle_forward(ql, k, v, mask, B, H, L, d, N, Lc, pos, causal, DROP, ol, NULL) == 0);
         for (int bh = 0; bh < B * H; ++bh)
             for (int i = 0; i < Lc; ++i)
                 for (int x = 0; x < d; ++x)
                     CHECK(fabs(ol[((size_t)bh * Lc + i) * d + x] - o1[((size_t)bh * L + pos[i]) * d + x]) < 1e-12);
         free(ql); free(ol); free(pos);
         double *dq = malloc(n * sizeof(double)), *dk = malloc(n * sizeof(double)), *dv = malloc(n * sizeof(double));
-        CHECK(oracle_backward(q, k, v, g, mask, B, H, L, d, N, causal, dq, dk, dv) == 0);
+        CHECK(oracle_backward(q, k, v, g, mask, B, H, L, d, N, causal, DROP, dq, dk, dv) == 0);
         for (size_t i = 0; i < n; ++i) CHECK(isfinite(dq[i]) && isfinite(dk[i]) && isfinite(dv[i]));
         free(dq); free(dk); free(dv);
     }
-    CHECK(oracle_forward(q, k, v, mask, B, H, L, d, 3, L, NULL, causal, oN, lN) == (L % 3 ? 2 : 0));
+    CHECK(oracle_forward(q, k, v, mask, B, H, L, d, 3, L, NULL, causal, DROP, oN, lN) == (L % 3 ? 2 : 0));
     free(q); free(k); free(v); free(g); free(o1); free(oN); free(l1); free(lN);
 }
 
@@ -84,6 +91,10 @@ int main(void) {
     run_case(2, 1, 12, 5, 1, mask);
     run_case(2, 1, 12, 2, 0, none);          /* every row without a key */
     run_case(1, 1, 1, 1, 1, NULL);
+    P8 = 77;   /* the same cases with dropout */
+    run_case(1, 2, 12, 4, 0, NULL);
+    run_case(2, 2, 12, 3, 1, mask);
+    run_case(2, 1, 12, 2, 0, none);
     if (failures) {
         fprintf(stderr, "%d oracle check(s) failed\n", failures);
         return 1;
