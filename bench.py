@@ -64,6 +64,9 @@ def parse():
                          "(implies --forward-only)")
     ap.add_argument("--causal", action="store_true",
                     help="the causal variant (row i sees keys j <= i); the backward is timed as one call")
+    ap.add_argument("--dropout", type=float, default=0.0,
+                    help="dropout probability of the softmax weights (Philox-4x32-10 keep decisions, seed 1234); "
+                         "the backward is timed as one call")
     ap.add_argument("--capacity", action="store_true",
                     help="single-GPU sequence-length capacity of the fused and the two-stage forward "
                          "(B=H=1, d=64) instead of the step benchmark")
@@ -136,7 +139,7 @@ def cpu_model() -> str:
     return "unknown"
 
 
-def cpu_baseline(w, x, threads, causal=False):
+def cpu_baseline(w, x, threads, causal=False, dropout=None):
     """fp64 oracle, forward (+ backward) on the first `threads` heads of the
     workload (batch row 0 first, then row 1, ...; full sequence length),
     timed once. One head per thread keeps every thread busy in the backward,
@@ -156,17 +159,19 @@ def cpu_baseline(w, x, threads, causal=False):
     what = "forward"
     t0 = time.perf_counter()
     if w.rank is not None:
-        oracle.forward(q, k, v, m, N=w.N, qpos=rows, causal=causal)
+        oracle.forward(q, k, v, m, N=w.N, qpos=rows, causal=causal, dropout=dropout)
     else:
-        oracle.forward(q, k, v, m, N=w.N, causal=causal)
+        oracle.forward(q, k, v, m, N=w.N, causal=causal, dropout=dropout)
     flops = 4.0 * pairs * w.d
     if w.rank is None and x.get("dout") is not None:
         g = np.ascontiguousarray(np.stack([x["dout"][b, h] for b, h in picks])[:, None])
-        oracle.backward(q, k, v, g, m, N=w.N, causal=causal)
+        oracle.backward(q, k, v, g, m, N=w.N, causal=causal, dropout=dropout)
         flops += 8.0 * pairs * w.d
         what = "forward+backward"
     if causal:
         what = "causal " + what
+    if dropout is not None:
+        what += f" with dropout {dropout[0]}"
     dt = time.perf_counter() - t0
     return {
         "value": flops / dt / 1e12,
@@ -389,8 +394,10 @@ def main():
         return 2
     twopass = args.forward_variant == "twopass"
     causal = args.causal
-    if twopass and (w.rank is not None or w.dtype != "bf16" or causal):
-        print("the two-stage forward covers full-sequence, non-causal bf16 workloads", file=sys.stderr)
+    dropout = (args.dropout, 1234, 0) if args.dropout > 0 else None
+    if twopass and (w.rank is not None or w.dtype != "bf16" or causal or dropout):
+        print("the two-stage forward covers full-sequence, non-causal bf16 workloads without dropout",
+              file=sys.stderr)
         return 2
     dev = torch.device("cuda:0")
     with_dout = w.rank is None
@@ -417,10 +424,11 @@ def main():
         ws = torch.empty(rsa.forward_twopass_workspace_bytes(w.B, w.H, w.L, w.d, w.N), dtype=torch.uint8,
                          device=dev)
     bws = None
-    if do_bwd and causal:
+    one_call_bwd = causal or dropout is not None   # the backward's stages have no causal or dropout form
+    if do_bwd and one_call_bwd:
         bws = torch.empty(rsa.backward_workspace_bytes(w.B, w.H, w.L, w.d, w.N), dtype=torch.uint8, device=dev)
 
-    if causal:
+    if one_call_bwd:
         names = ["forward"] + (["backward"] if do_bwd else [])
     else:
         names = ["forward"] + (["bwd_preprocess", "bwd_dq", "bwd_dkdv"] if do_bwd else [])
@@ -433,12 +441,14 @@ def main():
         if twopass:
             rsa.forward_twopass(q, k, v, mask, N=w.N, out=out, lse=lse, workspace=ws)
         elif w.rank is not None:
-            rsa.forward_rank(q, k, v, mask, N=w.N, rank=w.rank, out=out, lse=lse, workspace=ws, causal=causal)
+            rsa.forward_rank(q, k, v, mask, N=w.N, rank=w.rank, out=out, lse=lse, workspace=ws, causal=causal,
+                             dropout=dropout)
         else:
-            rsa.forward(q, k, v, mask, N=w.N, out=out, lse=lse, causal=causal)
+            rsa.forward(q, k, v, mask, N=w.N, out=out, lse=lse, causal=causal, dropout=dropout)
         mark(1)
-        if do_bwd and causal:
-            rsa.backward(q, k, v, out, g, lse, mask, N=w.N, dq=dq, dk=dk, dv=dv, workspace=bws, causal=True)
+        if do_bwd and one_call_bwd:
+            rsa.backward(q, k, v, out, g, lse, mask, N=w.N, dq=dq, dk=dk, dv=dv, workspace=bws, causal=causal,
+                         dropout=dropout)
             mark(2)
         elif do_bwd:
             rsa.backward_preprocess(out, g, lse, rowstats=stats)
@@ -536,7 +546,7 @@ def main():
             "peak": peak,
             "unit": "TFLOP/s",
             "frac": achieved / peak,
-            "traffic": None if causal else recorded_traffic(w.name, dominant),
+            "traffic": None if one_call_bwd else recorded_traffic(w.name, dominant),
             "traffic_unit": "bytes per launch (calibrated FETCH_SIZE + WRITE_SIZE)",
             "avg_ms": per_kernel[dominant]["avg_ms"],
             "flops_per_launch": credited[dominant],
@@ -559,6 +569,7 @@ def main():
         "config": {"workload": w.name, "B": w.B, "H": w.H, "L": w.L, "d": w.d, "N": w.N,
                    "rank": w.rank, "key_mask": w.valid_range is not None,
                    "pass": "fwd+bwd" if do_bwd else "fwd", "forward": args.forward_variant, "causal": causal,
+                   "dropout": args.dropout,
                    "description": w.description},
         "fwd_tflops": fwd_flops / fwd_s / 1e12,
         "fwd_tflops_nominal_keys": fwd_flops_nominal / fwd_s / 1e12,
@@ -577,7 +588,7 @@ def main():
         # --cpu-threads says fewer
         threads = args.cpu_threads or int(os.environ.get("OMP_NUM_THREADS", 0)) or len(os.sched_getaffinity(0))
         os.environ["OMP_NUM_THREADS"] = str(threads)
-        line["cpu_baseline"] = cpu_baseline(w, x, threads, causal)
+        line["cpu_baseline"] = cpu_baseline(w, x, threads, causal, dropout)
     else:
         line["cpu_baseline"] = None
     print(json.dumps(line), flush=True)

@@ -173,6 +173,49 @@ int rsa_backward_ex(const void* q, const void* k, const void* v, const void* out
 size_t rsa_backward_workspace_bytes(int B, int H, int L, int d, int N, int dtype);
 
 /*
+ * ---- Dropout of the attention weights ---------------------------------------
+ * The pages do not describe dropout; these entry points add the usual
+ * attention dropout to the plain ones. P = softmax(Q K^T / sqrt(d) + M) over
+ * the full key length is formed as before (lse unchanged); each weight is
+ * then kept with probability 1 - p and scaled by 1 / (1 - p), or dropped:
+ * O = (P o Z) V. p is quantised to p8 / 256 with p8 = floor(256 p + 1/2),
+ * p8 in [0, 255] (p8 = 0: no dropout; larger p: RSA_ERR_UNSUPPORTED). The
+ * keep decision of the weight of query position i and key position j in head
+ * b*H + h is byte (j mod 4) of word ((j/8) mod 4) of Philox-4x32-10 (Salmon,
+ * Moraes, Dror and Shaw, "Parallel Random Numbers: As Easy as 1, 2, 3",
+ * SC'11) at counter ((j/32)*2 + bit 2 of j, i, b*H + h, offset) and key
+ * (seed low 32 bits, seed high 32 bits); kept iff that byte >= p8. The
+ * decision depends on positions only, so the result does not depend on N,
+ * a rank's share sees the same decisions as the full forward, and the
+ * backward, given the same settings, regenerates them.
+ */
+typedef struct rsa_dropout {
+    float p;           /* drop probability */
+    uint32_t offset;   /* fourth counter word (e.g. a step number) */
+    uint64_t seed;     /* Philox key */
+} rsa_dropout;
+
+/* rsa_forward_ex with dropout (dropout NULL or p8 = 0: the plain forward). */
+int rsa_forward_dropout(const void* q, const void* k, const void* v, const uint8_t* key_mask,
+                        int B, int H, int L, int d, int N, int dtype, int flags, const rsa_dropout* dropout,
+                        void* stream, void* out, float* lse);
+
+/* rsa_forward_rank_ex with dropout (query positions rank * L/N + row). */
+int rsa_forward_rank_dropout(const void* q_local, const void* k, const void* v, const uint8_t* key_mask,
+                             int B, int H, int L, int d, int N, int rank, int dtype, int flags,
+                             const rsa_dropout* dropout, void* workspace, size_t workspace_bytes,
+                             void* stream, void* out_local, float* lse_local);
+
+/* rsa_backward_ex with dropout: out and lse come from rsa_forward_dropout
+ * with the same flags and dropout settings; dV = (P o Z)^T dO,
+ * dP = Z o (dO V^T), dS = P o (dP - D) with D = rowsum(dO o out). */
+int rsa_backward_dropout(const void* q, const void* k, const void* v, const void* out, const void* dout,
+                         const float* lse, const uint8_t* key_mask,
+                         int B, int H, int L, int d, int N, int dtype, int flags, const rsa_dropout* dropout,
+                         void* workspace, size_t workspace_bytes,
+                         void* stream, void* dq, void* dk, void* dv);
+
+/*
  * rsa_backward_ex for callers that cannot allocate device memory where they
  * call it: code under HIP graph capture, serving loops that must not
  * allocate, harnesses that forbid hipMalloc. Same arguments, results and

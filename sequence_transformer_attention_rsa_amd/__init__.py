@@ -66,6 +66,11 @@ SIGNATURES = {
     "rsa_backward_workspace_bytes": (_sz, [_ci, _ci, _ci, _ci, _ci, _ci]),
     "rsa_backward_noalloc": (_ci, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _ci, _ci, _ci, _ci, _ci, _ci, _ci,
                                    _vp, _vp, _vp, _vp]),
+    "rsa_forward_dropout": (_ci, [_vp, _vp, _vp, _vp, _ci, _ci, _ci, _ci, _ci, _ci, _ci, _vp, _vp, _vp, _vp]),
+    "rsa_forward_rank_dropout": (_ci, [_vp, _vp, _vp, _vp, _ci, _ci, _ci, _ci, _ci, _ci, _ci, _ci, _vp, _vp, _sz,
+                                       _vp, _vp, _vp]),
+    "rsa_backward_dropout": (_ci, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _ci, _ci, _ci, _ci, _ci, _ci, _ci, _vp,
+                                   _vp, _sz, _vp, _vp, _vp, _vp]),
     "rsa_backward_preprocess": (_ci, [_vp, _vp, _vp, _ci, _ci, _ci, _ci, _ci, _vp, _vp]),
     "rsa_backward_dq": (_ci, [_vp, _vp, _vp, _vp, _vp, _vp, _ci, _ci, _ci, _ci, _ci, _ci, _vp, _vp]),
     "rsa_backward_dkdv": (_ci, [_vp, _vp, _vp, _vp, _vp, _vp, _ci, _ci, _ci, _ci, _ci, _ci, _vp, _vp, _vp]),
@@ -85,6 +90,24 @@ LAYER_WEIGHTS = ("w_qkv", "b_qkv", "w_o", "b_o", "ln1_gamma", "ln1_beta",
 
 class _LayerWeights(ctypes.Structure):
     _fields_ = [(name, ctypes.c_void_p) for name in LAYER_WEIGHTS]
+
+
+class _Dropout(ctypes.Structure):
+    """struct rsa_dropout: drop probability, fourth counter word, Philox key."""
+    _fields_ = [("p", ctypes.c_float), ("offset", ctypes.c_uint32), ("seed", ctypes.c_uint64)]
+
+
+def _dropout(dropout):
+    """None, or (p, seed[, offset]) -> a struct rsa_dropout (kept alive by the caller)."""
+    if dropout is None:
+        return None
+    p, seed = float(dropout[0]), int(dropout[1])
+    offset = int(dropout[2]) if len(dropout) > 2 else 0
+    return _Dropout(p, offset & 0xFFFFFFFF, seed & 0xFFFFFFFFFFFFFFFF)
+
+
+def _ref(s):
+    return None if s is None else ctypes.byref(s)
 
 
 class RSAError(RuntimeError):
@@ -156,9 +179,10 @@ def _mask(key_mask, B, L, device):
 
 
 def forward(q, k, v, key_mask=None, N: int = 1, return_lse: bool = False, out=None, lse=None,
-            causal: bool = False):
+            causal: bool = False, dropout=None):
     """RSA forward over all N ranks: softmax(q k^T / sqrt(d) + mask) v
-    (causal: the row at position i sees keys j <= i only)."""
+    (causal: the row at position i sees keys j <= i only; dropout: None or
+    (p, seed[, offset]), dropout of the softmax weights, see rsa.h)."""
     B, H, L, d = q.shape
     dev = q.device
     _need(q, "q", (B, H, L, d), q.dtype, dev)
@@ -173,7 +197,11 @@ def forward(q, k, v, key_mask=None, N: int = 1, return_lse: bool = False, out=No
         lse = torch.empty((B, H, L), dtype=torch.float32, device=dev)
     if lse is not None:
         _need(lse, "lse", (B, H, L), torch.float32, dev)
-    if causal:
+    if dropout is not None:
+        dr = _dropout(dropout)
+        st = load().rsa_forward_dropout(_ptr(q), _ptr(k), _ptr(v), _ptr(m), B, H, L, d, int(N), code,
+                                        RSA_CAUSAL if causal else 0, _ref(dr), _stream(dev), _ptr(out), _ptr(lse))
+    elif causal:
         st = load().rsa_forward_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(m), B, H, L, d, int(N), code, RSA_CAUSAL,
                                    _stream(dev), _ptr(out), _ptr(lse))
     else:
@@ -189,7 +217,7 @@ def forward_rank_workspace_bytes(B: int, H: int, L: int, d: int, N: int) -> int:
 
 
 def forward_rank(q_local, k, v, key_mask=None, N: int = 1, rank: int = 0, return_lse: bool = False,
-                 out=None, lse=None, workspace=None, causal: bool = False):
+                 out=None, lse=None, workspace=None, causal: bool = False, dropout=None):
     """One rank's share: q_local [B,H,L/N,d] against all L keys in that rank's ring order."""
     B, H, L, d = k.shape
     dev = k.device
@@ -210,7 +238,13 @@ def forward_rank(q_local, k, v, key_mask=None, N: int = 1, rank: int = 0, return
     need = forward_rank_workspace_bytes(B, H, L, d, N)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
-    if causal:
+    if dropout is not None:
+        dr = _dropout(dropout)
+        st = load().rsa_forward_rank_dropout(_ptr(q_local), _ptr(k), _ptr(v), _ptr(m), B, H, L, d, int(N), int(rank),
+                                             code, RSA_CAUSAL if causal else 0, _ref(dr), _ptr(workspace),
+                                             workspace.numel() * workspace.element_size(), _stream(dev), _ptr(out),
+                                             _ptr(lse))
+    elif causal:
         st = load().rsa_forward_rank_ex(_ptr(q_local), _ptr(k), _ptr(v), _ptr(m), B, H, L, d, int(N), int(rank),
                                         code, RSA_CAUSAL, _ptr(workspace),
                                         workspace.numel() * workspace.element_size(), _stream(dev), _ptr(out),
@@ -315,9 +349,9 @@ def backward_dkdv(q, k, v, dout, rowstats, key_mask=None, N: int = 1, dk=None, d
 
 
 def backward(q, k, v, out, dout, lse, key_mask=None, N: int = 1, dq=None, dk=None, dv=None, workspace=None,
-             causal: bool = False):
+             causal: bool = False, dropout=None):
     """Gradients (dq, dk, dv) of <out, dout>; out and lse come from forward()
-    with the same causal setting."""
+    with the same causal and dropout settings."""
     B, H, L, d = q.shape
     dev = q.device
     for name, t in (("q", q), ("k", k), ("v", v), ("out", out), ("dout", dout)):
@@ -333,7 +367,13 @@ def backward(q, k, v, out, dout, lse, key_mask=None, N: int = 1, dq=None, dk=Non
     need = backward_workspace_bytes(B, H, L, d, N, code)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
-    if causal:
+    if dropout is not None:
+        dr = _dropout(dropout)
+        st = load().rsa_backward_dropout(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(lse), _ptr(m),
+                                         B, H, L, d, int(N), code, RSA_CAUSAL if causal else 0, _ref(dr),
+                                         _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                         _stream(dev), _ptr(dq), _ptr(dk), _ptr(dv))
+    elif causal:
         st = load().rsa_backward_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(lse), _ptr(m),
                                     B, H, L, d, int(N), code, RSA_CAUSAL, _ptr(workspace),
                                     workspace.numel() * workspace.element_size(), _stream(dev),

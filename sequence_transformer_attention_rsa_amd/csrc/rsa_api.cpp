@@ -13,6 +13,14 @@ constexpr int kMaxL = rsa::kFwdKeyTile * rsa::kFwdMaxTiles;   // longest key ran
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
+// NaN and infinities are recognised by their bits: the library is compiled
+// assuming arithmetic never meets a NaN, so a comparison would not reject one.
+bool finite_float(float x) {
+    uint32_t bits;
+    __builtin_memcpy(&bits, &x, sizeof(bits));
+    return (bits & 0x7f800000u) != 0x7f800000u;
+}
+
 int check_sizes(int B, int H, int L, int d, int N, int dtype) {
     if (B <= 0 || H <= 0 || L <= 0 || d <= 0 || N <= 0 || L % N != 0) return RSA_ERR_SHAPE;
     if (d != 64 && d != 128) return RSA_ERR_UNSUPPORTED;
@@ -24,6 +32,26 @@ int check_sizes(int B, int H, int L, int d, int N, int dtype) {
 }
 
 int launch_status(hipError_t e) { return e == hipSuccess ? RSA_OK : RSA_ERR_HIP; }
+
+// The dropout probability quantised to p8 / 256, p8 = floor(256 p + 1/2);
+// false if p is not a number or p8 falls outside [0, 255].
+bool dropout_p8(const rsa_dropout* dr, uint32_t* p8) {
+    *p8 = 0;
+    if (dr == nullptr) return true;
+    const float p = dr->p;
+    if (!finite_float(p) || !(p >= 0.0f && p < 1.0f)) return false;
+    const float q = __builtin_floorf(p * 256.0f + 0.5f);   // exact: p * 256 and the sum are representable
+    if (q > 255.0f) return false;
+    *p8 = (uint32_t)q;
+    return true;
+}
+
+template <class Call>
+void set_dropout(Call& c, const rsa_dropout* dr, uint32_t p8) {
+    c.drop_p8 = p8;
+    c.drop_seed = p8 != 0 ? dr->seed : 0;
+    c.drop_offset = p8 != 0 ? dr->offset : 0;
+}
 
 int check_backward(int B, int H, int L, int d, int N, int dtype) {
     int st = check_sizes(B, H, L, d, N, dtype);
@@ -75,7 +103,7 @@ int check_heads(int B, int L, int E, int H) {
 
 int check_layernorm(int rows, int E, float eps) {
     if (rows <= 0 || E <= 0) return RSA_ERR_SHAPE;
-    if (E % 8 != 0 || E > 4096 || !(eps >= 0.0f)) return RSA_ERR_UNSUPPORTED;
+    if (E % 8 != 0 || E > 4096 || !finite_float(eps) || !(eps >= 0.0f)) return RSA_ERR_UNSUPPORTED;
     return RSA_OK;
 }
 
@@ -142,7 +170,15 @@ int rsa_forward(const void* q, const void* k, const void* v, const uint8_t* key_
 int rsa_forward_ex(const void* q, const void* k, const void* v, const uint8_t* key_mask,
                    int B, int H, int L, int d, int N, int dtype, int flags,
                    void* stream, void* out, float* lse) {
+    return rsa_forward_dropout(q, k, v, key_mask, B, H, L, d, N, dtype, flags, nullptr, stream, out, lse);
+}
+
+int rsa_forward_dropout(const void* q, const void* k, const void* v, const uint8_t* key_mask,
+                        int B, int H, int L, int d, int N, int dtype, int flags, const rsa_dropout* dropout,
+                        void* stream, void* out, float* lse) {
     if (!q || !k || !v || !out) return RSA_ERR_NULL;
+    uint32_t p8 = 0;
+    if (!dropout_p8(dropout, &p8)) return RSA_ERR_UNSUPPORTED;
     int st = check_sizes(B, H, L, d, N, dtype);
     if (st != RSA_OK) return st;
     if (flags & ~RSA_CAUSAL) return RSA_ERR_UNSUPPORTED;
@@ -168,6 +204,7 @@ int rsa_forward_ex(const void* q, const void* k, const void* v, const uint8_t* k
     c.groups = 1;
     c.bf16 = dtype == RSA_BF16;
     c.causal = (flags & RSA_CAUSAL) != 0;
+    set_dropout(c, dropout, p8);
     return launch_status(rsa::launch_forward(c, static_cast<hipStream_t>(stream)));
 }
 
@@ -190,7 +227,17 @@ int rsa_forward_rank_ex(const void* q_local, const void* k, const void* v, const
                         int B, int H, int L, int d, int N, int rank, int dtype, int flags,
                         void* workspace, size_t workspace_bytes,
                         void* stream, void* out_local, float* lse_local) {
+    return rsa_forward_rank_dropout(q_local, k, v, key_mask, B, H, L, d, N, rank, dtype, flags, nullptr, workspace,
+                                    workspace_bytes, stream, out_local, lse_local);
+}
+
+int rsa_forward_rank_dropout(const void* q_local, const void* k, const void* v, const uint8_t* key_mask,
+                             int B, int H, int L, int d, int N, int rank, int dtype, int flags,
+                             const rsa_dropout* dropout, void* workspace, size_t workspace_bytes,
+                             void* stream, void* out_local, float* lse_local) {
     if (!q_local || !k || !v || !out_local) return RSA_ERR_NULL;
+    uint32_t p8 = 0;
+    if (!dropout_p8(dropout, &p8)) return RSA_ERR_UNSUPPORTED;
     int st = check_sizes(B, H, L, d, N, dtype);
     if (st != RSA_OK) return st;
     if (flags & ~RSA_CAUSAL) return RSA_ERR_UNSUPPORTED;
@@ -221,6 +268,7 @@ int rsa_forward_rank_ex(const void* q_local, const void* k, const void* v, const
     c.groups = g;
     c.bf16 = dtype == RSA_BF16;
     c.causal = (flags & RSA_CAUSAL) != 0;
+    set_dropout(c, dropout, p8);
     return launch_status(rsa::launch_forward(c, static_cast<hipStream_t>(stream)));
 }
 
@@ -280,8 +328,19 @@ int rsa_backward_ex(const void* q, const void* k, const void* v, const void* out
                     int B, int H, int L, int d, int N, int dtype, int flags,
                     void* workspace, size_t workspace_bytes,
                     void* stream, void* dq, void* dk, void* dv) {
+    return rsa_backward_dropout(q, k, v, out, dout, lse, key_mask, B, H, L, d, N, dtype, flags, nullptr, workspace,
+                                workspace_bytes, stream, dq, dk, dv);
+}
+
+int rsa_backward_dropout(const void* q, const void* k, const void* v, const void* out, const void* dout,
+                         const float* lse, const uint8_t* key_mask,
+                         int B, int H, int L, int d, int N, int dtype, int flags, const rsa_dropout* dropout,
+                         void* workspace, size_t workspace_bytes,
+                         void* stream, void* dq, void* dk, void* dv) {
     int st = rsa::check_backward_call(q, k, v, out, dout, lse, key_mask, B, H, L, d, N, dtype, flags, dq, dk, dv);
     if (st != RSA_OK) return st;
+    uint32_t p8 = 0;
+    if (!dropout_p8(dropout, &p8)) return RSA_ERR_UNSUPPORTED;
     if (!aligned(workspace, 16)) return RSA_ERR_ALIGN;
     if (!workspace || workspace_bytes < rsa::backward_workspace_bytes(B, H, L, d)) return RSA_ERR_WORKSPACE;
     rsa::BackwardCall c = backward_call(q, k, v, out, dout, lse, key_mask, B, H, L, d, N, dtype);
@@ -290,6 +349,7 @@ int rsa_backward_ex(const void* q, const void* k, const void* v, const void* out
     c.dk = dk;
     c.dv = dv;
     c.causal = (flags & RSA_CAUSAL) != 0;
+    set_dropout(c, dropout, p8);
     return launch_status(rsa::launch_backward(c, rsa::kBwdStageAll, static_cast<hipStream_t>(stream)));
 }
 

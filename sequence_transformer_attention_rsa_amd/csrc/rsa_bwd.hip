@@ -54,6 +54,7 @@ struct BwdParams {
     float sl2;                 // log2(e) / sqrt(d)
     float scale;               // 1 / sqrt(d)
     int causal;                // the query at position i sees keys at positions <= i only
+    Dropout drop;              // the forward's dropout (drop.p8 == 0: none)
 };
 
 // Sequence position of the u-th query row that key chunk c meets: ring step
@@ -107,7 +108,10 @@ __device__ __forceinline__ void load_rowvec(uint8_t* lds, const float* src, RowO
 // Query-stationary, mirror of the forward: 4 waves x 32 query rows; per key
 // tile S^T = K Q^T and dP^T = V dO^T (lane <-> query), then
 // dQ^T += K^T dS^T with K^T from the transposing read of the same K tile.
-template <int D, bool CONTIG, bool CAUSAL>
+// DROP: with dropout, dS = P o (Z o dP - D) for the forward's keep factors Z
+// (kept: 1 / (1 - p), dropped: 0); the dP accumulator then starts at
+// -D (1 - p), so that a kept weight takes acc / (1 - p) and a dropped one -D.
+template <int D, bool CONTIG, bool CAUSAL, bool DROP = false>
 __global__ __launch_bounds__(kThreads, D == 64 ? 3 : 1) void rsa_bwd_dq(BwdParams p) {
     using T = DirectTile<D>;
     constexpr int BUF = 2 * T::BYTES;   // K, V
@@ -156,6 +160,7 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 3 : 1) void rsa_bwd_dq(BwdParam
     // tail rows get P = 0 through nl2 = -inf
     const float nD = row_ok ? p.stats[(size_t)bh * p.L + row] : 0.0f;
     const float nl2 = row_ok ? p.stats[rows_all + (size_t)bh * p.L + row] : -INFINITY;
+    const float nD0 = DROP ? nD / p.drop.scale : nD;   // the dP accumulator's start
 
     f32x16 acc[D / 32];
 #pragma unroll
@@ -240,12 +245,30 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 3 : 1) void rsa_bwd_dq(BwdParam
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     s[r] = 0.0f;
-                    dp[r] = nD;
+                    dp[r] = nD0;
                 }
 #pragma unroll
                 for (int ks = 0; ks < D / 16; ++ks) {
                     s = mfma_32x32x16_bf16(kfr[ks], qf[ks], s);
                     dp = mfma_32x32x16_bf16(vfr[ks], gf[ks], dp);
+                }
+            }
+            if constexpr (DROP) {
+                // register r holds key 8 (r / 4) + 4 h + r % 4 of this 32-key
+                // half: byte r % 4 of word r / 4 of its keep bytes
+                if constexpr (CONTIG) {
+                    const int jb = (ring_pos(t * kKT, n, p.N, p.Lc) >> 5) + kb2;
+                    const u32x4 x = dropout_bytes(p.drop, jb, h, row, bh);
+#pragma unroll
+                    for (int r = 0; r < 16; ++r)
+                        dp[r] = ((x[r >> 2] >> (8 * (r & 3))) & 0xffu) >= p.drop.p8 ? dp[r] * p.drop.scale : nD;
+                } else {
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int vk = t * kKT + 32 * kb2 + acc_row(r, h);
+                        const bool keep = vk >= p.L || dropout_keep(p.drop, row, ring_pos(vk, n, p.N, p.Lc), bh);
+                        dp[r] = keep ? dp[r] * p.drop.scale : nD;
+                    }
                 }
             }
             if (bits != ~0ull) {
@@ -331,13 +354,22 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 3 : 1) void rsa_bwd_dq(BwdParam
 // (The causal instance runs at two waves per SIMD: its per-element mask of
 // the diagonal tiles pushes three waves' worth of registers into spills,
 // which measured 21% slower.)
-template <int D, bool CONTIG, bool CAUSAL>
-__global__ __launch_bounds__(kThreads, D == 64 ? (CAUSAL ? 2 : 3) : 1) void rsa_bwd_dkdv(BwdParams p) {
+// DROP: dropout of the forward's weights. The lanes of this kernel hold keys
+// and its registers query rows, the transpose of the forward's layout, so
+// the keep bytes are exchanged through LDS: per query tile each lane draws
+// the two counters of one query row (the wave's 32 keys are one 32-key
+// block, two halves), writes their 32 bytes into the wave's table, and each
+// lane then reads its key's byte for its 32 rows. dV takes P Z, and dS =
+// P (Z dP - D) as in the dQ kernel.
+template <int D, bool CONTIG, bool CAUSAL, bool DROP = false>
+__global__ __launch_bounds__(kThreads, D == 64 ? ((CAUSAL || DROP) ? 2 : 3) : 1) void rsa_bwd_dkdv(BwdParams p) {
     using T = DirectTile<D>;
     constexpr int NBUF = 3;
     constexpr int ROWV = 2 * kKT * 4;             // -D and -lse*log2(e) for 64 rows
     constexpr int BUF = 2 * T::BYTES + ROWV;      // Q, dO, row statistics
     __shared__ __attribute__((aligned(1024))) uint8_t smem[NBUF * BUF];
+    // per wave: keep words [half hh][word w][row u]
+    __shared__ __attribute__((aligned(16))) uint32_t keep_tab[DROP ? 4 * 2 * 4 * kKT : 1];
 
     const int lid = xcd_remap(blockIdx.x, p.nt * p.BH);
     const int kt = lid % p.nt, bh = lid / p.nt, b = bh / p.H;
@@ -458,6 +490,22 @@ __global__ __launch_bounds__(kThreads, D == 64 ? (CAUSAL ? 2 : 3) : 1) void rsa_
         // workgroup (then rows are masked per element)?
         const int pos0c = (CAUSAL && CONTIG) ? ring_pos_rev(t * kKT, c, p.N, p.Lc) : 0;
         const bool cmask = CAUSAL && (!CONTIG || pos0c < key_last);
+        uint32_t* ktab = keep_tab + (DROP ? wave * (2 * 4 * kKT) : 0);
+        if constexpr (DROP) {
+            // lane l draws the keep bytes of query row l of the tile for the
+            // wave's 32-key block (both halves) and writes them to its table
+            const int u = t * kKT + lane;
+            if (u < p.L) {
+                const int qpos = CONTIG ? ring_pos_rev(t * kKT, c, p.N, p.Lc) + lane : ring_pos_rev(u, c, p.N, p.Lc);
+                const int jb = (key0 >> 5) + wave;
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh) {
+                    const u32x4 x = dropout_bytes(p.drop, jb, hh, qpos, bh);
+#pragma unroll
+                    for (int w = 0; w < 4; ++w) ktab[(hh * 4 + w) * kKT + lane] = x[w];
+                }
+            }
+        }
         // two 32-query halves in turn, to bound the live registers
 #pragma unroll
         for (int qb2 = 0; qb2 < 2; ++qb2) {
@@ -474,7 +522,7 @@ __global__ __launch_bounds__(kThreads, D == 64 ? (CAUSAL ? 2 : 3) : 1) void rsa_
                 for (int r4 = 0; r4 < 4; ++r4) {   // dP accumulators start at -D of their rows
                     const f32x4 d4 = *reinterpret_cast<const f32x4*>(nDs + 32 * qb2 + 8 * r4 + 4 * h);
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) dp[4 * r4 + e] = d4[e];
+                    for (int e = 0; e < 4; ++e) dp[4 * r4 + e] = DROP ? d4[e] / p.drop.scale : d4[e];
                 }
 #pragma unroll
                 for (int r = 0; r < 16; ++r) s[r] = 0.0f;
@@ -512,11 +560,26 @@ __global__ __launch_bounds__(kThreads, D == 64 ? (CAUSAL ? 2 : 3) : 1) void rsa_
             for (int r4 = 0; r4 < 4; ++r4) {
                 const f32x4 l4 = *reinterpret_cast<const f32x4*>(nLs + 32 * qb2 + 8 * r4 + 4 * h);
                 float pv[4], dsv[4];
+                if constexpr (DROP) {
+                    // keep bytes of rows 32 qb2 + 8 r4 + 4 h + {0..3} for this lane's key
+                    const u32x4 kw = *reinterpret_cast<const u32x4*>(
+                        ktab + (((j >> 2) & 1) * 4 + ((j >> 3) & 3)) * kKT + 32 * qb2 + 8 * r4 + 4 * h);
+                    const f32x4 d4 = *reinterpret_cast<const f32x4*>(nDs + 32 * qb2 + 8 * r4 + 4 * h);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int r = 4 * r4 + e;
-                    pv[e] = fast_exp2(fmaf(s[r], p.sl2, l4[e]));
-                    dsv[e] = pv[e] * dp[r];
+                    for (int e = 0; e < 4; ++e) {
+                        const int r = 4 * r4 + e;
+                        const bool keep = ((kw[e] >> (8 * (j & 3))) & 0xffu) >= p.drop.p8;
+                        const float pr = fast_exp2(fmaf(s[r], p.sl2, l4[e]));
+                        pv[e] = keep ? pr * p.drop.scale : 0.0f;
+                        dsv[e] = pr * (keep ? dp[r] * p.drop.scale : d4[e]);
+                    }
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int r = 4 * r4 + e;
+                        pv[e] = fast_exp2(fmaf(s[r], p.sl2, l4[e]));
+                        dsv[e] = pv[e] * dp[r];
+                    }
                 }
                 pp[2 * r4] = pack_bf16x2(pv[0], pv[1]);
                 pp[2 * r4 + 1] = pack_bf16x2(pv[2], pv[3]);
@@ -614,6 +677,11 @@ BwdParams make_params(const BackwardCall& c) {
     p.scale = (float)(1.0 / __builtin_sqrt((double)c.d));
     p.causal = c.causal ? 1 : 0;
     p.sl2 = (float)(1.4426950408889634 / __builtin_sqrt((double)c.d));
+    p.drop.p8 = c.drop_p8;
+    p.drop.seed_lo = (uint32_t)c.drop_seed;
+    p.drop.seed_hi = (uint32_t)(c.drop_seed >> 32);
+    p.drop.offset = c.drop_offset;
+    p.drop.scale = (float)(256.0 / (256.0 - (double)c.drop_p8));
     return p;
 }
 
@@ -630,6 +698,33 @@ hipError_t launch_t(const BackwardCall& c, int stages, hipStream_t stream) {
         if (e != hipSuccess) return e;
     }
     const unsigned blocks = (unsigned)((long long)p.nt * p.BH);
+    if (p.drop.p8 != 0u) {
+        if (stages & kBwdStageDq) {
+            if (contig && !p.causal)
+                hipLaunchKernelGGL((rsa_bwd_dq<D, true, false, true>), dim3(blocks), dim3(kThreads), 0, stream, p);
+            else if (!p.causal)
+                hipLaunchKernelGGL((rsa_bwd_dq<D, false, false, true>), dim3(blocks), dim3(kThreads), 0, stream, p);
+            else if (contig)
+                hipLaunchKernelGGL((rsa_bwd_dq<D, true, true, true>), dim3(blocks), dim3(kThreads), 0, stream, p);
+            else
+                hipLaunchKernelGGL((rsa_bwd_dq<D, false, true, true>), dim3(blocks), dim3(kThreads), 0, stream, p);
+            hipError_t e = hipGetLastError();
+            if (e != hipSuccess) return e;
+        }
+        if (stages & kBwdStageDkDv) {
+            if (contig && !p.causal)
+                hipLaunchKernelGGL((rsa_bwd_dkdv<D, true, false, true>), dim3(blocks), dim3(kThreads), 0, stream, p);
+            else if (!p.causal)
+                hipLaunchKernelGGL((rsa_bwd_dkdv<D, false, false, true>), dim3(blocks), dim3(kThreads), 0, stream, p);
+            else if (contig)
+                hipLaunchKernelGGL((rsa_bwd_dkdv<D, true, true, true>), dim3(blocks), dim3(kThreads), 0, stream, p);
+            else
+                hipLaunchKernelGGL((rsa_bwd_dkdv<D, false, true, true>), dim3(blocks), dim3(kThreads), 0, stream, p);
+            hipError_t e = hipGetLastError();
+            if (e != hipSuccess) return e;
+        }
+        return hipSuccess;
+    }
     if (stages & kBwdStageDq) {
         if (contig && !p.causal)
             hipLaunchKernelGGL((rsa_bwd_dq<D, true, false>), dim3(blocks), dim3(kThreads), 0, stream, p);

@@ -42,6 +42,7 @@ struct BwdF32Params {
     float sl2;                 // log2(e) / sqrt(d)
     float scale;               // 1 / sqrt(d)
     int causal;
+    Dropout drop;              // the forward's dropout (drop.p8 == 0: none)
 };
 
 // Sequence position of the u-th query row that key chunk c meets: ring step
@@ -171,7 +172,12 @@ __global__ __launch_bounds__(kThreads) void rsa_bwd_dq_f32(BwdF32Params p) {
                     vis = (mrow == nullptr || mrow[pos] != 0) && !(p.causal && pos > row);
                 }
                 const float pr = vis ? fast_exp2(fmaf(s[r], p.sl2, nl2)) : 0.0f;
-                const float ds = pr * dp[r];
+                float dpz = dp[r];   // dP - D, or with dropout Z dP - D
+                if (p.drop.p8 != 0u && vis) {
+                    const bool keep = dropout_keep(p.drop, row, ring_pos(vk, n, p.N, p.Lc), bh);
+                    dpz = keep ? fmaf(dp[r] - nD, p.drop.scale, nD) : nD;
+                }
+                const float ds = pr * dpz;
 #pragma unroll
                 for (int db = 0; db < D / 32; ++db) acc[db] = mfma_32x32x2_f32(ks[kr * KP + 32 * db + j], ds, acc[db]);
             }
@@ -265,8 +271,13 @@ __global__ __launch_bounds__(kThreads) void rsa_bwd_dkdv_f32(BwdF32Params p) {
             for (int r = 0; r < 16; ++r) {
                 const int u = 32 * qb + acc_row(r, h);   // query row of the tile
                 const bool vis = !(p.causal && key > st_pos[u]);
-                const float pr = vis ? fast_exp2(fmaf(s[r], p.sl2, st_l[u])) : 0.0f;
-                const float ds = pr * (dp[r] + st_d[u]);
+                float pr = vis ? fast_exp2(fmaf(s[r], p.sl2, st_l[u])) : 0.0f;
+                float ds = pr * (dp[r] + st_d[u]);
+                if (p.drop.p8 != 0u && vis && st_pos[u] >= 0) {   // dV takes P Z, dS = P (Z dP - D)
+                    const bool keep = dropout_keep(p.drop, st_pos[u], key, bh);
+                    ds = pr * (keep ? fmaf(dp[r], p.drop.scale, st_d[u]) : st_d[u]);
+                    pr = keep ? pr * p.drop.scale : 0.0f;
+                }
 #pragma unroll
                 for (int db = 0; db < D / 32; ++db) {
                     dv[db] = mfma_32x32x2_f32(gs[u * KP + 32 * db + j], pr, dv[db]);
@@ -320,6 +331,11 @@ hipError_t launch_t(const BackwardCall& c, int stages, hipStream_t stream) {
     p.scale = (float)(1.0 / __builtin_sqrt((double)D));
     p.sl2 = (float)(1.4426950408889634 / __builtin_sqrt((double)D));
     p.causal = c.causal ? 1 : 0;
+    p.drop.p8 = c.drop_p8;
+    p.drop.seed_lo = (uint32_t)c.drop_seed;
+    p.drop.seed_hi = (uint32_t)(c.drop_seed >> 32);
+    p.drop.offset = c.drop_offset;
+    p.drop.scale = (float)(256.0 / (256.0 - (double)c.drop_p8));
     const long long rows = (long long)p.BH * c.L;
     if (stages & kBwdStagePre) {
         const long long threads = rows * (D / 4);

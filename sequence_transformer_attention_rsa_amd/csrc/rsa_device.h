@@ -67,6 +67,61 @@ __device__ __forceinline__ int ring_pos(int v, int n, int N, int Lc) {
     return c * Lc + (v - t * Lc);
 }
 
+// -------------------------------------------------------------- dropout ---
+// Philox-4x32-10 (Salmon, Moraes, Dror and Shaw, "Parallel Random Numbers:
+// As Easy as 1, 2, 3", SC'11): counter (c0..c3), key (k0, k1); ten rounds of
+// hi0:lo0 = M0 * c0, hi1:lo1 = M1 * c2, counter <- (hi1 ^ c1 ^ k0, lo1,
+// hi0 ^ c3 ^ k1, lo0), with the key increased by the Weyl constants between
+// rounds. Each 32x32 -> 64 product is one v_mad_u64_u32.
+__device__ __forceinline__ u32x4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3, uint32_t k0,
+                                               uint32_t k1) {
+#pragma unroll
+    for (int r = 0; r < 10; ++r) {
+        const uint64_t p0 = (uint64_t)0xD2511F53u * c0;
+        const uint64_t p1 = (uint64_t)0xCD9E8D57u * c2;
+        const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0;
+        const uint32_t n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+        c1 = (uint32_t)p1;
+        c3 = (uint32_t)p0;
+        c0 = n0;
+        c2 = n2;
+        k0 += 0x9E3779B9u;
+        k1 += 0xBB67AE85u;
+    }
+    const u32x4 x = {c0, c1, c2, c3};
+    return x;
+}
+
+// Dropout of the softmax weights. The keep decision of the weight of query
+// position i and key position j in head bh is byte (j mod 4) of word
+// ((j / 8) mod 4) of Philox-4x32-10 at counter ((j / 32) * 2 + bit 2 of j,
+// i, bh, offset), key (seed low, seed high) words; the weight is kept iff
+// that byte is >= p8 (drop probability p8 / 256) and then scaled by
+// 256 / (256 - p8). One counter covers the 16 keys of a 32-key block that
+// share bit 2 of j -- the keys one lane of a 32x32 accumulator holds.
+struct Dropout {
+    uint32_t p8;       // 0: no dropout
+    uint32_t seed_lo, seed_hi, offset;
+    float scale;       // 256 / (256 - p8)
+};
+
+// The 16 bytes of the counter of (key block jb = j / 32, half hh = bit 2 of j, query i, head bh).
+__device__ __forceinline__ u32x4 dropout_bytes(const Dropout& dr, int jb, int hh, int i, int bh) {
+    return philox4x32_10((uint32_t)((jb << 1) | hh), (uint32_t)i, (uint32_t)bh, dr.offset, dr.seed_lo, dr.seed_hi);
+}
+
+// Keep decision of one weight (query position i, key position j, head bh).
+__device__ __forceinline__ bool dropout_keep(const Dropout& dr, int i, int j, int bh) {
+    const u32x4 x = dropout_bytes(dr, j >> 5, (j >> 2) & 1, i, bh);
+    return ((x[(j >> 3) & 3] >> (8 * (j & 3))) & 0xffu) >= dr.p8;
+}
+
+// Mask for a dword of two bf16 weights whose keep bytes are the low two
+// bytes of w: each 16-bit half all ones if kept, zero if dropped.
+__device__ __forceinline__ uint32_t keep_mask_bf16x2(uint32_t w, uint32_t p8) {
+    return ((w & 0xffu) >= p8 ? 0x0000ffffu : 0u) | (((w >> 8) & 0xffu) >= p8 ? 0xffff0000u : 0u);
+}
+
 // ------------------------------------------------------------- dispatch ---
 // Workgroups are dealt to the XCDs round-robin by id. Renumber them so that
 // each XCD receives a contiguous range of logical work items: neighbouring

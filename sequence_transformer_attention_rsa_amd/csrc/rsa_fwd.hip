@@ -78,6 +78,7 @@ struct FwdParams {
     int contiguous;   // Lc % kKT == 0: a tile never straddles two chunks
     int strided;      // bf16, groups > 1, contiguous: group g takes ring steps g, g + groups, ...
     int causal;       // the query at position i sees keys at positions <= i only
+    Dropout drop;     // dropout of the normalised weights (drop.p8 == 0: none)
 };
 
 // fp32 forward (fp32 inputs and output): the same ring-ordered online
@@ -252,9 +253,13 @@ __global__ __launch_bounds__(kThreads) void rsa_fwd_f32(FwdParams p) {
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const float pr = fast_exp2(fmaf(s[kb][r], p.sl2, nb));
-                l += pr;
+                float pr = fast_exp2(fmaf(s[kb][r], p.sl2, nb));
+                l += pr;   // the row sum counts every weight, kept or dropped
                 const int key = 32 * kb + acc_row(r, h);
+                if (p.drop.p8 != 0u) {
+                    const int vk = v0 + key;
+                    if (vk < vend && !dropout_keep(p.drop, p.q_pos0 + row, ring_pos(vk, n, p.N, p.Lc), bh)) pr = 0.0f;
+                }
 #pragma unroll
                 for (int db = 0; db < D / 32; ++db) o[db] = mfma_32x32x2_f32(vs_[key * D + 32 * db + j], pr, o[db]);
             }
@@ -266,8 +271,9 @@ __global__ __launch_bounds__(kThreads) void rsa_fwd_f32(FwdParams p) {
 
     const float l_row = l + shfl_xor32(l);
     if (!row_ok) return;
+    const float ks = p.drop.p8 != 0u ? p.drop.scale : 1.0f;   // kept weights scaled by 1 / (1 - p)
     if (p.groups == 1) {
-        const float inv = l_row > 0.0f ? 1.0f / l_row : 0.0f;
+        const float inv = l_row > 0.0f ? ks / l_row : 0.0f;
         float* orow = static_cast<float*>(p.out) + ((size_t)bh * p.Lq + row) * D;
 #pragma unroll
         for (int db = 0; db < D / 32; ++db)
@@ -286,7 +292,8 @@ __global__ __launch_bounds__(kThreads) void rsa_fwd_f32(FwdParams p) {
         for (int db = 0; db < D / 32; ++db)
 #pragma unroll
             for (int r4 = 0; r4 < 4; ++r4) {
-                const f32x4 w = {o[db][4 * r4], o[db][4 * r4 + 1], o[db][4 * r4 + 2], o[db][4 * r4 + 3]};
+                const f32x4 w = {o[db][4 * r4] * ks, o[db][4 * r4 + 1] * ks, o[db][4 * r4 + 2] * ks,
+                                 o[db][4 * r4 + 3] * ks};
                 *reinterpret_cast<f32x4*>(po + 32 * db + 8 * r4 + 4 * h) = w;
             }
         if (h == 0) {
@@ -309,10 +316,14 @@ __global__ __launch_bounds__(kThreads) void rsa_fwd_f32(FwdParams p) {
 // FULL: no key mask, no causal mask and chunk-aligned tiles, so every key
 // tile of the range is whole and visible: the occupancy table is not built
 // and the loop takes every tile without looking it up.
-template <int D, bool CONTIG, int QB, bool CAUSAL, bool FULL = false>
+// DROP: dropout of the normalised weights (the row sums count every weight;
+// dropped ones are zeroed in the packed bf16 operand of the PV product and
+// the output is scaled by 1 / (1 - p) at the end).
+template <int D, bool CONTIG, int QB, bool CAUSAL, bool FULL = false, bool DROP = false>
 __global__ __launch_bounds__(256 / QB, (D == 64 && QB == 1) ? 4 : 2)
 void rsa_fwd_bf16(FwdParams p) {
     static_assert(!FULL || (CONTIG && !CAUSAL), "whole tiles need chunk-aligned, non-causal ranges");
+    static_assert(!DROP || (QB == 1 && !FULL), "dropout instances: one query block per wave, general tiles");
     // QB 32-row query blocks per wave; 128 query rows per workgroup either
     // way (4 waves x 32 rows, or 2 waves x 64 rows: each K and V^T fragment
     // read from LDS then feeds two MFMAs).
@@ -573,6 +584,38 @@ void rsa_fwd_bf16(FwdParams p) {
             l1[qb] = tl1[qb];
             lim[qb] = tsum[qb] + kMaxTileSum;
         }
+        if constexpr (DROP) {
+            // zero the dropped weights: dword i of block kb holds keys
+            // 8 (i / 2) + 4 h + 2 (i % 2) + {0, 1} of the block, whose keep
+            // bytes are bytes 2 (i % 2) + {0, 1} of word i / 2
+            const int qpos = p.q_pos0 + wrow0 + j;
+            const int tv0 = tile_v0(t);
+            if constexpr (CONTIG) {
+                const int jb0 = ring_pos(tv0, n, p.N, p.Lc) >> 5;   // tiles are 64-key aligned here
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb) {
+                    const u32x4 x = dropout_bytes(p.drop, jb0 + kb, h, qpos, bh);
+#pragma unroll
+                    for (int i = 0; i < 8; ++i)
+                        pk[0][kb][i] &= keep_mask_bf16x2(x[i >> 1] >> (16 * (i & 1)), p.drop.p8);
+                }
+            } else {
+                const int ve = tile_end(tv0);
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) {
+                        uint32_t m = 0xffffffffu;
+#pragma unroll
+                        for (int e = 0; e < 2; ++e) {
+                            const int vk = tv0 + 32 * kb + acc_row(2 * i + e, h);
+                            if (vk < ve && !dropout_keep(p.drop, qpos, ring_pos(vk, n, p.N, p.Lc), bh))
+                                m &= e ? 0x0000ffffu : 0xffff0000u;
+                        }
+                        pk[0][kb][i] &= m;
+                    }
+            }
+        }
         // ---- O^T += V^T P^T, four 16-key steps
 #pragma unroll
         for (int stp = 0; stp < 4; ++stp) {
@@ -600,6 +643,7 @@ void rsa_fwd_bf16(FwdParams p) {
     }
 
     // ---- epilogue
+    const float ks = DROP ? p.drop.scale : 1.0f;   // kept weights scaled by 1 / (1 - p)
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
         const int row = wrow0 + 32 * qb + j;
@@ -607,7 +651,7 @@ void rsa_fwd_bf16(FwdParams p) {
         const float l_row = lsum + shfl_xor32(lsum);
         if (row >= p.Lq) continue;
         if (p.groups == 1) {
-            const float inv = l_row > 0.0f ? 1.0f / l_row : 0.0f;
+            const float inv = l_row > 0.0f ? ks / l_row : 0.0f;
             uint16_t* orow = static_cast<uint16_t*>(p.out) + ((size_t)bh * p.Lq + row) * D;
 #pragma unroll
             for (int db = 0; db < D / 32; ++db)
@@ -629,7 +673,7 @@ void rsa_fwd_bf16(FwdParams p) {
 #pragma unroll
                 for (int r4 = 0; r4 < 4; ++r4) {
                     const f32x16& a = o[qb][db];
-                    const f32x4 w = {a[4 * r4], a[4 * r4 + 1], a[4 * r4 + 2], a[4 * r4 + 3]};
+                    const f32x4 w = {a[4 * r4] * ks, a[4 * r4 + 1] * ks, a[4 * r4 + 2] * ks, a[4 * r4 + 3] * ks};
                     *reinterpret_cast<f32x4*>(po + 32 * db + 8 * r4 + 4 * h) = w;
                 }
             if (h == 0) {
@@ -706,6 +750,11 @@ hipError_t launch_t(const ForwardCall& c, hipStream_t stream) {
     p.contiguous = (p.Lc % kKT) == 0;
     p.strided = (BF16 && c.groups > 1 && p.contiguous) ? 1 : 0;
     p.causal = c.causal ? 1 : 0;
+    p.drop.p8 = c.drop_p8;
+    p.drop.seed_lo = (uint32_t)c.drop_seed;
+    p.drop.seed_hi = (uint32_t)(c.drop_seed >> 32);
+    p.drop.offset = c.drop_offset;
+    p.drop.scale = (float)(256.0 / (256.0 - (double)c.drop_p8));
     if (c.groups > 1) {
         p.part_o = c.part;
         p.part_ml = c.part + (size_t)c.groups * p.BH * c.Lq * D;
@@ -718,7 +767,20 @@ hipError_t launch_t(const ForwardCall& c, hipStream_t stream) {
         // measured 12% slower at d = 64.
         constexpr int QB = 1;
         const dim3 block(kWave * 4 / QB);
-        if (p.contiguous && !p.causal && p.mask == nullptr)
+        if (p.drop.p8 != 0u) {
+            if (p.contiguous && !p.causal)
+                hipLaunchKernelGGL((rsa_fwd_bf16<D, true, QB, false, false, true>), dim3((unsigned)total), block, 0,
+                                   stream, p);
+            else if (!p.causal)
+                hipLaunchKernelGGL((rsa_fwd_bf16<D, false, QB, false, false, true>), dim3((unsigned)total), block, 0,
+                                   stream, p);
+            else if (p.contiguous)
+                hipLaunchKernelGGL((rsa_fwd_bf16<D, true, QB, true, false, true>), dim3((unsigned)total), block, 0,
+                                   stream, p);
+            else
+                hipLaunchKernelGGL((rsa_fwd_bf16<D, false, QB, true, false, true>), dim3((unsigned)total), block, 0,
+                                   stream, p);
+        } else if (p.contiguous && !p.causal && p.mask == nullptr)
             hipLaunchKernelGGL((rsa_fwd_bf16<D, true, QB, false, true>), dim3((unsigned)total), block, 0, stream, p);
         else if (p.contiguous && !p.causal)
             hipLaunchKernelGGL((rsa_fwd_bf16<D, true, QB, false>), dim3((unsigned)total), block, 0, stream, p);

@@ -30,6 +30,9 @@ struct ForwardCall {
     int groups;             // ring-step groups computed in parallel (1 = no split)
     bool bf16;
     bool causal;            // the query at position i sees keys at positions <= i only
+    uint32_t drop_p8;       // dropout of the softmax weights, probability drop_p8 / 256 (0: none)
+    uint32_t drop_offset;
+    uint64_t drop_seed;
 };
 
 // Bytes of split partials for `groups` ring-step groups.
@@ -63,6 +66,9 @@ struct BackwardCall {
     int B, H, L, d, N;
     bool bf16;              // bf16 tensors; fp32 otherwise
     bool causal;
+    uint32_t drop_p8;       // dropout as in ForwardCall (the forward's settings)
+    uint32_t drop_offset;
+    uint64_t drop_seed;
 };
 
 size_t backward_workspace_bytes(int B, int H, int L, int d);

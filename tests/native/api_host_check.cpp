@@ -119,6 +119,27 @@ void forward_checks() {
     CHECK(rsa_forward(cp(P), cp(P), cp(P), nullptr, 1 << 15, 1 << 15, 2, 64, 1, RSA_BF16, nullptr, vp(P), nullptr) ==
           RSA_ERR_UNSUPPORTED);   // more rows than the launch grid covers
     CHECK(g_fwd == n0 + 2);
+    // dropout: the probability is quantised to p8 / 256 and carried with the seed and offset
+    rsa_dropout dr;
+    dr.p = 0.1f;
+    dr.offset = 9;
+    dr.seed = 0x1122334455667788ull;
+    CHECK(rsa_forward_dropout(cp(P), cp(P), cp(P), nullptr, 1, 2, 256, 64, 4, RSA_BF16, 0, &dr, nullptr, vp(P),
+                              nullptr) == RSA_OK);
+    CHECK(g_last_fwd.drop_p8 == 26 && g_last_fwd.drop_offset == 9 && g_last_fwd.drop_seed == dr.seed);
+    dr.p = 0.0f;
+    CHECK(rsa_forward_dropout(cp(P), cp(P), cp(P), nullptr, 1, 2, 256, 64, 4, RSA_BF16, 0, &dr, nullptr, vp(P),
+                              nullptr) == RSA_OK);
+    CHECK(g_last_fwd.drop_p8 == 0 && g_last_fwd.drop_seed == 0);
+    CHECK(rsa_forward(cp(P), cp(P), cp(P), nullptr, 1, 2, 256, 64, 4, RSA_BF16, nullptr, vp(P), nullptr) == RSA_OK);
+    CHECK(g_last_fwd.drop_p8 == 0);
+    dr.p = 0.999f;
+    CHECK(rsa_forward_dropout(cp(P), cp(P), cp(P), nullptr, 1, 2, 256, 64, 4, RSA_BF16, 0, &dr, nullptr, vp(P),
+                              nullptr) == RSA_ERR_UNSUPPORTED);
+    dr.p = 1.0f / 512.0f;
+    CHECK(rsa_forward_dropout(cp(P), cp(P), cp(P), nullptr, 1, 2, 256, 64, 4, RSA_F32, 0, &dr, nullptr, vp(P),
+                              nullptr) == RSA_OK);
+    CHECK(g_last_fwd.drop_p8 == 1);
 }
 
 void rank_checks() {
@@ -158,7 +179,15 @@ void backward_checks() {
     CHECK(g_last_stages == rsa::kBwdStageAll && g_last_bwd.stats == fp(W) && g_last_bwd.bf16);
     CHECK(rsa_backward(cp(P), cp(P), cp(P), cp(P), cp(P), fp(P), nullptr, B, H, L, d, N, RSA_F32, vp(W), ws,
                        nullptr, vp(P), vp(P), vp(P)) == RSA_OK);
-    CHECK(!g_last_bwd.bf16);
+    CHECK(!g_last_bwd.bf16 && g_last_bwd.drop_p8 == 0);
+    rsa_dropout dr;
+    dr.p = 0.5f;
+    dr.offset = 3;
+    dr.seed = 42;
+    CHECK(rsa_backward_dropout(cp(P), cp(P), cp(P), cp(P), cp(P), fp(P), nullptr, B, H, L, d, N, RSA_BF16,
+                               RSA_CAUSAL, &dr, vp(W), ws, nullptr, vp(P), vp(P), vp(P)) == RSA_OK);
+    CHECK(g_last_bwd.drop_p8 == 128 && g_last_bwd.drop_offset == 3 && g_last_bwd.drop_seed == 42 &&
+          g_last_bwd.causal);
     CHECK(rsa_backward(cp(P), cp(P), cp(P), cp(P), cp(P), fp(P), nullptr, B, H, L, d, N, RSA_BF16, vp(W), ws - 4,
                        nullptr, vp(P), vp(P), vp(P)) == RSA_ERR_WORKSPACE);
     CHECK(rsa_backward_ex(cp(P), cp(P), cp(P), cp(P), cp(P), fp(P), nullptr, B, H, L, d, N, RSA_BF16, 8, vp(W), ws,

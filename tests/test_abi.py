@@ -148,6 +148,8 @@ def test_linear_and_layernorm_validation(lib):
     assert ln(E=100) == EUNSUP
     assert ln(E=8192) == EUNSUP
     assert ln(eps=-1.0) == EUNSUP
+    assert ln(eps=float("nan")) == EUNSUP
+    assert ln(eps=float("inf")) == EUNSUP
     assert ln(y=P + 2) == EALIGN
 
 
@@ -230,3 +232,31 @@ def test_backward_noalloc_validation(lib):
     assert call(B=1, H=3, L=1048576, N=64) == ESCRATCH
     assert call(B=4, H=1, L=524288 + 64, N=64) == ESCRATCH
     assert "static scratch" in rsa.status_string(ESCRATCH)
+
+
+def test_dropout_validation(lib):
+    """The dropout entry points reject probabilities outside [0, 1 - 1/512]
+    and NaN, and validate the rest like the plain ones, before any HIP call."""
+    import math
+
+    def fwd(p, q=P, flags=0, L=256):
+        dr = rsa._Dropout(p, 0, 123)
+        return lib.rsa_forward_dropout(q, P, P, None, 1, 2, L, 64, 4, BF16, flags, ctypes.byref(dr), None, P, None)
+
+    assert fwd(1.0) == EUNSUP
+    assert fwd(0.999) == EUNSUP          # 256 p + 1/2 rounds to 256
+    assert fwd(-0.01) == EUNSUP
+    assert fwd(math.nan) == EUNSUP
+    assert fwd(0.5, q=None) == ENULL
+    assert fwd(0.5, L=255) == ESHAPE
+    assert fwd(0.5, flags=2) == EUNSUP
+    bws = lib.rsa_backward_workspace_bytes(1, 2, 256, 64, 4, BF16)
+    dr = rsa._Dropout(1.5, 0, 1)
+    assert lib.rsa_backward_dropout(P, P, P, P, P, P, None, 1, 2, 256, 64, 4, BF16, 0, ctypes.byref(dr), P, bws,
+                                    None, P, P, P) == EUNSUP
+    dr = rsa._Dropout(0.1, 0, 1)
+    assert lib.rsa_backward_dropout(P, P, P, P, P, P, None, 1, 2, 256, 64, 4, BF16, 0, ctypes.byref(dr), None, bws,
+                                    None, P, P, P) == EWS
+    ws = lib.rsa_forward_rank_workspace_bytes(1, 16, 32768, 128, 64)
+    assert lib.rsa_forward_rank_dropout(P, P, P, None, 1, 16, 32768, 128, 64, 64, BF16, 0, ctypes.byref(dr), P, ws,
+                                        None, P, None) == ESHAPE
