@@ -102,23 +102,23 @@ __device__ __forceinline__ void load_rowvec(uint8_t* lds, const float* src, RowO
 }
 
 // ------------------------------------------------------------------ dQ ---
-#ifndef RSA_DQ_NBUF
-#define RSA_DQ_NBUF 2
-#endif
 // Query-stationary, mirror of the forward: 4 waves x 32 query rows; per key
 // tile S^T = K Q^T and dP^T = V dO^T (lane <-> query), then
 // dQ^T += K^T dS^T with K^T from the transposing read of the same K tile.
 // DROP: with dropout, dS = P o (Z o dP - D) for the forward's keep factors Z
 // (kept: 1 / (1 - p), dropped: 0); the dP accumulator then starts at
 // -D (1 - p), so that a kept weight takes acc / (1 - p) and a dropped one -D.
-template <int D, bool CONTIG, bool CAUSAL, bool DROP = false>
+// FULL: no key mask, no causal mask and chunk-aligned tiles, so every key
+// tile is whole and visible: no occupancy table is built or consulted, and
+// the two 32-key halves of a tile are unrolled (their LDS offsets become
+// constants of the read instructions).
+template <int D, bool CONTIG, bool CAUSAL, bool DROP = false, bool FULL = false>
 __global__ __launch_bounds__(kThreads, D == 64 ? 3 : 1) void rsa_bwd_dq(BwdParams p) {
+    static_assert(!FULL || (CONTIG && !CAUSAL && !DROP), "whole tiles need chunk-aligned, unmasked ranges");
     using T = DirectTile<D>;
     constexpr int BUF = 2 * T::BYTES;   // K, V
-    constexpr int NBUF = RSA_DQ_NBUF;
-    constexpr int kCopies = 2 * T::IPW;   // copies per wave and tile
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[NBUF * BUF];
-    __shared__ uint8_t tflag_bytes[kFwdMaxTiles / 4];
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * BUF];
+    __shared__ uint8_t tflag_bytes[FULL ? 4 : kFwdMaxTiles / 4];
     const TileTable tflag{tflag_bytes};
 
     const int lid = xcd_remap(blockIdx.x, p.nt * p.BH);
@@ -141,10 +141,13 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 3 : 1) void rsa_bwd_dq(BwdParam
     const size_t rows_all = (size_t)p.BH * p.L;
 
     const int qhi = min(row0 + 128, p.L) - 1;
-    tflag.build(ntile, kThreads, [&](int t) {
-        const uint32_t f = key_tile_flags(mrow, n, p.N, p.Lc, CONTIG, t * kKT, p.L);
-        return CAUSAL ? f & causal_tile_class(t * kKT, min(kKT, p.L - t * kKT), n, p.N, p.Lc, CONTIG, row0, qhi) : f;
-    });
+    if constexpr (!FULL) {
+        tflag.build(ntile, kThreads, [&](int t) {
+            const uint32_t f = key_tile_flags(mrow, n, p.N, p.Lc, CONTIG, t * kKT, p.L);
+            return CAUSAL ? f & causal_tile_class(t * kKT, min(kKT, p.L - t * kKT), n, p.N, p.Lc, CONTIG, row0, qhi)
+                          : f;
+        });
+    }
 
     u32x4 qf[D / 16], gf[D / 16];
 #pragma unroll
@@ -193,46 +196,33 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 3 : 1) void rsa_bwd_dq(BwdParam
     };
     auto next_tile = [&](int t) {
         ++t;
-        while (t < ntile && !(tflag.get(t) & 1)) ++t;
+        if constexpr (!FULL)
+            while (t < ntile && !(tflag.get(t) & 1)) ++t;
         return t;
     };
 
-    // Two LDS buffers (RSA_DQ_NBUF): the copy of tile t+1 is issued right after
-    // the barrier that opens tile t and lands while t is computed. Three
-    // buffers (the copy of t+2 in flight until t+1 opens) need 100 KB of LDS
-    // per workgroup at d = 64, leave one workgroup per CU and measured 3.7x
-    // slower.
+    // Two LDS buffers: the copy of tile t+1 is issued right after the barrier
+    // that opens tile t and lands while t is computed. (Three buffers, the
+    // copy of t+2 in flight until t+1 opens, need 100 KB of LDS per
+    // workgroup at d = 64, leave one workgroup per CU and measured 3.7x
+    // slower.)
     int t = next_tile(-1);
-    int t1 = t < ntile ? next_tile(t) : ntile;
     auto body = [&](auto cb_c) -> bool {
         constexpr int CB = decltype(cb_c)::value;
-        constexpr int FB = (CB + NBUF - 1) % NBUF;   // buffer of tile t-1
-        if (NBUF == 3 && t1 < ntile)
-            vm_wait<kCopies>();   // tile t landed; the copy of t1 may stay in flight
-        else
-            vm_wait<0>();
+        vm_wait<0>();
         bare_barrier();   // every wave's part of tile t landed, tile t-1 consumed
-        int tn;
-        if constexpr (NBUF == 3) {
-            tn = t1;
-            const int t2 = t1 < ntile ? next_tile(t1) : ntile;
-            if (t2 < ntile) load(t2, FB);
-            t1 = t2;
-        } else {
-            tn = next_tile(t);
-            if (tn < ntile) load(tn, FB);
-        }
+        const int tn = next_tile(t);
+        if (tn < ntile) load(tn, CB ^ 1);
         const uint8_t* kb = smem + CB * BUF;
         const uint8_t* vb = kb + T::BYTES;
         // key acc_row(r, h) = 8 (r / 4) + 4 h + r % 4 of a 32-key half: after one
         // shift by 4 h every bit position is a constant
-        const bool partial = !(tflag.get(t) & 2);
-        const uint64_t bits = partial ? key_tile_bits(mrow, n, p.N, p.Lc, CONTIG, t * kKT, p.L) >> (4 * h) : ~0ull;
+        const bool partial = FULL ? false : !(tflag.get(t) & 2);
+        const uint64_t bits =
+            partial ? key_tile_bits(mrow, n, p.N, p.Lc, CONTIG, t * kKT, p.L) >> (4 * h) : ~0ull;
         // causal: key i of a chunk-aligned tile sits at position kp0 + i
         const int kp0 = (CAUSAL && CONTIG) ? ring_pos(t * kKT, n, p.N, p.Lc) : 0;
-        // two 32-key halves in turn, to bound the live registers
-#pragma unroll 1
-        for (int kb2 = 0; kb2 < 2; ++kb2) {
+        auto half = [&](int kb2) __attribute__((always_inline)) {
             // ---- S^T = K Q^T and dP^T - D = V dO^T - D for keys 32 kb2 .. +32
             f32x16 s, dp;
             {
@@ -271,25 +261,27 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 3 : 1) void rsa_bwd_dq(BwdParam
                     }
                 }
             }
-            if (bits != ~0ull) {
-                const uint32_t hb = (uint32_t)(bits >> (32 * kb2));
+            if constexpr (!FULL) {
+                if (bits != ~0ull) {
+                    const uint32_t hb = (uint32_t)(bits >> (32 * kb2));
 #pragma unroll
-                for (int r = 0; r < 16; ++r)
-                    if (!((hb >> (8 * (r >> 2) + (r & 3))) & 1u)) s[r] = -INFINITY;
-            }
-            if (CAUSAL && partial) {   // keys after this lane's row
-                const int rel = row - kp0 - 32 * kb2 - 4 * h;
+                    for (int r = 0; r < 16; ++r)
+                        if (!((hb >> (8 * (r >> 2) + (r & 3))) & 1u)) s[r] = -INFINITY;
+                }
+                if (CAUSAL && partial) {   // keys after this lane's row
+                    const int rel = row - kp0 - 32 * kb2 - 4 * h;
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int i = 8 * (r >> 2) + (r & 3);
-                    bool hide;
-                    if constexpr (CONTIG) {
-                        hide = i > rel;
-                    } else {
-                        const int vk = t * kKT + 32 * kb2 + 4 * h + i;
-                        hide = vk < p.L && ring_pos(vk, n, p.N, p.Lc) > row;
+                    for (int r = 0; r < 16; ++r) {
+                        const int i = 8 * (r >> 2) + (r & 3);
+                        bool hide;
+                        if constexpr (CONTIG) {
+                            hide = i > rel;
+                        } else {
+                            const int vk = t * kKT + 32 * kb2 + 4 * h + i;
+                            hide = vk < p.L && ring_pos(vk, n, p.N, p.Lc) > row;
+                        }
+                        if (hide) s[r] = -INFINITY;
                     }
-                    if (hide) s[r] = -INFINITY;
                 }
             }
             uint32_t pk[8];
@@ -307,6 +299,14 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 3 : 1) void rsa_bwd_dq(BwdParam
                 for (int db = 0; db < D / 32; ++db)
                     acc[db] = mfma_32x32x16_bf16(T::tfrag(kb, 32 * kb2 + 16 * hs, 32 * db), bfrag, acc[db]);
             }
+        };
+        if constexpr (FULL) {
+            half(0);
+            half(1);
+        } else {
+            // two 32-key halves in turn, to bound the live registers
+#pragma unroll 1
+            for (int kb2 = 0; kb2 < 2; ++kb2) half(kb2);
         }
         t = tn;
         return t >= ntile;
@@ -315,20 +315,10 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 3 : 1) void rsa_bwd_dq(BwdParam
     if (t < ntile) {
         using C0 = std::integral_constant<int, 0>;
         using C1 = std::integral_constant<int, 1>;
-        using C2 = std::integral_constant<int, 2>;
         load(t, 0);
-        if constexpr (NBUF == 3) {
-            if (t1 < ntile) load(t1, 1);
-            while (true) {
-                if (body(C0{})) break;
-                if (body(C1{})) break;
-                if (body(C2{})) break;
-            }
-        } else {
-            while (true) {
-                if (body(C0{})) break;
-                if (body(C1{})) break;
-            }
+        while (true) {
+            if (body(C0{})) break;
+            if (body(C1{})) break;
         }
     }
 
@@ -726,7 +716,9 @@ hipError_t launch_t(const BackwardCall& c, int stages, hipStream_t stream) {
         return hipSuccess;
     }
     if (stages & kBwdStageDq) {
-        if (contig && !p.causal)
+        if (contig && !p.causal && p.mask == nullptr)
+            hipLaunchKernelGGL((rsa_bwd_dq<D, true, false, false, true>), dim3(blocks), dim3(kThreads), 0, stream, p);
+        else if (contig && !p.causal)
             hipLaunchKernelGGL((rsa_bwd_dq<D, true, false>), dim3(blocks), dim3(kThreads), 0, stream, p);
         else if (!p.causal)
             hipLaunchKernelGGL((rsa_bwd_dq<D, false, false>), dim3(blocks), dim3(kThreads), 0, stream, p);
