@@ -108,13 +108,18 @@ __device__ __forceinline__ void load_rowvec(uint8_t* lds, const float* src, RowO
 // DROP: with dropout, dS = P o (Z o dP - D) for the forward's keep factors Z
 // (kept: 1 / (1 - p), dropped: 0); the dP accumulator then starts at
 // -D (1 - p), so that a kept weight takes acc / (1 - p) and a dropped one -D.
-// FULL: no key mask, no causal mask and chunk-aligned tiles, so every key
-// tile is whole and visible: no occupancy table is built or consulted, and
-// the two 32-key halves of a tile are unrolled (their LDS offsets become
-// constants of the read instructions).
+// FULL: no key mask and chunk-aligned tiles, so every key tile is whole: no
+// occupancy table is built or consulted, and the two 32-key halves of a tile
+// are unrolled (their LDS offsets become constants of the read
+// instructions). With the causal mask (FULL and CAUSAL, chunks a multiple
+// of 128 rows so that a workgroup's rows lie in one chunk) the visible tiles
+// are walked directly: in ring order the row's own chunk comes first, whose
+// tiles up to the workgroup's last row are visible (the last two of them
+// partly, masked per element), then the earlier chunks, whole; the later
+// chunks are hidden.
 template <int D, bool CONTIG, bool CAUSAL, bool DROP = false, bool FULL = false>
 __global__ __launch_bounds__(kThreads, D == 64 ? 3 : 1) void rsa_bwd_dq(BwdParams p) {
-    static_assert(!FULL || (CONTIG && !CAUSAL && !DROP), "whole tiles need chunk-aligned, unmasked ranges");
+    static_assert(!FULL || (CONTIG && !DROP), "whole tiles need chunk-aligned, unmasked ranges");
     using T = DirectTile<D>;
     constexpr int BUF = 2 * T::BYTES;   // K, V
     __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * BUF];
@@ -194,10 +199,18 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 3 : 1) void rsa_bwd_dq(BwdParam
             T::load(kb + T::BYTES, [&](int r) { return vh + off(r); });
         }
     };
+    // FULL and CAUSAL: tiles 0 .. lo/64 + 1 of the own chunk (lo = the
+    // workgroup's first row within it), then tiles tpc .. (n + 1) tpc - 1
+    const int tpc = p.Lc / kKT;
+    const int tdiag = (row0 - n * p.Lc) / kKT;               // first partly visible tile
+    const int tend = (FULL && CAUSAL) ? (n + 1) * tpc : ntile;
     auto next_tile = [&](int t) {
         ++t;
-        if constexpr (!FULL)
+        if constexpr (FULL && CAUSAL) {
+            if (t == tdiag + 2) t = tpc;
+        } else if constexpr (!FULL) {
             while (t < ntile && !(tflag.get(t) & 1)) ++t;
+        }
         return t;
     };
 
@@ -212,14 +225,14 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 3 : 1) void rsa_bwd_dq(BwdParam
         vm_wait<0>();
         bare_barrier();   // every wave's part of tile t landed, tile t-1 consumed
         const int tn = next_tile(t);
-        if (tn < ntile) load(tn, CB ^ 1);
+        if (tn < tend) load(tn, CB ^ 1);
         const uint8_t* kb = smem + CB * BUF;
         const uint8_t* vb = kb + T::BYTES;
         // key acc_row(r, h) = 8 (r / 4) + 4 h + r % 4 of a 32-key half: after one
         // shift by 4 h every bit position is a constant
-        const bool partial = FULL ? false : !(tflag.get(t) & 2);
+        const bool partial = FULL ? (CAUSAL && t >= tdiag && t < tpc) : !(tflag.get(t) & 2);
         const uint64_t bits =
-            partial ? key_tile_bits(mrow, n, p.N, p.Lc, CONTIG, t * kKT, p.L) >> (4 * h) : ~0ull;
+            (!FULL && partial) ? key_tile_bits(mrow, n, p.N, p.Lc, CONTIG, t * kKT, p.L) >> (4 * h) : ~0ull;
         // causal: key i of a chunk-aligned tile sits at position kp0 + i
         const int kp0 = (CAUSAL && CONTIG) ? ring_pos(t * kKT, n, p.N, p.Lc) : 0;
         auto half = [&](int kb2) __attribute__((always_inline)) {
@@ -261,8 +274,8 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 3 : 1) void rsa_bwd_dq(BwdParam
                     }
                 }
             }
-            if constexpr (!FULL) {
-                if (bits != ~0ull) {
+            if constexpr (!FULL || CAUSAL) {
+                if (!FULL && bits != ~0ull) {
                     const uint32_t hb = (uint32_t)(bits >> (32 * kb2));
 #pragma unroll
                     for (int r = 0; r < 16; ++r)
@@ -309,10 +322,10 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 3 : 1) void rsa_bwd_dq(BwdParam
             for (int kb2 = 0; kb2 < 2; ++kb2) half(kb2);
         }
         t = tn;
-        return t >= ntile;
+        return t >= tend;
     };
 
-    if (t < ntile) {
+    if (t < tend) {
         using C0 = std::integral_constant<int, 0>;
         using C1 = std::integral_constant<int, 1>;
         load(t, 0);
@@ -718,6 +731,8 @@ hipError_t launch_t(const BackwardCall& c, int stages, hipStream_t stream) {
     if (stages & kBwdStageDq) {
         if (contig && !p.causal && p.mask == nullptr)
             hipLaunchKernelGGL((rsa_bwd_dq<D, true, false, false, true>), dim3(blocks), dim3(kThreads), 0, stream, p);
+        else if (contig && p.causal && p.mask == nullptr && p.Lc % 128 == 0)
+            hipLaunchKernelGGL((rsa_bwd_dq<D, true, true, false, true>), dim3(blocks), dim3(kThreads), 0, stream, p);
         else if (contig && !p.causal)
             hipLaunchKernelGGL((rsa_bwd_dq<D, true, false>), dim3(blocks), dim3(kThreads), 0, stream, p);
         else if (!p.causal)

@@ -93,7 +93,9 @@ def test_causal_rank_share(oracle_lib, dtype, L, N, d):
     (512, 2, (400, 512)),    # chunks of 256, key padding
     (200, 5, (120, 200)),    # chunks of 40: every tile masked per element
     (130, 13, None),         # chunks of 10
-    (384, 3, None),
+    (384, 3, None),          # chunks of 128, no key mask: the table-free dQ
+    (1024, 4, None),         # chunks of 256: two workgroups per chunk, diagonal tiles at two offsets
+    (512, 1, None),          # one chunk
 ])
 def test_causal_backward_small_parity(oracle_lib, d, L, N, valid):
     dev = device()
@@ -123,6 +125,25 @@ def test_causal_long_sequence_sampled_rows(oracle_lib):
                                             x["v"][b:b + 1, h:h + 1], None, N=w.N, qpos=rows, causal=True)
         assert_parity(out[b, h, rows], want[0, 0], "bf16", f"causal long_seq b={b} h={h}")
         check_lse(lse[b, h, rows], want_lse[0, 0], "bf16", "causal long_seq")
+
+
+def test_causal_backward_long_sequence_one_head(oracle_lib):
+    """The long-sequence workload (B=2 H=12 L=8192 d=64 N=16, no key mask)
+    with the causal mask, the launch the causal bench times: dQ, dK and dV of
+    one head element by element against the oracle."""
+    w = rsa_inputs.WORKLOADS["long_seq"]
+    dev = device()
+    x = rsa_inputs.make_inputs(w.B, w.H, w.L, w.d, w.seed, w.dtype, with_dout=True)
+    q, k, v, g = (to_dev(x[n], "bf16", dev) for n in ("q", "k", "v", "dout"))
+    say("causal long_seq backward")
+    out, lse = rsa.forward(q, k, v, None, N=w.N, return_lse=True, causal=True)
+    dq, dk, dv = rsa.backward(q, k, v, out, g, lse, None, N=w.N, causal=True)
+    torch.cuda.synchronize()
+    b, h = 1, 5
+    sl = (slice(b, b + 1), slice(h, h + 1))
+    want = oracle_lib.backward(x["q"][sl], x["k"][sl], x["v"][sl], x["dout"][sl], None, N=w.N, causal=True)
+    for name, a, ref in zip(("dq", "dk", "dv"), (dq, dk, dv), want):
+        assert_parity(from_dev(a)[sl], ref, "bf16", f"causal long_seq {name} b={b} h={h}", grad=True)
 
 
 def test_causal_backward_workload_two_heads(oracle_lib):
