@@ -313,16 +313,21 @@ __global__ __launch_bounds__(kThreads) void rsa_fwd_f32(FwdParams p) {
 // the vector ALU. (A variant that overlapped the next tile's score MFMAs
 // with this tile's softmax inside one wave needed more registers, ran at
 // fewer waves per SIMD and was slower; so was three buffers at three waves.)
-// FULL: no key mask, no causal mask and chunk-aligned tiles, so every key
-// tile of the range is whole and visible: the occupancy table is not built
-// and the loop takes every tile without looking it up.
+// FULL: no key mask and chunk-aligned tiles, so every key tile of the range
+// is whole: the occupancy table is not built and the loop takes every tile
+// without looking it up. With the causal mask (FULL and CAUSAL: one group,
+// chunks and the rows' first position multiples of 128, so that a
+// workgroup's rows lie in one chunk) the visible tiles are walked directly:
+// in ring order the rows' own chunk comes first, whose tiles up to the
+// workgroup's last row are visible (the last two of them partly, masked per
+// element), then the earlier chunks, whole; the later chunks are hidden.
 // DROP: dropout of the normalised weights (the row sums count every weight;
 // dropped ones are zeroed in the packed bf16 operand of the PV product and
 // the output is scaled by 1 / (1 - p) at the end).
 template <int D, bool CONTIG, int QB, bool CAUSAL, bool FULL = false, bool DROP = false>
 __global__ __launch_bounds__(256 / QB, (D == 64 && QB == 1) ? 4 : 2)
 void rsa_fwd_bf16(FwdParams p) {
-    static_assert(!FULL || (CONTIG && !CAUSAL), "whole tiles need chunk-aligned, non-causal ranges");
+    static_assert(!FULL || CONTIG, "whole tiles need chunk-aligned ranges");
     static_assert(!DROP || (QB == 1 && !FULL), "dropout instances: one query block per wave, general tiles");
     // QB 32-row query blocks per wave; 128 query rows per workgroup either
     // way (4 waves x 32 rows, or 2 waves x 64 rows: each K and V^T fragment
@@ -438,10 +443,17 @@ void rsa_fwd_bf16(FwdParams p) {
             VTile::load(vbuf, [&](int r) { return vh + rowoff(r); });
         }
     };
+    // FULL and CAUSAL: tiles 0 .. lo/64 + 1 of the own chunk (lo = the
+    // workgroup's first row position within it), then tpc .. (n + 1) tpc - 1
+    const int tdiag = (qlo - n * p.Lc) / kKT;   // first partly visible tile
+    const int tend = (FULL && CAUSAL) ? (n + 1) * tpc : ntile;
     auto next_tile = [&](int t) {
         ++t;
-        if constexpr (!FULL)
+        if constexpr (FULL && CAUSAL) {
+            if (t == tdiag + 2) t = tpc;
+        } else if constexpr (!FULL) {
             while (t < ntile && !(tflag.get(t) & 1)) ++t;
+        }
         return t;
     };
 
@@ -451,7 +463,7 @@ void rsa_fwd_bf16(FwdParams p) {
         vm_wait<0>();
         bare_barrier();   // every wave's part of tile t landed, tile t-1 consumed
         const int tn = next_tile(t);
-        if (tn < ntile) load(tn, CB ^ 1);
+        if (tn < tend) load(tn, CB ^ 1);
         const uint8_t* kbuf = smem + CB * BUF;
         const uint8_t* vbuf = kbuf + KTile::BYTES;
 
@@ -481,20 +493,23 @@ void rsa_fwd_bf16(FwdParams p) {
                         s[qb][kb] = mfma_32x32x16_bf16(kf[kb][kq], qf[qb][kq], s[qb][kb]);
         }
         // ---- key mask and range tail (tiles not fully valid)
-        if (!FULL && !(tflag.get(t) & 2)) {
-            // key acc_row(r, h) = 8 (r / 4) + 4 h + r % 4 of block kb: after one
-            // shift by 4 h every bit position is a constant (no per-register
-            // masks held in registers)
-            const int tv0 = tile_v0(t);
-            const uint64_t bits = key_tile_bits(mrow, n, p.N, p.Lc, CONTIG, tv0, tile_end(tv0)) >> (4 * h);
+        const bool part = FULL ? (CAUSAL && t >= tdiag && t < tpc) : !(tflag.get(t) & 2);
+        if (part) {
+            if constexpr (!FULL) {
+                // key acc_row(r, h) = 8 (r / 4) + 4 h + r % 4 of block kb: after
+                // one shift by 4 h every bit position is a constant (no
+                // per-register masks held in registers)
+                const int tv0 = tile_v0(t);
+                const uint64_t bits = key_tile_bits(mrow, n, p.N, p.Lc, CONTIG, tv0, tile_end(tv0)) >> (4 * h);
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
+                for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-                for (int r = 0; r < 16; ++r)
-                    if (!((bits >> (32 * kb + 8 * (r >> 2) + (r & 3))) & 1ull)) {
+                    for (int r = 0; r < 16; ++r)
+                        if (!((bits >> (32 * kb + 8 * (r >> 2) + (r & 3))) & 1ull)) {
 #pragma unroll
-                        for (int qb = 0; qb < QB; ++qb) s[qb][kb][r] = -INFINITY;
-                    }
+                            for (int qb = 0; qb < QB; ++qb) s[qb][kb][r] = -INFINITY;
+                        }
+            }
             if constexpr (CAUSAL) {
                 // keys after this lane's query position; within a chunk-aligned
                 // tile key 32 kb + acc_row(r, h) sits at position kp0 plus that,
@@ -630,9 +645,9 @@ void rsa_fwd_bf16(FwdParams p) {
             }
         }
         t = tn;
-        return t >= ntile;
+        return t >= tend;
     };
-    if (t < ntile) {
+    if (t < tend) {
         using C0 = std::integral_constant<int, 0>;
         using C1 = std::integral_constant<int, 1>;
         load(t, 0);
@@ -782,6 +797,9 @@ hipError_t launch_t(const ForwardCall& c, hipStream_t stream) {
                                    stream, p);
         } else if (p.contiguous && !p.causal && p.mask == nullptr)
             hipLaunchKernelGGL((rsa_fwd_bf16<D, true, QB, false, true>), dim3((unsigned)total), block, 0, stream, p);
+        else if (p.contiguous && p.causal && p.mask == nullptr && c.groups == 1 && p.Lc % 128 == 0 &&
+                 c.q_pos0 % 128 == 0 && c.Lq % 128 == 0)
+            hipLaunchKernelGGL((rsa_fwd_bf16<D, true, QB, true, true>), dim3((unsigned)total), block, 0, stream, p);
         else if (p.contiguous && !p.causal)
             hipLaunchKernelGGL((rsa_fwd_bf16<D, true, QB, false>), dim3((unsigned)total), block, 0, stream, p);
         else if (!p.causal)

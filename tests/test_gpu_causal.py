@@ -40,6 +40,8 @@ def gpu_forward(x, dtype, N, dev):
     (130, 13, None),         # chunks of 10
     (1, 1, None),
     (384, 2, None),          # three query blocks in a chunk of 192
+    (1024, 4, None),         # chunks of 256, no key mask: the table-free walk, diagonal tiles at two offsets
+    (512, 1, None),          # one chunk
 ])
 def test_causal_forward_small_parity(oracle_lib, dtype, d, L, N, valid):
     dev = device()
