@@ -9,7 +9,8 @@
 //   dQ = dS K / sqrt(d),  dK = dS^T Q / sqrt(d),  dV = P^T dO.
 //
 // Three kernels, all deterministic (no atomics):
-//   rsa_bwd_pre   row statistics: -D_i and -lse_i * log2(e)       (HBM-bound)
+//   rsa_bwd_pre   row statistics: -D_i (times 1 - p with dropout) and
+//                 -lse_i * log2(e)                                  (HBM-bound)
 //   rsa_bwd_dq    query-stationary: a rank's query tile meets the key chunks
 //                 in ring order (as in the forward) and accumulates dQ;
 //                 recomputes S, P and dP (3 contractions)
@@ -71,7 +72,7 @@ template <int D>
 __global__ __launch_bounds__(kThreads) void rsa_bwd_pre(const uint16_t* __restrict__ o,
                                                         const uint16_t* __restrict__ dout,
                                                         const float* __restrict__ lse, float* __restrict__ stats,
-                                                        long long rows) {
+                                                        long long rows, float dmul) {
     constexpr int TPR = D / 8;   // lanes per row, 8 elements each
     const long long t = (long long)blockIdx.x * kThreads + threadIdx.x;
     const long long row = t / TPR;
@@ -86,7 +87,7 @@ __global__ __launch_bounds__(kThreads) void rsa_bwd_pre(const uint16_t* __restri
 #pragma unroll
     for (int off = TPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
     if (row < rows && c == 0) {
-        stats[row] = -acc;
+        stats[row] = -acc * dmul;
         const float l = lse[row];
         stats[rows + row] = l == -INFINITY ? -INFINITY : -l * kLog2e;   // a row without keys gets P = 0
     }
@@ -106,8 +107,10 @@ __device__ __forceinline__ void load_rowvec(uint8_t* lds, const float* src, RowO
 // tile S^T = K Q^T and dP^T = V dO^T (lane <-> query), then
 // dQ^T += K^T dS^T with K^T from the transposing read of the same K tile.
 // DROP: with dropout, dS = P o (Z o dP - D) for the forward's keep factors Z
-// (kept: 1 / (1 - p), dropped: 0); the dP accumulator then starts at
-// -D (1 - p), so that a kept weight takes acc / (1 - p) and a dropped one -D.
+// (kept: 1 / (1 - p), dropped: 0). The row statistic then holds -D (1 - p),
+// where the dP accumulator starts: dS (1 - p) = P acc for a kept weight and
+// P (-D (1 - p)) for a dropped one, and the common factor 1 / (1 - p) is
+// applied to dQ at the end.
 // FULL: no key mask and chunk-aligned tiles, so every key tile is whole: no
 // occupancy table is built or consulted, and the two 32-key halves of a tile
 // are unrolled (their LDS offsets become constants of the read
@@ -168,7 +171,7 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 3 : 1) void rsa_bwd_dq(BwdParam
     // tail rows get P = 0 through nl2 = -inf
     const float nD = row_ok ? p.stats[(size_t)bh * p.L + row] : 0.0f;
     const float nl2 = row_ok ? p.stats[rows_all + (size_t)bh * p.L + row] : -INFINITY;
-    const float nD0 = DROP ? nD / p.drop.scale : nD;   // the dP accumulator's start
+    const float nD0 = nD;   // the dP accumulator's start
 
     f32x16 acc[D / 32];
 #pragma unroll
@@ -264,13 +267,13 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 3 : 1) void rsa_bwd_dq(BwdParam
                     const u32x4 x = dropout_bytes(p.drop, jb, h, row, bh);
 #pragma unroll
                     for (int r = 0; r < 16; ++r)
-                        dp[r] = ((x[r >> 2] >> (8 * (r & 3))) & 0xffu) >= p.drop.p8 ? dp[r] * p.drop.scale : nD;
+                        dp[r] = ((x[r >> 2] >> (8 * (r & 3))) & 0xffu) >= p.drop.p8 ? dp[r] : nD;
                 } else {
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
                         const int vk = t * kKT + 32 * kb2 + acc_row(r, h);
                         const bool keep = vk >= p.L || dropout_keep(p.drop, row, ring_pos(vk, n, p.N, p.Lc), bh);
-                        dp[r] = keep ? dp[r] * p.drop.scale : nD;
+                        dp[r] = keep ? dp[r] : nD;
                     }
                 }
             }
@@ -337,12 +340,13 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 3 : 1) void rsa_bwd_dq(BwdParam
 
     if (row_ok) {
         uint16_t* out = p.dq + hoff + (size_t)row * D;
+        const float qs = DROP ? p.scale * p.drop.scale : p.scale;   // dropout: the kept weights' 1 / (1 - p)
 #pragma unroll
         for (int db = 0; db < D / 32; ++db)
 #pragma unroll
             for (int r4 = 0; r4 < 4; ++r4) {
-                const u32x2 w = {pack_bf16x2(acc[db][4 * r4] * p.scale, acc[db][4 * r4 + 1] * p.scale),
-                                 pack_bf16x2(acc[db][4 * r4 + 2] * p.scale, acc[db][4 * r4 + 3] * p.scale)};
+                const u32x2 w = {pack_bf16x2(acc[db][4 * r4] * qs, acc[db][4 * r4 + 1] * qs),
+                                 pack_bf16x2(acc[db][4 * r4 + 2] * qs, acc[db][4 * r4 + 3] * qs)};
                 *reinterpret_cast<u32x2*>(out + 32 * db + 8 * r4 + 4 * h) = w;
             }
     }
@@ -362,8 +366,9 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 3 : 1) void rsa_bwd_dq(BwdParam
 // the keep bytes are exchanged through LDS: per query tile each lane draws
 // the two counters of one query row (the wave's 32 keys are one 32-key
 // block, two halves), writes their 32 bytes into the wave's table, and each
-// lane then reads its key's byte for its 32 rows. dV takes P Z, and dS =
-// P (Z dP - D) as in the dQ kernel.
+// lane then reads its key's byte for its 32 rows. dV accumulates P over the
+// kept weights and dK the dS (1 - p) of the dQ kernel; both take the factor
+// 1 / (1 - p) at the end.
 template <int D, bool CONTIG, bool CAUSAL, bool DROP = false>
 __global__ __launch_bounds__(kThreads, D == 64 ? ((CAUSAL || DROP) ? 2 : 3) : 1) void rsa_bwd_dkdv(BwdParams p) {
     using T = DirectTile<D>;
@@ -525,7 +530,7 @@ __global__ __launch_bounds__(kThreads, D == 64 ? ((CAUSAL || DROP) ? 2 : 3) : 1)
                 for (int r4 = 0; r4 < 4; ++r4) {   // dP accumulators start at -D of their rows
                     const f32x4 d4 = *reinterpret_cast<const f32x4*>(nDs + 32 * qb2 + 8 * r4 + 4 * h);
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) dp[4 * r4 + e] = DROP ? d4[e] / p.drop.scale : d4[e];
+                    for (int e = 0; e < 4; ++e) dp[4 * r4 + e] = d4[e];
                 }
 #pragma unroll
                 for (int r = 0; r < 16; ++r) s[r] = 0.0f;
@@ -573,8 +578,8 @@ __global__ __launch_bounds__(kThreads, D == 64 ? ((CAUSAL || DROP) ? 2 : 3) : 1)
                         const int r = 4 * r4 + e;
                         const bool keep = ((kw[e] >> (8 * (j & 3))) & 0xffu) >= p.drop.p8;
                         const float pr = fast_exp2(fmaf(s[r], p.sl2, l4[e]));
-                        pv[e] = keep ? pr * p.drop.scale : 0.0f;
-                        dsv[e] = pr * (keep ? dp[r] * p.drop.scale : d4[e]);
+                        pv[e] = keep ? pr : 0.0f;
+                        dsv[e] = pr * (keep ? dp[r] : d4[e]);
                     }
                 } else {
 #pragma unroll
@@ -635,8 +640,9 @@ __global__ __launch_bounds__(kThreads, D == 64 ? ((CAUSAL || DROP) ? 2 : 3) : 1)
 
     if (key_in) {
         // a padded key's lane accumulated only into its own columns; it is 0
-        const float sk = key_ok ? p.scale : 0.0f;
-        const float sv = key_ok ? 1.0f : 0.0f;
+        const float zs = DROP ? p.drop.scale : 1.0f;   // dropout: the kept weights' 1 / (1 - p)
+        const float sk = key_ok ? p.scale * zs : 0.0f;
+        const float sv = key_ok ? zs : 0.0f;
         uint16_t* okk = p.dk + hoff + (size_t)key * D;
         uint16_t* ovv = p.dv + hoff + (size_t)key * D;
 #pragma unroll
@@ -685,6 +691,7 @@ BwdParams make_params(const BackwardCall& c) {
     p.drop.seed_hi = (uint32_t)(c.drop_seed >> 32);
     p.drop.offset = c.drop_offset;
     p.drop.scale = (float)(256.0 / (256.0 - (double)c.drop_p8));
+    p.drop.keep = (float)((256.0 - (double)c.drop_p8) / 256.0);
     return p;
 }
 
@@ -696,7 +703,7 @@ hipError_t launch_t(const BackwardCall& c, int stages, hipStream_t stream) {
     if (stages & kBwdStagePre) {
         const long long threads = rows * (D / 8);
         hipLaunchKernelGGL((rsa_bwd_pre<D>), dim3((unsigned)((threads + kThreads - 1) / kThreads)), dim3(kThreads), 0,
-                           stream, p.o, p.dout, p.lse, p.stats, rows);
+                           stream, p.o, p.dout, p.lse, p.stats, rows, p.drop.p8 != 0u ? p.drop.keep : 1.0f);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }

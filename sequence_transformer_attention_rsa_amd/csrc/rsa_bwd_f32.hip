@@ -336,6 +336,7 @@ hipError_t launch_t(const BackwardCall& c, int stages, hipStream_t stream) {
     p.drop.seed_hi = (uint32_t)(c.drop_seed >> 32);
     p.drop.offset = c.drop_offset;
     p.drop.scale = (float)(256.0 / (256.0 - (double)c.drop_p8));
+    p.drop.keep = (float)((256.0 - (double)c.drop_p8) / 256.0);
     const long long rows = (long long)p.BH * c.L;
     if (stages & kBwdStagePre) {
         const long long threads = rows * (D / 4);

@@ -103,6 +103,7 @@ struct Dropout {
     uint32_t p8;       // 0: no dropout
     uint32_t seed_lo, seed_hi, offset;
     float scale;       // 256 / (256 - p8)
+    float keep;        // (256 - p8) / 256, exact
 };
 
 // The 16 bytes of the counter of (key block jb = j / 32, half hh = bit 2 of j, query i, head bh).

@@ -770,6 +770,7 @@ hipError_t launch_t(const ForwardCall& c, hipStream_t stream) {
     p.drop.seed_hi = (uint32_t)(c.drop_seed >> 32);
     p.drop.offset = c.drop_offset;
     p.drop.scale = (float)(256.0 / (256.0 - (double)c.drop_p8));
+    p.drop.keep = (float)((256.0 - (double)c.drop_p8) / 256.0);
     if (c.groups > 1) {
         p.part_o = c.part;
         p.part_ml = c.part + (size_t)c.groups * p.BH * c.Lq * D;
