@@ -323,12 +323,14 @@ __global__ __launch_bounds__(kThreads) void rsa_fwd_f32(FwdParams p) {
 // element), then the earlier chunks, whole; the later chunks are hidden.
 // DROP: dropout of the normalised weights (the row sums count every weight;
 // dropped ones are zeroed in the packed bf16 operand of the PV product and
-// the output is scaled by 1 / (1 - p) at the end).
+// the output is scaled by 1 / (1 - p) at the end). The dropout instances run
+// at three waves per SIMD: the keep-decision generator does not fit 128
+// registers (11-16 of them went to scratch at four waves).
 template <int D, bool CONTIG, int QB, bool CAUSAL, bool FULL = false, bool DROP = false>
-__global__ __launch_bounds__(256 / QB, (D == 64 && QB == 1) ? 4 : 2)
+__global__ __launch_bounds__(256 / QB, (D == 64 && QB == 1) ? (DROP ? 3 : 4) : 2)
 void rsa_fwd_bf16(FwdParams p) {
     static_assert(!FULL || CONTIG, "whole tiles need chunk-aligned ranges");
-    static_assert(!DROP || (QB == 1 && !FULL), "dropout instances: one query block per wave, general tiles");
+    static_assert(!DROP || QB == 1, "dropout instances: one query block per wave");
     // QB 32-row query blocks per wave; 128 query rows per workgroup either
     // way (4 waves x 32 rows, or 2 waves x 64 rows: each K and V^T fragment
     // read from LDS then feeds two MFMAs).
@@ -784,7 +786,10 @@ hipError_t launch_t(const ForwardCall& c, hipStream_t stream) {
         constexpr int QB = 1;
         const dim3 block(kWave * 4 / QB);
         if (p.drop.p8 != 0u) {
-            if (p.contiguous && !p.causal)
+            if (p.contiguous && !p.causal && p.mask == nullptr)
+                hipLaunchKernelGGL((rsa_fwd_bf16<D, true, QB, false, true, true>), dim3((unsigned)total), block, 0,
+                                   stream, p);
+            else if (p.contiguous && !p.causal)
                 hipLaunchKernelGGL((rsa_fwd_bf16<D, true, QB, false, false, true>), dim3((unsigned)total), block, 0,
                                    stream, p);
             else if (!p.causal)
