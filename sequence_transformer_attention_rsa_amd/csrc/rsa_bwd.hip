@@ -110,19 +110,20 @@ __device__ __forceinline__ void load_rowvec(uint8_t* lds, const float* src, RowO
 // (kept: 1 / (1 - p), dropped: 0). The row statistic then holds -D (1 - p),
 // where the dP accumulator starts: dS (1 - p) = P acc for a kept weight and
 // P (-D (1 - p)) for a dropped one, and the common factor 1 / (1 - p) is
-// applied to dQ at the end.
-// FULL: no key mask and chunk-aligned tiles, so every key tile is whole: no
-// occupancy table is built or consulted, and the two 32-key halves of a tile
-// are unrolled (their LDS offsets become constants of the read
-// instructions). With the causal mask (FULL and CAUSAL, chunks a multiple
+// applied to dQ at the end. The dropout instances run at two waves per SIMD
+// (at three, the keep-decision generator pushed 14 registers into scratch).
+// FULL (with or without dropout): no key mask and chunk-aligned tiles, so
+// every key tile is whole: no occupancy table is built or consulted, and the
+// two 32-key halves of a tile are unrolled (their LDS offsets become
+// constants of the read instructions). With the causal mask (FULL and CAUSAL, chunks a multiple
 // of 128 rows so that a workgroup's rows lie in one chunk) the visible tiles
 // are walked directly: in ring order the row's own chunk comes first, whose
 // tiles up to the workgroup's last row are visible (the last two of them
 // partly, masked per element), then the earlier chunks, whole; the later
 // chunks are hidden.
 template <int D, bool CONTIG, bool CAUSAL, bool DROP = false, bool FULL = false>
-__global__ __launch_bounds__(kThreads, D == 64 ? 3 : 1) void rsa_bwd_dq(BwdParams p) {
-    static_assert(!FULL || (CONTIG && !DROP), "whole tiles need chunk-aligned, unmasked ranges");
+__global__ __launch_bounds__(kThreads, D == 64 ? (DROP ? 2 : 3) : 1) void rsa_bwd_dq(BwdParams p) {
+    static_assert(!FULL || CONTIG, "whole tiles need chunk-aligned, unmasked ranges");
     using T = DirectTile<D>;
     constexpr int BUF = 2 * T::BYTES;   // K, V
     __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * BUF];
@@ -710,7 +711,9 @@ hipError_t launch_t(const BackwardCall& c, int stages, hipStream_t stream) {
     const unsigned blocks = (unsigned)((long long)p.nt * p.BH);
     if (p.drop.p8 != 0u) {
         if (stages & kBwdStageDq) {
-            if (contig && !p.causal)
+            if (contig && !p.causal && p.mask == nullptr)
+                hipLaunchKernelGGL((rsa_bwd_dq<D, true, false, true, true>), dim3(blocks), dim3(kThreads), 0, stream, p);
+            else if (contig && !p.causal)
                 hipLaunchKernelGGL((rsa_bwd_dq<D, true, false, true>), dim3(blocks), dim3(kThreads), 0, stream, p);
             else if (!p.causal)
                 hipLaunchKernelGGL((rsa_bwd_dq<D, false, false, true>), dim3(blocks), dim3(kThreads), 0, stream, p);
