@@ -41,6 +41,7 @@ def gpu_forward(x, dtype, N, dev):
     (1, 1, None),
     (384, 2, None),          # three query blocks in a chunk of 192
     (1024, 4, None),         # chunks of 256, no key mask: the table-free walk, diagonal tiles at two offsets
+    (1536, 4, None),         # chunks of 384: diagonal tiles at three offsets
     (512, 1, None),          # one chunk
 ])
 def test_causal_forward_small_parity(oracle_lib, dtype, d, L, N, valid):
@@ -97,6 +98,7 @@ def test_causal_rank_share(oracle_lib, dtype, L, N, d):
     (130, 13, None),         # chunks of 10
     (384, 3, None),          # chunks of 128, no key mask: the table-free dQ
     (1024, 4, None),         # chunks of 256: two workgroups per chunk, diagonal tiles at two offsets
+    (1536, 4, None),         # chunks of 384: diagonal tiles at three offsets
     (512, 1, None),          # one chunk
 ])
 def test_causal_backward_small_parity(oracle_lib, d, L, N, valid):
