@@ -90,6 +90,31 @@ def test_causal_rank_share(oracle_lib, dtype, L, N, d):
         check_lse(lse.cpu().numpy().astype(np.float64), want_lse, dtype, f"causal rank {rank}")
 
 
+@pytest.mark.parametrize("B,H,L,N,rank", [
+    (1, 2, 1024, 1, 0),        # one chunk: the share is the whole sequence
+    (1, 8, 16384, 2, 1),       # 512 query tiles: one ring-step group, rows from position 8192
+])
+def test_causal_rank_share_unmasked_one_group(oracle_lib, B, H, L, N, rank):
+    """A rank's share without a key mask launched as one ring-step group
+    takes the forward's table-free causal walk; the oracle checks 96 sampled
+    rows of every head."""
+    dev = device()
+    d = 64
+    x = inputs(B, H, L, d, seed=L + N + rank, dtype="bf16")
+    Lc = L // N
+    rows = np.arange(rank * Lc, (rank + 1) * Lc)
+    k, v = to_dev(x["k"], "bf16", dev), to_dev(x["v"], "bf16", dev)
+    say("causal rank share unmasked", B, H, L, N, rank)
+    out, lse = rsa.forward_rank(to_dev(x["q"][:, :, rows], "bf16", dev), k, v, None, N=N, rank=rank,
+                                return_lse=True, causal=True)
+    torch.cuda.synchronize()
+    pick = np.sort(np.random.default_rng(L + rank).choice(Lc, 96, replace=False))
+    want, want_lse = oracle_lib.forward(x["q"][:, :, rows[pick]], x["k"], x["v"], None, N=N, qpos=rows[pick],
+                                        causal=True)
+    assert_parity(from_dev(out)[:, :, pick], want, "bf16", f"causal unmasked rank {rank}")
+    check_lse(lse.cpu().numpy().astype(np.float64)[:, :, pick], want_lse, "bf16", f"causal unmasked rank {rank}")
+
+
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("L,N,valid", [
     (256, 4, None),          # chunks of 64: 128-key workgroups span two chunks
