@@ -24,11 +24,7 @@ constexpr int kGT = 128;                         // output tile: 128 rows x 128 
 constexpr int kGK = 64;                          // contraction step
 using GTile = DirectTile<64>;                    // [64 rows][64 bf16], 8 KB, swizzled
 constexpr int kStageBytes = 4 * GTile::BYTES;    // A rows 0-63, 64-127; W rows 0-63, 64-127
-#ifndef RSA_GEMM_NBUF
-#define RSA_GEMM_NBUF 2
-#endif
-constexpr int kGemmBuf = RSA_GEMM_NBUF;          // stage buffers: kGemmBuf - 1 steps in flight
-static_assert(kGemmBuf >= 2 && kGemmBuf <= 4, "stage buffers");
+constexpr int kGemmBuf = 2;                      // stage buffers: one step in flight
 constexpr int kStagePitch = kGT * 4 + 16;        // fp32 epilogue row, bytes (16 B pad)
 constexpr int kGemmLds = (kGemmBuf * kStageBytes > kGT * kStagePitch) ? kGemmBuf * kStageBytes
                                                                        : kGT * kStagePitch;
@@ -524,10 +520,6 @@ __global__ __launch_bounds__(kThreads) void rsa_layernorm_bf16(const uint16_t* _
     }
 }
 
-#ifndef RSA_GEMM_BIG
-#define RSA_GEMM_BIG 1
-#endif
-
 // Compute units of the current device (cached per device; threads that
 // race on the first call store the same value).
 int device_cus() {
@@ -549,7 +541,7 @@ hipError_t launch_gemm_t(const GemmParams& p0, hipStream_t stream) {
     // straddle a tile), else 128x128. Between 256 and 192 columns, the one
     // with the shorter schedule: rounds of one workgroup per CU times the
     // tile's share of a 256x256 tile's work (ties go to 256).
-    auto fits = [&](int nt) { return RSA_GEMM_BIG && p.N % nt == 0 && (EPI != kEpiQkv || p.E % nt == 0); };
+    auto fits = [&](int nt) { return p.N % nt == 0 && (EPI != kEpiQkv || p.E % nt == 0); };
     const long long mt = (p.M + kBT - 1) / kBT, cus = device_cus();
     auto cost = [&](int nt) { return (mt * (p.N / nt) + cus - 1) / cus * nt; };
     int nt = 0;
