@@ -425,7 +425,7 @@ def main():
                          device=dev)
     bws = None
     one_call_bwd = causal or dropout is not None   # the backward's stages have no causal or dropout form
-    if do_bwd and one_call_bwd:
+    if do_bwd:
         bws = torch.empty(rsa.backward_workspace_bytes(w.B, w.H, w.L, w.d, w.N), dtype=torch.uint8, device=dev)
 
     if one_call_bwd:
@@ -433,7 +433,10 @@ def main():
     else:
         names = ["forward"] + (["bwd_preprocess", "bwd_dq", "bwd_dkdv"] if do_bwd else [])
 
-    def step(ev=None):
+    def step(ev=None, stages=True):
+        # stages: the backward as its three stage calls, one kernel each, so
+        # that events between them time each kernel; else one rsa_backward
+        # call, which forms the row statistics inside the dQ kernel
         def mark(i):
             if ev is not None:
                 ev[i].record()
@@ -446,7 +449,7 @@ def main():
         else:
             rsa.forward(q, k, v, mask, N=w.N, out=out, lse=lse, causal=causal, dropout=dropout)
         mark(1)
-        if do_bwd and one_call_bwd:
+        if do_bwd and (one_call_bwd or not stages):
             rsa.backward(q, k, v, out, g, lse, mask, N=w.N, dq=dq, dk=dk, dv=dv, workspace=bws, causal=causal,
                          dropout=dropout)
             mark(2)
@@ -467,25 +470,29 @@ def main():
         del src, dst
 
     for _ in range(args.warmup):
-        step()
+        step(stages=False)
     torch.cuda.synchronize()
 
-    # The timed region: K steps with nothing recorded between the calls (an
-    # event between two kernels costs a few microseconds of its own).
+    # The timed region: K steps of the one-call API with nothing recorded
+    # between the calls (an event between two kernels costs a few
+    # microseconds of its own).
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_wall = time.perf_counter()
     start.record()
     for s in range(args.steps):
-        step()
+        step(stages=False)
     stop.record()
     torch.cuda.synchronize()
     t_wall = time.perf_counter() - t_wall
     ms_total = start.elapsed_time(stop)
     ms_per_step = ms_total / args.steps
-    # Per-call times: a second pass of K steps with HIP events between the calls.
+    # Per-call times: a second pass of K steps with HIP events between the
+    # calls, the backward as its stages where it has them.
     nev = len(names) + 1
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(args.steps)]
+    for _ in range(2):
+        step()
     for s in range(args.steps):
         step(events[s])
     torch.cuda.synchronize()
@@ -578,6 +585,10 @@ def main():
                        if do_bwd else None),
         "step_frac_peak": value / peak,
         "kernels": per_kernel,
+        "backward_calls": None if not do_bwd else {
+            "timed_region": "rsa_backward",
+            "kernels_pass": "rsa_backward" if one_call_bwd else
+            "rsa_backward_preprocess + rsa_backward_dq + rsa_backward_dkdv"},
         "roofline": roofline,
         "wall_s_timed_region": t_wall,
         "gpu": torch.cuda.get_device_name(dev),

@@ -241,7 +241,9 @@ int rsa_backward_noalloc(const void* q, const void* k, const void* v, const void
  * The three stages rsa_backward runs, for callers that schedule them
  * separately (on several devices dQ stays with its rank while the dK/dV
  * contributions travel the ring back to the key chunk's owner; proposed-
- * method section). Same conventions and validation as rsa_backward.
+ * method section). Same conventions and validation as rsa_backward. (In
+ * rsa_backward with RSA_BF16 the dQ kernel forms stage 1's statistics
+ * itself, one launch fewer; they are the same bits.)
  *
  * Stage 1: row statistics of the forward, rowstats fp32 [2][B,H,L]:
  *   rowstats[0][b,h,i] = -sum_x dout[b,h,i,x] * out[b,h,i,x]

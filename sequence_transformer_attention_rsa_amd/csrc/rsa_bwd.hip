@@ -56,6 +56,8 @@ struct BwdParams {
     float scale;               // 1 / sqrt(d)
     int causal;                // the query at position i sees keys at positions <= i only
     Dropout drop;              // the forward's dropout (drop.p8 == 0: none)
+    float dmul;                // -D is stored times dmul (1, or 1 - p with dropout)
+    int pre_in_dq;             // the dQ kernel computes and stores the row statistics itself
 };
 
 // Sequence position of the u-th query row that key chunk c meets: ring step
@@ -68,6 +70,15 @@ __device__ __forceinline__ int ring_pos_rev(int u, int c, int N, int Lc) {
 }
 
 // --------------------------------------------------------- row statistics ---
+// dO . O over 8 elements (one 16-byte chunk of each row), in the order both
+// the preprocess and the dQ kernel that can replace it use.
+__device__ __forceinline__ float dot8_bf16(const u32x4& a, const u32x4& g) {
+    float acc = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc += bf16_lo(a[e]) * bf16_lo(g[e]) + bf16_hi(a[e]) * bf16_hi(g[e]);
+    return acc;
+}
+
 template <int D>
 __global__ __launch_bounds__(kThreads) void rsa_bwd_pre(const uint16_t* __restrict__ o,
                                                         const uint16_t* __restrict__ dout,
@@ -81,8 +92,7 @@ __global__ __launch_bounds__(kThreads) void rsa_bwd_pre(const uint16_t* __restri
     if (row < rows) {
         const u32x4 a = *reinterpret_cast<const u32x4*>(o + row * D + 8 * c);
         const u32x4 g = *reinterpret_cast<const u32x4*>(dout + row * D + 8 * c);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) acc += bf16_lo(a[e]) * bf16_lo(g[e]) + bf16_hi(a[e]) * bf16_hi(g[e]);
+        acc = dot8_bf16(a, g);
     }
 #pragma unroll
     for (int off = TPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
@@ -170,8 +180,37 @@ __global__ __launch_bounds__(kThreads, D == 64 ? (DROP ? 2 : 3) : 1) void rsa_bw
         gf[ks] = g;
     }
     // tail rows get P = 0 through nl2 = -inf
-    const float nD = row_ok ? p.stats[(size_t)bh * p.L + row] : 0.0f;
-    const float nl2 = row_ok ? p.stats[rows_all + (size_t)bh * p.L + row] : -INFINITY;
+    float nD, nl2;
+    if (p.pre_in_dq) {
+        // The preprocess for this lane's row, here: this lane holds chunks
+        // 2 ks + h of dO (16 bytes each); their dot products with O are
+        // combined in the order of the preprocess's lane reduction (chunks c
+        // and c + TPR/2 first, ..., the two lane halves last), so the
+        // statistics are the same bits.
+        float part[D / 16];
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks) {
+            u32x4 a = {0u, 0u, 0u, 0u};
+            if (row_ok) a = *reinterpret_cast<const u32x4*>(p.o + hoff + (size_t)row * D + 16 * ks + 8 * h);
+            part[ks] = dot8_bf16(a, gf[ks]);
+        }
+#pragma unroll
+        for (int m = D / 32; m >= 1; m >>= 1)
+#pragma unroll
+            for (int ks = 0; ks < m; ++ks) part[ks] = part[ks] + part[ks + m];
+        const float other = __shfl_xor(part[0], 32);
+        const float dsum = h == 0 ? part[0] + other : other + part[0];
+        const float l = row_ok ? p.lse[(size_t)bh * p.L + row] : -INFINITY;
+        nD = row_ok ? -dsum * p.dmul : 0.0f;
+        nl2 = l == -INFINITY ? -INFINITY : -l * kLog2e;
+        if (row_ok && h == 0) {
+            p.stats[(size_t)bh * p.L + row] = nD;
+            p.stats[rows_all + (size_t)bh * p.L + row] = nl2;
+        }
+    } else {
+        nD = row_ok ? p.stats[(size_t)bh * p.L + row] : 0.0f;
+        nl2 = row_ok ? p.stats[rows_all + (size_t)bh * p.L + row] : -INFINITY;
+    }
     const float nD0 = nD;   // the dP accumulator's start
 
     f32x16 acc[D / 32];
@@ -693,18 +732,23 @@ BwdParams make_params(const BackwardCall& c) {
     p.drop.offset = c.drop_offset;
     p.drop.scale = (float)(256.0 / (256.0 - (double)c.drop_p8));
     p.drop.keep = (float)((256.0 - (double)c.drop_p8) / 256.0);
+    p.dmul = c.drop_p8 != 0 ? p.drop.keep : 1.0f;
+    p.pre_in_dq = 0;
     return p;
 }
 
 template <int D>
 hipError_t launch_t(const BackwardCall& c, int stages, hipStream_t stream) {
-    const BwdParams p = make_params(c);
+    BwdParams p = make_params(c);
     const long long rows = (long long)p.BH * c.L;
     const bool contig = (p.Lc % kKT) == 0;
-    if (stages & kBwdStagePre) {
+    // Both stages in one call: the dQ kernel, which holds each row's dO
+    // anyway, forms the row statistics itself (one launch less).
+    p.pre_in_dq = (stages & kBwdStagePre) && (stages & kBwdStageDq) ? 1 : 0;
+    if ((stages & kBwdStagePre) && !p.pre_in_dq) {
         const long long threads = rows * (D / 8);
         hipLaunchKernelGGL((rsa_bwd_pre<D>), dim3((unsigned)((threads + kThreads - 1) / kThreads)), dim3(kThreads), 0,
-                           stream, p.o, p.dout, p.lse, p.stats, rows, p.drop.p8 != 0u ? p.drop.keep : 1.0f);
+                           stream, p.o, p.dout, p.lse, p.stats, rows, p.dmul);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
