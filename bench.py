@@ -424,11 +424,11 @@ def main():
         ws = torch.empty(rsa.forward_twopass_workspace_bytes(w.B, w.H, w.L, w.d, w.N), dtype=torch.uint8,
                          device=dev)
     bws = None
-    one_call_bwd = causal or dropout is not None   # the backward's stages have no causal or dropout form
+    has_stages = not (causal or dropout is not None)   # the stage entry points have no causal or dropout form
     if do_bwd:
         bws = torch.empty(rsa.backward_workspace_bytes(w.B, w.H, w.L, w.d, w.N), dtype=torch.uint8, device=dev)
 
-    if one_call_bwd:
+    if not has_stages:
         names = ["forward"] + (["backward"] if do_bwd else [])
     else:
         names = ["forward"] + (["bwd_preprocess", "bwd_dq", "bwd_dkdv"] if do_bwd else [])
@@ -449,7 +449,7 @@ def main():
         else:
             rsa.forward(q, k, v, mask, N=w.N, out=out, lse=lse, causal=causal, dropout=dropout)
         mark(1)
-        if do_bwd and (one_call_bwd or not stages):
+        if do_bwd and (not has_stages or not stages):
             rsa.backward(q, k, v, out, g, lse, mask, N=w.N, dq=dq, dk=dk, dv=dv, workspace=bws, causal=causal,
                          dropout=dropout)
             mark(2)
@@ -553,7 +553,7 @@ def main():
             "peak": peak,
             "unit": "TFLOP/s",
             "frac": achieved / peak,
-            "traffic": None if one_call_bwd else recorded_traffic(w.name, dominant),
+            "traffic": None if not has_stages else recorded_traffic(w.name, dominant),
             "traffic_unit": "bytes per launch (calibrated FETCH_SIZE + WRITE_SIZE)",
             "avg_ms": per_kernel[dominant]["avg_ms"],
             "flops_per_launch": credited[dominant],
@@ -587,7 +587,7 @@ def main():
         "kernels": per_kernel,
         "backward_calls": None if not do_bwd else {
             "timed_region": "rsa_backward",
-            "kernels_pass": "rsa_backward" if one_call_bwd else
+            "kernels_pass": "rsa_backward" if not has_stages else
             "rsa_backward_preprocess + rsa_backward_dq + rsa_backward_dkdv"},
         "roofline": roofline,
         "wall_s_timed_region": t_wall,

@@ -13,7 +13,9 @@
 //                 -lse_i * log2(e)                                  (HBM-bound)
 //   rsa_bwd_dq    query-stationary: a rank's query tile meets the key chunks
 //                 in ring order (as in the forward) and accumulates dQ;
-//                 recomputes S, P and dP (3 contractions)
+//                 recomputes S, P and dP (3 contractions); when one call
+//                 asks for the statistics and dQ together it forms the
+//                 statistics itself and rsa_bwd_pre is not launched
 //   rsa_bwd_dkdv  key-stationary: a key chunk meets every query chunk in the
 //                 order the ring delivers them (query chunk (c + t) mod N at
 //                 step t) and accumulates dK and dV -- the sum over query
