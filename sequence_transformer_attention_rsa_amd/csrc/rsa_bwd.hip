@@ -142,10 +142,18 @@ __global__ __launch_bounds__(kThreads, D == 64 ? (DROP ? 2 : 3) : 1) void rsa_bw
     __shared__ uint8_t tflag_bytes[FULL ? 4 : kFwdMaxTiles / 4];
     const TileTable tflag{tflag_bytes};
 
-    const int lid = xcd_remap(blockIdx.x, p.nt * p.BH);
-    // causal: the last query tiles see the most keys; dispatch them first
-    const int qt = CAUSAL ? p.nt - 1 - lid % p.nt : lid % p.nt;
-    const int bh = lid / p.nt, b = bh / p.H;
+    int qt, bh;
+    if constexpr (CAUSAL) {
+        // the last query tiles see the most keys: dispatch them first
+        int rank;
+        causal_order(blockIdx.x, p.nt, p.BH, rank, bh);
+        qt = p.nt - 1 - rank;
+    } else {
+        const int lid = xcd_remap(blockIdx.x, p.nt * p.BH);
+        qt = lid % p.nt;
+        bh = lid / p.nt;
+    }
+    const int b = bh / p.H;
     const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
     const int j = lane & 31, h = lane >> 5;
     const int row0 = qt * 128;
@@ -421,8 +429,16 @@ __global__ __launch_bounds__(kThreads, D == 64 ? ((CAUSAL || DROP) ? 2 : 3) : 1)
     // per wave: keep words [half hh][word w][row u]
     __shared__ __attribute__((aligned(16))) uint32_t keep_tab[DROP ? 4 * 2 * 4 * kKT : 1];
 
-    const int lid = xcd_remap(blockIdx.x, p.nt * p.BH);
-    const int kt = lid % p.nt, bh = lid / p.nt, b = bh / p.H;
+    int kt, bh;
+    if constexpr (CAUSAL) {
+        // the first key tiles are seen by the most rows: dispatch them first
+        causal_order(blockIdx.x, p.nt, p.BH, kt, bh);
+    } else {
+        const int lid = xcd_remap(blockIdx.x, p.nt * p.BH);
+        kt = lid % p.nt;
+        bh = lid / p.nt;
+    }
+    const int b = bh / p.H;
     const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
     const int j = lane & 31, h = lane >> 5;
     const int key0 = kt * 128;

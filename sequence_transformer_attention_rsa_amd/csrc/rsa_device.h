@@ -133,6 +133,23 @@ __device__ __forceinline__ int xcd_remap(int id, int n) {
     return (xcd < rem) ? xcd * (per + 1) + local : rem * (per + 1) + (xcd - rem) * per + local;
 }
 
+// Causal launches of nt tiles per head, whose work falls off with the
+// tile's rank (rank 0 heaviest). When the heads split evenly over the XCDs,
+// XCD x takes heads x, x + 8, ... and dispatches the rank-i tile of each
+// of them before the rank-(i + 1) tile of any, so the heavy tiles of all
+// its heads start first. Otherwise: xcd_remap order, rank = lid % nt.
+__device__ __forceinline__ void causal_order(int id, int nt, int BH, int& rank, int& bh) {
+    if (BH % kXcds == 0) {
+        const int xcd = id % kXcds, local = id / kXcds, hx = BH / kXcds;
+        rank = local / hx;
+        bh = xcd + kXcds * (local % hx);
+    } else {
+        const int lid = xcd_remap(id, nt * BH);
+        rank = lid % nt;
+        bh = lid / nt;
+    }
+}
+
 __device__ __forceinline__ bool wave_any(bool p) { return __any(p); }
 
 __device__ __forceinline__ float shfl_xor32(float x) { return __shfl_xor(x, 32); }

@@ -345,14 +345,21 @@ void rsa_fwd_bf16(FwdParams p) {
     __shared__ uint8_t tflag_bytes[FULL ? 4 : kFwdMaxTiles / 4];
     const TileTable tflag{tflag_bytes};
 
-    const int total = p.nqt * p.BH * p.groups;
-    const int lid = xcd_remap(blockIdx.x, total);
-    // causal: the last query tiles of a head see the most keys; dispatch them
-    // first so that the light ones fill the tail
-    const int qt = CAUSAL ? p.nqt - 1 - lid % p.nqt : lid % p.nqt;
-    const int rest = lid / p.nqt;
-    const int g = rest % p.groups;
-    const int bh = rest / p.groups;
+    int qt, g, bh;
+    if (CAUSAL && p.groups == 1) {
+        // the last query tiles of a head see the most keys: dispatch them
+        // first so that the light ones fill the tail
+        int rank;
+        causal_order(blockIdx.x, p.nqt, p.BH, rank, bh);
+        qt = p.nqt - 1 - rank;
+        g = 0;
+    } else {
+        const int lid = xcd_remap(blockIdx.x, p.nqt * p.BH * p.groups);
+        qt = CAUSAL ? p.nqt - 1 - lid % p.nqt : lid % p.nqt;
+        const int rest = lid / p.nqt;
+        g = rest % p.groups;
+        bh = rest / p.groups;
+    }
     const int b = bh / p.H;
 
     const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
