@@ -142,17 +142,10 @@ __global__ __launch_bounds__(kThreads, D == 64 ? (DROP ? 2 : 3) : 1) void rsa_bw
     __shared__ uint8_t tflag_bytes[FULL ? 4 : kFwdMaxTiles / 4];
     const TileTable tflag{tflag_bytes};
 
+    // causal: the last query tiles see the most keys; dispatch them first
     int qt, bh;
-    if constexpr (CAUSAL) {
-        // the last query tiles see the most keys: dispatch them first
-        int rank;
-        causal_order(blockIdx.x, p.nt, p.BH, rank, bh);
-        qt = p.nt - 1 - rank;
-    } else {
-        const int lid = xcd_remap(blockIdx.x, p.nt * p.BH);
-        qt = lid % p.nt;
-        bh = lid / p.nt;
-    }
+    head_order(blockIdx.x, p.nt, p.BH, CAUSAL, qt, bh);
+    if (CAUSAL) qt = p.nt - 1 - qt;
     const int b = bh / p.H;
     const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
     const int j = lane & 31, h = lane >> 5;
@@ -429,15 +422,9 @@ __global__ __launch_bounds__(kThreads, D == 64 ? ((CAUSAL || DROP) ? 2 : 3) : 1)
     // per wave: keep words [half hh][word w][row u]
     __shared__ __attribute__((aligned(16))) uint32_t keep_tab[DROP ? 4 * 2 * 4 * kKT : 1];
 
+    // causal: the first key tiles are seen by the most rows (tile 0 first)
     int kt, bh;
-    if constexpr (CAUSAL) {
-        // the first key tiles are seen by the most rows: dispatch them first
-        causal_order(blockIdx.x, p.nt, p.BH, kt, bh);
-    } else {
-        const int lid = xcd_remap(blockIdx.x, p.nt * p.BH);
-        kt = lid % p.nt;
-        bh = lid / p.nt;
-    }
+    head_order(blockIdx.x, p.nt, p.BH, CAUSAL, kt, bh);
     const int b = bh / p.H;
     const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
     const int j = lane & 31, h = lane >> 5;

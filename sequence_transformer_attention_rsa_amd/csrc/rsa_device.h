@@ -133,19 +133,22 @@ __device__ __forceinline__ int xcd_remap(int id, int n) {
     return (xcd < rem) ? xcd * (per + 1) + local : rem * (per + 1) + (xcd - rem) * per + local;
 }
 
-// Causal launches of nt tiles per head, whose work falls off with the
-// tile's rank (rank 0 heaviest). When the heads split evenly over the XCDs,
-// XCD x takes heads x, x + 8, ... and dispatches the rank-i tile of each
-// of them before the rank-(i + 1) tile of any, so the heavy tiles of all
-// its heads start first. Otherwise: xcd_remap order, rank = lid % nt.
-__device__ __forceinline__ void causal_order(int id, int nt, int BH, int& rank, int& bh) {
+// Tile t and head bh of workgroup id, for launches of nt tiles per head.
+// When the heads split evenly over the XCDs, XCD x (ids x, x + 8, ...) takes
+// heads x, x + 8, ...: a head's tiles share one L2, and every XCD gets the
+// same mix of batch rows, whose key padding differs. Within an XCD the tiles
+// go head by head, or, with rank_major (causal launches, whose tile t = 0 is
+// the heaviest), the t-th tile of each of its heads before the (t + 1)-th of
+// any, so that the heavy tiles start first. Other head counts: xcd_remap
+// order, head by head.
+__device__ __forceinline__ void head_order(int id, int nt, int BH, bool rank_major, int& t, int& bh) {
     if (BH % kXcds == 0) {
         const int xcd = id % kXcds, local = id / kXcds, hx = BH / kXcds;
-        rank = local / hx;
-        bh = xcd + kXcds * (local % hx);
+        t = rank_major ? local / hx : local % nt;
+        bh = xcd + kXcds * (rank_major ? local % hx : local / nt);
     } else {
         const int lid = xcd_remap(id, nt * BH);
-        rank = lid % nt;
+        t = lid % nt;
         bh = lid / nt;
     }
 }

@@ -346,12 +346,11 @@ void rsa_fwd_bf16(FwdParams p) {
     const TileTable tflag{tflag_bytes};
 
     int qt, g, bh;
-    if (CAUSAL && p.groups == 1) {
-        // the last query tiles of a head see the most keys: dispatch them
-        // first so that the light ones fill the tail
-        int rank;
-        causal_order(blockIdx.x, p.nqt, p.BH, rank, bh);
-        qt = p.nqt - 1 - rank;
+    if (p.groups == 1) {
+        // causal: the last query tiles of a head see the most keys; dispatch
+        // them first so that the light ones fill the tail
+        head_order(blockIdx.x, p.nqt, p.BH, CAUSAL, qt, bh);
+        if (CAUSAL) qt = p.nqt - 1 - qt;
         g = 0;
     } else {
         const int lid = xcd_remap(blockIdx.x, p.nqt * p.BH * p.groups);
