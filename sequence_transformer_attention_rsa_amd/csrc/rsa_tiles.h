@@ -75,7 +75,10 @@ __device__ __forceinline__ uint32_t causal_tile_class(int v0, int cnt, int n, in
 
 // Occupancy table of a workgroup's key tiles in LDS: the two bits of
 // key_tile_flags per tile, four tiles per byte. build() is called by all
-// `nthreads` threads and must be followed by a barrier before get().
+// `nthreads` threads (a multiple of the wave size) and must be followed by a
+// barrier before get(). Thread i classifies tile i (so every thread's mask
+// reads are in flight at once), and four neighbouring lanes combine their
+// flags into one byte.
 struct TileTable {
     uint8_t* bytes;
 
@@ -83,12 +86,11 @@ struct TileTable {
 
     template <class Flags>
     __device__ __forceinline__ void build(int ntile, int nthreads, Flags flags) const {
-        for (int i = threadIdx.x; 4 * i < ntile; i += nthreads) {
-            uint32_t b = 0;
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-                if (4 * i + e < ntile) b |= (uint32_t)flags(4 * i + e) << (2 * e);
-            bytes[i] = (uint8_t)b;
+        for (int t0 = 0; t0 < ntile; t0 += nthreads) {   // the same trip count in every thread
+            const int t = t0 + (int)threadIdx.x;
+            const uint32_t f = t < ntile ? (uint32_t)flags(t) : 0u;
+            const uint32_t b = f | (__shfl_down(f, 1) << 2) | (__shfl_down(f, 2) << 4) | (__shfl_down(f, 3) << 6);
+            if ((threadIdx.x & 3) == 0 && t < ntile) bytes[t >> 2] = (uint8_t)b;
         }
     }
 };
