@@ -16,6 +16,7 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWave = 64;
 constexpr int kXcds = 8;          // MI355X: 8 accelerator complex dies, one L2 each
+constexpr int kCUs = 256;         // MI355X: compute units
 constexpr float kLn2 = 0.69314718055994530942f;
 
 // ---------------------------------------------------------------- MFMA ---

@@ -326,11 +326,12 @@ __global__ __launch_bounds__(kThreads) void rsa_fwd_f32(FwdParams p) {
 // the output is scaled by 1 / (1 - p) at the end). The dropout instances run
 // at three waves per SIMD: the keep-decision generator does not fit 128
 // registers (11-16 of them went to scratch at four waves).
-template <int D, bool CONTIG, int QB, bool CAUSAL, bool FULL = false, bool DROP = false>
+template <int D, bool CONTIG, int QB, bool CAUSAL, bool FULL = false, bool DROP = false, bool KSPLIT = false>
 __global__ __launch_bounds__(256 / QB, (D == 64 && QB == 1) ? (DROP ? 3 : 4) : 2)
 void rsa_fwd_bf16(FwdParams p) {
     static_assert(!FULL || CONTIG, "whole tiles need chunk-aligned ranges");
     static_assert(!DROP || QB == 1, "dropout instances: one query block per wave");
+    static_assert(!KSPLIT || (QB == 1 && !CAUSAL && !DROP), "key-split instances: plain launches");
     // QB 32-row query blocks per wave; 128 query rows per workgroup either
     // way (4 waves x 32 rows, or 2 waves x 64 rows: each K and V^T fragment
     // read from LDS then feeds two MFMAs).
@@ -340,7 +341,11 @@ void rsa_fwd_bf16(FwdParams p) {
     using VTile = DirectTile<D, WAVES>;
     constexpr int BUF = KTile::BYTES + VTile::BYTES;
     constexpr int NBUF = 2;   // 4 x (2 x 16 KB + 4 KB) of LDS per CU at d = 64
-    constexpr int ROWS = 4 * 32;
+    // KSPLIT (small grids): 64 rows per workgroup, waves 0 and 1 take rows
+    // 0-31 and 32-63 against keys 0-31 of every tile, waves 2 and 3 the same
+    // rows against keys 32-63; the two halves merge at the end
+    constexpr int ROWS = KSPLIT ? 2 * 32 : 4 * 32;
+    constexpr int NKB = KSPLIT ? 1 : 2;   // 32-key blocks of a tile per wave
     __shared__ __attribute__((aligned(1024))) uint8_t smem[NBUF * BUF];
     __shared__ uint8_t tflag_bytes[FULL ? 4 : kFwdMaxTiles / 4];
     const TileTable tflag{tflag_bytes};
@@ -364,7 +369,8 @@ void rsa_fwd_bf16(FwdParams p) {
     const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
     const int j = lane & 31, h = lane >> 5;
     const int row0 = qt * ROWS;
-    const int wrow0 = row0 + wave * 32 * QB;
+    const int wrow0 = row0 + (KSPLIT ? (wave & 1) : wave) * 32 * QB;
+    const int khalf = KSPLIT ? wave >> 1 : 0;   // this wave's 32-key half of each tile
     const int n = (p.q_pos0 + row0) / p.Lc;
 
     const int step0 = g * p.spg;
@@ -481,11 +487,11 @@ void rsa_fwd_bf16(FwdParams p) {
         {
             u32x4 kf[2][D / 16];
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
+            for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-                for (int kq = 0; kq < D / 16; ++kq) kf[kb][kq] = KTile::chunk(kbuf, 32 * kb + j, 2 * kq + h);
+                for (int kq = 0; kq < D / 16; ++kq) kf[kb][kq] = KTile::chunk(kbuf, 32 * (kb + khalf) + j, 2 * kq + h);
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
+            for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
                 for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
@@ -495,7 +501,7 @@ void rsa_fwd_bf16(FwdParams p) {
 #pragma unroll
             for (int kq = 0; kq < D / 16; ++kq)
 #pragma unroll
-                for (int kb = 0; kb < 2; ++kb)
+                for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
                     for (int qb = 0; qb < QB; ++qb)
                         s[qb][kb] = mfma_32x32x16_bf16(kf[kb][kq], qf[qb][kq], s[qb][kb]);
@@ -508,9 +514,9 @@ void rsa_fwd_bf16(FwdParams p) {
                 // one shift by 4 h every bit position is a constant (no
                 // per-register masks held in registers)
                 const int tv0 = tile_v0(t);
-                const uint64_t bits = key_tile_bits(mrow, n, p.N, p.Lc, CONTIG, tv0, tile_end(tv0)) >> (4 * h);
+                const uint64_t bits = key_tile_bits(mrow, n, p.N, p.Lc, CONTIG, tv0, tile_end(tv0)) >> (4 * h + 32 * khalf);
 #pragma unroll
-                for (int kb = 0; kb < 2; ++kb)
+                for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
                     for (int r = 0; r < 16; ++r)
                         if (!((bits >> (32 * kb + 8 * (r >> 2) + (r & 3))) & 1ull)) {
@@ -555,7 +561,7 @@ void rsa_fwd_bf16(FwdParams p) {
         float tl0[QB], tl1[QB], tsum[QB];
         auto weights = [&](int qb) {
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
+            for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
                 for (int i = 0; i < 8; ++i) {
                     const float p0 = fast_exp2(fmaf(s[qb][kb][2 * i], p.sl2, nb[qb]));
@@ -567,8 +573,10 @@ void rsa_fwd_bf16(FwdParams p) {
             for (int i = 0; i < 8; i += 2) {
                 a0 = add_bf16x2(pk[qb][0][i], a0);
                 a1 = add_bf16x2(pk[qb][0][i + 1], a1);
-                a0 = add_bf16x2(pk[qb][1][i], a0);
-                a1 = add_bf16x2(pk[qb][1][i + 1], a1);
+                if constexpr (NKB == 2) {
+                    a0 = add_bf16x2(pk[qb][1][i], a0);
+                    a1 = add_bf16x2(pk[qb][1][i + 1], a1);
+                }
             }
             tl0[qb] = a0;
             tl1[qb] = a1;
@@ -586,8 +594,10 @@ void rsa_fwd_bf16(FwdParams p) {
                 float a = __builtin_fmaxf(s[qb][0][0], s[qb][0][1]);
 #pragma unroll
                 for (int r = 2; r < 16; r += 2) a = __builtin_fmaxf(a, __builtin_fmaxf(s[qb][0][r], s[qb][0][r + 1]));
+                if constexpr (NKB == 2) {
 #pragma unroll
-                for (int r = 0; r < 16; r += 2) a = __builtin_fmaxf(a, __builtin_fmaxf(s[qb][1][r], s[qb][1][r + 1]));
+                    for (int r = 0; r < 16; r += 2) a = __builtin_fmaxf(a, __builtin_fmaxf(s[qb][1][r], s[qb][1][r + 1]));
+                }
                 const float m_new = fmaxf(m_b[qb], fmaxf(a, shfl_xor32(a)));
                 const float alpha = fast_exp2((m_b[qb] - m_new) * p.sl2);
                 m_b[qb] = m_new;
@@ -639,12 +649,12 @@ void rsa_fwd_bf16(FwdParams p) {
                     }
             }
         }
-        // ---- O^T += V^T P^T, four 16-key steps
+        // ---- O^T += V^T P^T, 16-key steps over this wave's keys
 #pragma unroll
-        for (int stp = 0; stp < 4; ++stp) {
+        for (int stp = 0; stp < 2 * NKB; ++stp) {
             u32x4 vf[D / 32];
 #pragma unroll
-            for (int db = 0; db < D / 32; ++db) vf[db] = VTile::tfrag(vbuf, 16 * stp, 32 * db);
+            for (int db = 0; db < D / 32; ++db) vf[db] = VTile::tfrag(vbuf, 16 * stp + 32 * khalf, 32 * db);
 #pragma unroll
             for (int qb = 0; qb < QB; ++qb) {
                 const u32x4 bfrag = acc_frag(pk[qb], stp);
@@ -663,6 +673,41 @@ void rsa_fwd_bf16(FwdParams p) {
             if (body(C0{})) break;
             if (body(C1{})) break;
         }
+    }
+
+    if constexpr (KSPLIT) {
+        // The exact merge of the two key halves (as for ring-step groups):
+        // waves 2 and 3 hand their base, lane row sum and O to waves 0 and 1
+        // through LDS; then waves 0 and 1 finish the rows.
+        float* xs = reinterpret_cast<float*>(smem) + ((wave & 1) * kWave + lane) * 36;
+        const float lsum = l0[0] + l1[0];
+        __syncthreads();   // every wave is done with the tile buffers
+        if (khalf == 1) {
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+                for (int r4 = 0; r4 < 4; ++r4)
+                    *reinterpret_cast<f32x4*>(xs + 16 * db + 4 * r4) =
+                        f32x4{o[0][db][4 * r4], o[0][db][4 * r4 + 1], o[0][db][4 * r4 + 2], o[0][db][4 * r4 + 3]};
+            xs[32] = m_b[0];
+            xs[33] = lsum;
+        }
+        __syncthreads();
+        if (khalf == 1) return;
+        const float m1 = xs[32], ls1 = xs[33];
+        const float mm = fmaxf(m_b[0], m1);
+        const float a0 = fast_exp2((m_b[0] - mm) * p.sl2), a1 = fast_exp2((m1 - mm) * p.sl2);
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4) {
+                const f32x4 x = *reinterpret_cast<const f32x4*>(xs + 16 * db + 4 * r4);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) o[0][db][4 * r4 + e] = a0 * o[0][db][4 * r4 + e] + a1 * x[e];
+            }
+        m_b[0] = mm;
+        l0[0] = a0 * lsum + a1 * ls1;
+        l1[0] = 0.0f;
     }
 
     // ---- epilogue
@@ -807,6 +852,19 @@ hipError_t launch_t(const ForwardCall& c, hipStream_t stream) {
             else
                 hipLaunchKernelGGL((rsa_fwd_bf16<D, false, QB, true, false, true>), dim3((unsigned)total), block, 0,
                                    stream, p);
+        } else if (D == 64 && p.contiguous && !p.causal && c.groups == 1 && total <= 2 * kCUs) {
+            // few workgroups (at most two per CU): split each tile's keys
+            // between two wave pairs, 64 rows per workgroup, so that twice
+            // as many waves run
+            if constexpr (D == 64) {
+                p.nqt = (c.Lq + 63) / 64;
+                const dim3 grid((unsigned)((long long)p.nqt * p.BH));
+                if (p.mask == nullptr)
+                    hipLaunchKernelGGL((rsa_fwd_bf16<D, true, QB, false, true, false, true>), grid, block, 0, stream, p);
+                else
+                    hipLaunchKernelGGL((rsa_fwd_bf16<D, true, QB, false, false, false, true>), grid, block, 0, stream,
+                                       p);
+            }
         } else if (p.contiguous && !p.causal && p.mask == nullptr)
             hipLaunchKernelGGL((rsa_fwd_bf16<D, true, QB, false, true>), dim3((unsigned)total), block, 0, stream, p);
         else if (p.contiguous && p.causal && p.mask == nullptr && c.groups == 1 && p.Lc % 128 == 0 &&
