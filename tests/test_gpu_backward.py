@@ -8,7 +8,7 @@ import torch
 
 import rsa_inputs
 import sequence_transformer_attention_rsa_amd as rsa
-from gates import assert_parity
+from gates import LSE_TOL, assert_parity
 from gpu_util import device, report, from_dev, inputs, mask_dev, say, to_dev
 
 pytestmark = pytest.mark.gpu
@@ -125,6 +125,42 @@ def test_backward_workload_full_parity(oracle_lib):
         for h in range(w.H):
             sl = (bb, h)
             check_grads([g[sl] for g in got], [g[sl] for g in want], f"backward b={bb} h={h}")
+
+
+def test_mask_with_holes_on_a_large_grid(oracle_lib):
+    """A key mask with holes inside the sequence -- the first key, one whole
+    64-key tile, scattered keys across ten partly valid tiles, padding at
+    the end -- on a grid large enough for the standard (not key-split)
+    forward instance: B=1, H=20, L=4096, d=64, N=8 (640 workgroups of 128
+    rows). Output, lse, dQ, dK and dV of all heads against the oracle."""
+    B, H, L, d, N = 1, 20, 4096, 64, 8
+    dev = device()
+    x = inputs(B, H, L, d, seed=4242, dtype="bf16", with_dout=True)
+    rng = np.random.default_rng(4243)
+    m = np.ones((B, L), dtype=np.uint8)
+    m[0, 0] = 0
+    m[0, 320:384] = 0                              # tile 5, all of it
+    m[0, 640:1280][rng.random(640) < 0.15] = 0     # tiles 10-19, partly
+    m[0, 4000:] = 0                                # padding
+    x["mask"] = m
+    say("mask with holes, B=1 H=20 L=4096")
+    q, k, v, g = (to_dev(x[n], "bf16", dev) for n in ("q", "k", "v", "dout"))
+    md = mask_dev(m, dev)
+    out, lse = rsa.forward(q, k, v, md, N=N, return_lse=True)
+    dq, dk, dv = rsa.backward(q, k, v, out, g, lse, md, N=N)
+    torch.cuda.synchronize()
+    want_out, want_lse = oracle_lib.forward(x["q"], x["k"], x["v"], m, N=N)
+    report("holes forward out (20 heads)", assert_parity(from_dev(out), want_out, "bf16", "holes out"))
+    got_lse = lse.cpu().numpy().astype(np.float64)
+    assert np.all(np.isfinite(got_lse)) and np.all(np.isfinite(want_lse))
+    assert np.abs(got_lse - want_lse).max() <= LSE_TOL["bf16"]
+    want = oracle_lib.backward(x["q"], x["k"], x["v"], x["dout"], m, N=N)
+    got = [from_dev(t) for t in (dq, dk, dv)]
+    for name, a, b in zip(("dq", "dk", "dv"), got, want):
+        report(f"holes backward {name} (20 heads)", assert_parity(a, b, "bf16", f"holes {name}", grad=True))
+    masked = m[0] == 0
+    for name, a in (("dk", got[1]), ("dv", got[2])):
+        assert np.all(a[:, :, masked] == 0.0), f"holes {name}: a masked key's gradient is not zero"
 
 
 def test_backward_long_sequence_four_heads(oracle_lib):
