@@ -253,6 +253,31 @@ def test_rank_share_matches_oracle_small(oracle_lib, dtype, L, N, d):
         check_lse(lse.cpu().numpy().astype(np.float64), want_lse, dtype, f"rank {rank}")
 
 
+@pytest.mark.parametrize("rank", [0, 1])
+def test_rank_share_one_group(oracle_lib, rank):
+    """A rank share with 512 query tiles (B=1, H=16, L=8192, N=2: 4096 rows
+    per rank) runs in one ring-step group, in the instance with 64-row
+    workgroups whose wave pairs split each tile's keys; rank 1 starts half
+    way down the sequence. Key padding; 96 sampled rows of every head
+    against the oracle."""
+    B, H, L, d, N = 1, 16, 8192, 64, 2
+    Lc = L // N
+    dev = device()
+    x = inputs(B, H, L, d, seed=8192 + rank, dtype="bf16", valid_range=(5000, 7000))
+    k, v = to_dev(x["k"], "bf16", dev), to_dev(x["v"], "bf16", dev)
+    rows = np.arange(rank * Lc, (rank + 1) * Lc)
+    ql = to_dev(x["q"][:, :, rows], "bf16", dev)
+    say("rank share one group", rank, "valid", x["valid_len"])
+    out, lse = rsa.forward_rank(ql, k, v, mask_dev(x["mask"], dev), N=N, rank=rank, return_lse=True)
+    torch.cuda.synchronize()
+    out, lse = from_dev(out), lse.cpu().numpy().astype(np.float64)
+    pick = sample_rows(Lc, 96, seed=rank)
+    want, want_lse = oracle_lib.forward(x["q"][:, :, rows[pick]], x["k"], x["v"], x["mask"], N=N, qpos=rows[pick])
+    report(f"rank share one group, rank {rank} (96 rows x 16 heads)",
+           assert_parity(out[:, :, pick], want, "bf16", f"one-group rank {rank}"))
+    check_lse(lse[:, :, pick], want_lse, "bf16", f"one-group rank {rank}")
+
+
 @pytest.mark.parametrize("d", [64, 128])
 def test_forward_longest_key_range(oracle_lib, d):
     """L = 1048576, the longest key range one launch covers (its tile table
