@@ -133,9 +133,10 @@ __device__ __forceinline__ void load_rowvec(uint8_t* lds, const float* src, RowO
 // tiles up to the workgroup's last row are visible (the last two of them
 // partly, masked per element), then the earlier chunks, whole; the later
 // chunks are hidden.
-template <int D, bool CONTIG, bool CAUSAL, bool DROP = false, bool FULL = false>
+template <int D, bool CONTIG, bool CAUSAL, bool DROP = false, bool FULL = false, bool KSPLIT = false>
 __global__ __launch_bounds__(kThreads, D == 64 ? (DROP ? 2 : 3) : 1) void rsa_bwd_dq(BwdParams p) {
     static_assert(!FULL || CONTIG, "whole tiles need chunk-aligned, unmasked ranges");
+    static_assert(!KSPLIT || (!CAUSAL && !DROP), "key-split instances: plain launches");
     using T = DirectTile<D>;
     constexpr int BUF = 2 * T::BYTES;   // K, V
     __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * BUF];
@@ -149,8 +150,13 @@ __global__ __launch_bounds__(kThreads, D == 64 ? (DROP ? 2 : 3) : 1) void rsa_bw
     const int b = bh / p.H;
     const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
     const int j = lane & 31, h = lane >> 5;
-    const int row0 = qt * 128;
-    const int row = row0 + wave * 32 + j;
+    // KSPLIT (small grids): 64 rows per workgroup; waves 0 and 1 take rows
+    // 0-31 and 32-63 against keys 0-31 of every tile, waves 2 and 3 the same
+    // rows against keys 32-63, and their dQ parts are added at the end
+    constexpr int ROWS = KSPLIT ? 64 : 128;
+    const int khalf = KSPLIT ? wave >> 1 : 0;
+    const int row0 = qt * ROWS;
+    const int row = row0 + (KSPLIT ? wave & 1 : wave) * 32 + j;
     const bool row_ok = row < p.L;
     const int n = row0 / p.Lc;
     const int ntile = (p.L + kKT - 1) / kKT;
@@ -162,7 +168,7 @@ __global__ __launch_bounds__(kThreads, D == 64 ? (DROP ? 2 : 3) : 1) void rsa_bw
     const uint8_t* mrow = p.mask ? p.mask + (size_t)b * p.L : nullptr;
     const size_t rows_all = (size_t)p.BH * p.L;
 
-    const int qhi = min(row0 + 128, p.L) - 1;
+    const int qhi = min(row0 + ROWS, p.L) - 1;
     if constexpr (!FULL) {
         tflag.build(ntile, kThreads, [&](int t) {
             const uint32_t f = key_tile_flags(mrow, n, p.N, p.Lc, CONTIG, t * kKT, p.L);
@@ -206,7 +212,7 @@ __global__ __launch_bounds__(kThreads, D == 64 ? (DROP ? 2 : 3) : 1) void rsa_bw
         const float l = row_ok ? p.lse[(size_t)bh * p.L + row] : -INFINITY;
         nD = row_ok ? -dsum * p.dmul : 0.0f;
         nl2 = l == -INFINITY ? -INFINITY : -l * kLog2e;
-        if (row_ok && h == 0) {
+        if (row_ok && h == 0 && khalf == 0) {
             p.stats[(size_t)bh * p.L + row] = nD;
             p.stats[rows_all + (size_t)bh * p.L + row] = nl2;
         }
@@ -359,7 +365,9 @@ __global__ __launch_bounds__(kThreads, D == 64 ? (DROP ? 2 : 3) : 1) void rsa_bw
                     acc[db] = mfma_32x32x16_bf16(T::tfrag(kb, 32 * kb2 + 16 * hs, 32 * db), bfrag, acc[db]);
             }
         };
-        if constexpr (FULL) {
+        if constexpr (KSPLIT) {
+            half(khalf);
+        } else if constexpr (FULL) {
             half(0);
             half(1);
         } else {
@@ -379,6 +387,32 @@ __global__ __launch_bounds__(kThreads, D == 64 ? (DROP ? 2 : 3) : 1) void rsa_bw
             if (body(C0{})) break;
             if (body(C1{})) break;
         }
+    }
+
+    if constexpr (KSPLIT) {
+        // waves 2 and 3 hand their part of dQ to waves 0 and 1
+        constexpr int XS = (D / 32) * 16;   // floats per lane: its dQ part
+        static_assert(2 * kWave * XS * sizeof(float) <= sizeof(smem), "merge area inside the tile buffers");
+        float* xs = reinterpret_cast<float*>(smem) + ((wave & 1) * kWave + lane) * XS;
+        __syncthreads();   // every wave is done with the tile buffers
+        if (khalf == 1) {
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+                for (int r4 = 0; r4 < 4; ++r4)
+                    *reinterpret_cast<f32x4*>(xs + 16 * db + 4 * r4) =
+                        f32x4{acc[db][4 * r4], acc[db][4 * r4 + 1], acc[db][4 * r4 + 2], acc[db][4 * r4 + 3]};
+        }
+        __syncthreads();
+        if (khalf == 1) return;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4) {
+                const f32x4 x = *reinterpret_cast<const f32x4*>(xs + 16 * db + 4 * r4);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc[db][4 * r4 + e] += x[e];
+            }
     }
 
     if (row_ok) {
@@ -788,7 +822,21 @@ hipError_t launch_t(const BackwardCall& c, int stages, hipStream_t stream) {
         return hipSuccess;
     }
     if (stages & kBwdStageDq) {
-        if (contig && !p.causal && p.mask == nullptr)
+        if (D == 64 && contig && !p.causal && blocks <= 2 * kCUs) {
+            // few workgroups (at most two per CU): 64 rows per workgroup,
+            // each tile's keys split between two wave pairs
+            if constexpr (D == 64) {
+                BwdParams pq = p;
+                pq.nt = (c.L + 63) / 64;
+                const dim3 grid((unsigned)((long long)pq.nt * p.BH));
+                if (p.mask == nullptr)
+                    hipLaunchKernelGGL((rsa_bwd_dq<D, true, false, false, true, true>), grid, dim3(kThreads), 0, stream,
+                                       pq);
+                else
+                    hipLaunchKernelGGL((rsa_bwd_dq<D, true, false, false, false, true>), grid, dim3(kThreads), 0,
+                                       stream, pq);
+            }
+        } else if (contig && !p.causal && p.mask == nullptr)
             hipLaunchKernelGGL((rsa_bwd_dq<D, true, false, false, true>), dim3(blocks), dim3(kThreads), 0, stream, p);
         else if (contig && p.causal && p.mask == nullptr && p.Lc % 128 == 0)
             hipLaunchKernelGGL((rsa_bwd_dq<D, true, true, false, true>), dim3(blocks), dim3(kThreads), 0, stream, p);

@@ -679,7 +679,9 @@ void rsa_fwd_bf16(FwdParams p) {
         // The exact merge of the two key halves (as for ring-step groups):
         // waves 2 and 3 hand their base, lane row sum and O to waves 0 and 1
         // through LDS; then waves 0 and 1 finish the rows.
-        float* xs = reinterpret_cast<float*>(smem) + ((wave & 1) * kWave + lane) * 36;
+        constexpr int XS = (D / 32) * 16 + 4;   // floats per lane: O, base, row sum (16-byte rows)
+        static_assert(2 * kWave * XS * sizeof(float) <= sizeof(smem), "merge area inside the tile buffers");
+        float* xs = reinterpret_cast<float*>(smem) + ((wave & 1) * kWave + lane) * XS;
         const float lsum = l0[0] + l1[0];
         __syncthreads();   // every wave is done with the tile buffers
         if (khalf == 1) {
@@ -689,12 +691,12 @@ void rsa_fwd_bf16(FwdParams p) {
                 for (int r4 = 0; r4 < 4; ++r4)
                     *reinterpret_cast<f32x4*>(xs + 16 * db + 4 * r4) =
                         f32x4{o[0][db][4 * r4], o[0][db][4 * r4 + 1], o[0][db][4 * r4 + 2], o[0][db][4 * r4 + 3]};
-            xs[32] = m_b[0];
-            xs[33] = lsum;
+            xs[XS - 4] = m_b[0];
+            xs[XS - 3] = lsum;
         }
         __syncthreads();
         if (khalf == 1) return;
-        const float m1 = xs[32], ls1 = xs[33];
+        const float m1 = xs[XS - 4], ls1 = xs[XS - 3];
         const float mm = fmaxf(m_b[0], m1);
         const float a0 = fast_exp2((m_b[0] - mm) * p.sl2), a1 = fast_exp2((m1 - mm) * p.sl2);
 #pragma unroll
