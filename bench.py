@@ -4,10 +4,13 @@
 
 One step is one pass of the whole path over one batch of seeded synthetic
 input already resident in HBM: the forward over all N ranks (rsa_forward,
-writing O and lse) and the backward (rsa_backward_preprocess, rsa_backward_dq,
-rsa_backward_dkdv). Each call launches exactly one kernel, so HIP events
-recorded between the calls on the library's stream (torch's current stream)
-time every kernel separately. Rank-share workloads (--workload rank_share)
+writing O and lse) and the backward (rsa_backward, whose dQ kernel also forms
+the row statistics). The timed region runs K such steps with nothing between
+the calls. A second pass of K steps makes the backward as its three stage
+calls (rsa_backward_preprocess, rsa_backward_dq, rsa_backward_dkdv), each of
+which launches exactly one kernel, so HIP events recorded between the calls on
+the library's stream (torch's current stream) time every kernel separately;
+the causal and dropout backwards have no stage calls and are timed whole. Rank-share workloads (--workload rank_share)
 time rsa_forward_rank (split kernel + merge) and have no backward.
 `--forward-variant twopass` times rsa_forward_twopass instead (score rows
 materialised in HBM, row softmax, then P V; forward only): its roofline is
