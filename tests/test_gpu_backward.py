@@ -127,37 +127,42 @@ def test_backward_workload_full_parity(oracle_lib):
             check_grads([g[sl] for g in got], [g[sl] for g in want], f"backward b={bb} h={h}")
 
 
-def test_mask_with_holes_on_a_large_grid(oracle_lib):
+@pytest.mark.parametrize("H,L,N", [
+    (20, 4096, 8),   # 640 workgroups of 128 rows: the standard forward and dQ instances
+    (4, 1024, 4),    # 32 workgroups: the key-split forward and dQ (each wave pair one key half)
+])
+def test_mask_with_holes(oracle_lib, H, L, N):
     """A key mask with holes inside the sequence -- the first key, one whole
-    64-key tile, scattered keys across ten partly valid tiles, padding at
-    the end -- on a grid large enough for the standard (not key-split)
-    forward instance: B=1, H=20, L=4096, d=64, N=8 (640 workgroups of 128
-    rows). Output, lse, dQ, dK and dV of all heads against the oracle."""
-    B, H, L, d, N = 1, 20, 4096, 64, 8
+    64-key tile, scattered keys across several partly valid tiles (both
+    32-key halves), padding at the end -- at B=1, d=64, on a grid that takes
+    the standard instances and on one that takes the key-split ones. Output,
+    lse, dQ, dK and dV of all heads against the oracle."""
+    B, d = 1, 64
     dev = device()
-    x = inputs(B, H, L, d, seed=4242, dtype="bf16", with_dout=True)
-    rng = np.random.default_rng(4243)
+    x = inputs(B, H, L, d, seed=4242 + L, dtype="bf16", with_dout=True)
+    rng = np.random.default_rng(4243 + L)
     m = np.ones((B, L), dtype=np.uint8)
     m[0, 0] = 0
-    m[0, 320:384] = 0                              # tile 5, all of it
-    m[0, 640:1280][rng.random(640) < 0.15] = 0     # tiles 10-19, partly
-    m[0, 4000:] = 0                                # padding
+    m[0, 320:384] = 0                                 # tile 5, all of it
+    span = slice(640, 640 + L // 4)
+    m[0, span][rng.random(L // 4) < 0.15] = 0         # partly valid tiles
+    m[0, L - 96:] = 0                                 # padding
     x["mask"] = m
-    say("mask with holes, B=1 H=20 L=4096")
+    say("mask with holes", B, H, L, N)
     q, k, v, g = (to_dev(x[n], "bf16", dev) for n in ("q", "k", "v", "dout"))
     md = mask_dev(m, dev)
     out, lse = rsa.forward(q, k, v, md, N=N, return_lse=True)
     dq, dk, dv = rsa.backward(q, k, v, out, g, lse, md, N=N)
     torch.cuda.synchronize()
     want_out, want_lse = oracle_lib.forward(x["q"], x["k"], x["v"], m, N=N)
-    report("holes forward out (20 heads)", assert_parity(from_dev(out), want_out, "bf16", "holes out"))
+    report(f"holes forward out (L={L}, {H} heads)", assert_parity(from_dev(out), want_out, "bf16", "holes out"))
     got_lse = lse.cpu().numpy().astype(np.float64)
     assert np.all(np.isfinite(got_lse)) and np.all(np.isfinite(want_lse))
     assert np.abs(got_lse - want_lse).max() <= LSE_TOL["bf16"]
     want = oracle_lib.backward(x["q"], x["k"], x["v"], x["dout"], m, N=N)
     got = [from_dev(t) for t in (dq, dk, dv)]
     for name, a, b in zip(("dq", "dk", "dv"), got, want):
-        report(f"holes backward {name} (20 heads)", assert_parity(a, b, "bf16", f"holes {name}", grad=True))
+        report(f"holes backward {name} (L={L}, {H} heads)", assert_parity(a, b, "bf16", f"holes {name}", grad=True))
     masked = m[0] == 0
     for name, a in (("dk", got[1]), ("dv", got[2])):
         assert np.all(a[:, :, masked] == 0.0), f"holes {name}: a masked key's gradient is not zero"
