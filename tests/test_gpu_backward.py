@@ -170,9 +170,10 @@ def test_mask_with_holes(oracle_lib, H, L, N):
 
 def test_backward_long_sequence_four_heads(oracle_lib):
     """The bench's own step at B=2, H=12, L=8192, d=64, N=16, no mask: the
-    forward and the three backward stages exactly as the bench launches them
-    (preprocess, dQ, dK/dV), and the gradients of the first and last head of
-    both batch rows against the oracle, element by element."""
+    forward and the backward as the bench launches it (one rsa_backward
+    call, bitwise equal to the three stage calls its per-kernel pass times),
+    and the gradients of the first and last head of both batch rows against
+    the oracle, element by element."""
     w = rsa_inputs.WORKLOADS["long_seq"]
     dev = device()
     x = rsa_inputs.make_inputs(w.B, w.H, w.L, w.d, w.seed, w.dtype, w.scale, w.valid_range, with_dout=True)
@@ -182,7 +183,11 @@ def test_backward_long_sequence_four_heads(oracle_lib):
     stats = rsa.backward_preprocess(out, g, lse)
     dq = rsa.backward_dq(q, k, v, g, stats, None, N=w.N)
     dk, dv = rsa.backward_dkdv(q, k, v, g, stats, None, N=w.N)
+    # the one call the bench times (its dQ kernel forms the row statistics)
+    dq1, dk1, dv1 = rsa.backward(q, k, v, out, g, lse, None, N=w.N)
     torch.cuda.synchronize()
+    for name, a, b in (("dq", dq, dq1), ("dk", dk, dk1), ("dv", dv, dv1)):
+        assert torch.equal(a, b), f"long_seq {name}: one call differs from the stage calls"
     got = [from_dev(t) for t in (dq, dk, dv)]
     heads = ((0, 0), (0, w.H - 1), (1, 0), (1, w.H - 1))
     sel = lambda a: np.stack([a[b, h] for b, h in heads])[None]
