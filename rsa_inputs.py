@@ -133,6 +133,24 @@ WORKLOADS = {
 }
 
 
+def plant_score_jumps(x: dict, jump: float, positions) -> dict:
+    """Keys that outscore every other key by a chosen margin.
+
+    Every query row gets q[..., 0] = 2 and the key at positions[i] gets
+    k[..., 0] = (jump + i) * sqrt(d) / 2, so its score (after the 1/sqrt(d)
+    scale) exceeds the row's other scores by about jump + i natural units
+    when Q and K are otherwise drawn small (scale 0.5). Values stay
+    bf16-representable. Modifies and returns x.
+    """
+    d = x["q"].shape[-1]
+    x["q"][..., 0] = 2.0
+    for i, pos in enumerate(positions):
+        x["k"][..., pos, 0] = (jump + i) * np.sqrt(d) / 2.0
+    x["q"] = bf16_round(x["q"])
+    x["k"] = bf16_round(x["k"])
+    return x
+
+
 def make_inputs(B: int, H: int, L: int, d: int, seed: int, dtype: str = "bf16",
                 scale: float = 1.0, valid_range: Optional[Tuple[int, int]] = None,
                 Lq: Optional[int] = None, with_dout: bool = False) -> dict:

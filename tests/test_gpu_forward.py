@@ -141,6 +141,54 @@ def test_large_scores_stress(oracle_lib):
     assert np.abs(lse - want_lse).max() <= 2e-2
 
 
+@pytest.mark.parametrize("jump", [25.0, 60.0, 200.0])
+@pytest.mark.parametrize("H,L,d,causal", [
+    (2, 1024, 64, False),    # small grid: 64-row workgroups, keys split between wave pairs
+    (40, 2048, 64, False),   # 128-row workgroups
+    (2, 1024, 128, False),
+    (2, 1024, 64, True),
+])
+def test_late_score_jumps(oracle_lib, jump, H, L, d, causal):
+    """Three late keys outscore every other key by jump, jump + 1 and
+    jump + 2 natural units (positions in different tiles and chunks, met
+    after other tiles by most ranks). A jump of 25 moves the running base
+    after the weights were used; 60 and 200 overflow them (200 even to
+    infinity), and the workgroup must run its key range again."""
+    dev = device()
+    N = 4
+    x = inputs(1, H, L, d, seed=int(jump) + L + d, dtype="bf16", scale=0.5)
+    rsa_inputs.plant_score_jumps(x, jump, [L - 400, L - 200, L - 30])
+    say("late score jumps", jump, H, L, d, "causal" if causal else "")
+    q, k, v = (to_dev(x[n], "bf16", dev) for n in ("q", "k", "v"))
+    out, lse = rsa.forward(q, k, v, None, N=N, return_lse=True, causal=causal)
+    torch.cuda.synchronize()
+    want, want_lse = oracle_lib.forward(x["q"], x["k"], x["v"], None, N=N, causal=causal)
+    report(f"late score jumps {jump} H={H} L={L} d={d} causal={causal}",
+           assert_parity(from_dev(out), want, "bf16", f"jump {jump}"))
+    check_lse(lse.cpu().numpy().astype(np.float64), want_lse, "bf16", f"jump {jump}")
+
+
+@pytest.mark.parametrize("jump", [25.0, 60.0])
+def test_late_score_jumps_rank_share(oracle_lib, jump):
+    """The same planted keys in one rank's share, split over ring-step
+    groups (each group's partial has its own base before the merge)."""
+    dev = device()
+    B, H, L, d, N = 1, 2, 4096, 64, 8
+    Lc = L // N
+    x = inputs(B, H, L, d, seed=int(jump) + 7, dtype="bf16", scale=0.5)
+    rsa_inputs.plant_score_jumps(x, jump, [1000, 2100, 3900])
+    k, v = to_dev(x["k"], "bf16", dev), to_dev(x["v"], "bf16", dev)
+    for rank in (0, 3, 7):
+        rows = np.arange(rank * Lc, (rank + 1) * Lc)
+        ql = to_dev(x["q"][:, :, rows], "bf16", dev)
+        say("late score jumps, rank share", jump, rank)
+        out, lse = rsa.forward_rank(ql, k, v, None, N=N, rank=rank, return_lse=True)
+        torch.cuda.synchronize()
+        want, want_lse = oracle_lib.forward(x["q"][:, :, rows], x["k"], x["v"], None, N=N, qpos=rows)
+        assert_parity(from_dev(out), want, "bf16", f"jump {jump} rank {rank}")
+        check_lse(lse.cpu().numpy().astype(np.float64), want_lse, "bf16", f"jump {jump} rank {rank}")
+
+
 def test_forward_is_deterministic():
     dev = device()
     x = inputs(2, 4, 1024, 64, seed=11, dtype="bf16", valid_range=(700, 1024))
