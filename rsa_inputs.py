@@ -136,16 +136,22 @@ WORKLOADS = {
 def plant_score_jumps(x: dict, jump: float, positions) -> dict:
     """Keys that outscore every other key by a chosen margin.
 
-    Every query row gets q[..., 0] = 2 and the key at positions[i] gets
-    k[..., 0] = (jump + i) * sqrt(d) / 2, so its score (after the 1/sqrt(d)
-    scale) exceeds the row's other scores by about jump + i natural units
-    when Q and K are otherwise drawn small (scale 0.5). Values stay
-    bf16-representable. Modifies and returns x.
+    With n = len(positions) (at most d), every query row gets q[..., :n] = 2
+    and the key at positions[i] gets k[..., positions[i], i] =
+    (jump + i) * sqrt(d) / 2, so its score (after the 1/sqrt(d) scale)
+    exceeds the row's other scores by about jump + i natural units when Q
+    and K are otherwise drawn small (scale 0.5). Each planted key is large in
+    its own component: keys that shared one large component would make dQ a
+    small difference of large terms, which no bf16 dS operand resolves.
+    Values stay bf16-representable. Modifies and returns x.
     """
     d = x["q"].shape[-1]
-    x["q"][..., 0] = 2.0
+    n = len(positions)
+    if n > d:
+        raise ValueError("at most d planted keys")
+    x["q"][..., :n] = 2.0
     for i, pos in enumerate(positions):
-        x["k"][..., pos, 0] = (jump + i) * np.sqrt(d) / 2.0
+        x["k"][..., pos, i] = (jump + i) * np.sqrt(d) / 2.0
     x["q"] = bf16_round(x["q"])
     x["k"] = bf16_round(x["k"])
     return x

@@ -8,7 +8,7 @@ import torch
 
 import rsa_inputs
 import sequence_transformer_attention_rsa_amd as rsa
-from gates import LSE_TOL, assert_parity
+from gates import LSE_TOL, MAX_ABS, REL_FRO_GRAD, assert_parity, errors
 from gpu_util import device, report, from_dev, inputs, mask_dev, say, to_dev
 
 pytestmark = pytest.mark.gpu
@@ -49,6 +49,31 @@ def test_backward_small_parity(oracle_lib, d, L, N, valid):
     if x["mask"] is not None:
         for b, vl in enumerate(x["valid_len"]):
             assert np.all(got[1][b, :, vl:] == 0) and np.all(got[2][b, :, vl:] == 0)
+
+
+@pytest.mark.parametrize("jump", [25.0, 60.0])
+@pytest.mark.parametrize("d", [64, 128])
+def test_backward_late_score_jumps(oracle_lib, jump, d):
+    """Gradients when three late keys outscore every other key by jump,
+    jump + 1 and jump + 2 natural units (the forward's lazy rescale under
+    stress, and large lse). dK and dV of the planted keys reach 10-30, where
+    the bf16 rounding of the stored gradient alone exceeds the unit-scale
+    max-abs bound, so that bound is taken relative to max(1, max |want|);
+    the relative Frobenius bound is the usual one."""
+    dev = device()
+    L, N = 1024, 4
+    x = inputs(1, 2, L, d, seed=int(jump) * 3 + d, dtype="bf16", scale=0.5, with_dout=True)
+    rsa_inputs.plant_score_jumps(x, jump, [L - 400, L - 200, L - 30])
+    say("backward late score jumps", jump, d)
+    got = gpu_fwd_bwd(x, N, dev)
+    want = oracle_lib.backward(x["q"], x["k"], x["v"], x["dout"], None, N=N)
+    for name, a, b in zip(("dq", "dk", "dv"), got, want):
+        e = errors(a, b)
+        bound = MAX_ABS["bf16"] * max(1.0, float(np.abs(b).max()))
+        report(f"backward late score jumps {jump} d={d} {name}", e)
+        assert e["finite"], f"{name}: non-finite values"
+        assert e["max_abs"] <= bound, f"{name}: max-abs {e['max_abs']:.3e} > {bound:.3e}"
+        assert e["rel_fro"] <= REL_FRO_GRAD["bf16"], f"{name}: rel-fro {e['rel_fro']:.3e}"
 
 
 def test_backward_every_ring_size(oracle_lib):
