@@ -76,6 +76,35 @@ def test_backward_late_score_jumps(oracle_lib, jump, d):
         assert e["rel_fro"] <= REL_FRO_GRAD["bf16"], f"{name}: rel-fro {e['rel_fro']:.3e}"
 
 
+@pytest.mark.parametrize("variant", ["plain", "causal", "dropout"])
+def test_backward_d128_all_heads(oracle_lib, variant):
+    """d = 128 at a grid that fills the GPU's XCDs (B=2, H=4: eight heads, so
+    each XCD takes one; L = 2048, N = 8, key padding): forward and backward
+    through the C ABI, every element of out, lse, dQ, dK and dV of every
+    head against the oracle, plain, causal and with dropout 0.1."""
+    dev = device()
+    B, H, L, d, N = 2, 4, 2048, 128, 8
+    x = inputs(B, H, L, d, seed=128 + len(variant), dtype="bf16", valid_range=(1500, 2048), with_dout=True)
+    causal = variant == "causal"
+    drop = (0.1, 77, 3) if variant == "dropout" else None
+    q, k, v, g = (to_dev(x[n], "bf16", dev) for n in ("q", "k", "v", "dout"))
+    m = mask_dev(x["mask"], dev)
+    say("backward d=128 all heads", variant)
+    out, lse = rsa.forward(q, k, v, m, N=N, return_lse=True, causal=causal, dropout=drop)
+    dq, dk, dv = rsa.backward(q, k, v, out, g, lse, m, N=N, causal=causal, dropout=drop)
+    torch.cuda.synchronize()
+    want_o, want_lse = oracle_lib.forward(x["q"], x["k"], x["v"], x["mask"], N=N, causal=causal, dropout=drop)
+    report(f"backward d=128 {variant} out", assert_parity(from_dev(out), want_o, "bf16", f"d=128 {variant} out"))
+    got_lse = lse.cpu().numpy().astype(np.float64)
+    fin = np.isfinite(want_lse)
+    assert np.array_equal(np.isfinite(got_lse), fin)
+    assert np.abs(got_lse[fin] - want_lse[fin]).max() <= LSE_TOL["bf16"]
+    want = oracle_lib.backward(x["q"], x["k"], x["v"], x["dout"], x["mask"], N=N, causal=causal, dropout=drop)
+    for name, a, b in zip(("dq", "dk", "dv"), (dq, dk, dv), want):
+        report(f"backward d=128 {variant} {name}",
+               assert_parity(from_dev(a), b, "bf16", f"d=128 {variant} {name}", grad=True))
+
+
 def test_backward_every_ring_size(oracle_lib):
     dev = device()
     L, d = 256, 64
