@@ -310,6 +310,32 @@ def test_backward_f32_parity(oracle_lib, d, L, N, valid, causal):
             assert np.all(got[1][b, :, vl:] == 0) and np.all(got[2][b, :, vl:] == 0)
 
 
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_f32_eight_heads(oracle_lib, d, causal):
+    """fp32 at eight heads (B=2 H=4, L=1024, N=8, key padding): several
+    query and key tiles per head on every XCD, forward and backward against
+    the oracle at the fp32 gates."""
+    dev = device()
+    x = inputs(2, 4, 1024, d, seed=1024 + d + causal, dtype="f32", valid_range=(700, 1024), with_dout=True)
+    say("backward f32 eight heads", d, causal)
+    q, k, v, g = (to_dev(x[n], "f32", dev) for n in ("q", "k", "v", "dout"))
+    m = mask_dev(x["mask"], dev)
+    out, lse = rsa.forward(q, k, v, m, N=8, return_lse=True, causal=causal)
+    dq, dk, dv = rsa.backward(q, k, v, out, g, lse, m, N=8, causal=causal)
+    torch.cuda.synchronize()
+    want_o, want_lse = oracle_lib.forward(x["q"], x["k"], x["v"], x["mask"], N=8, causal=causal)
+    assert_parity(from_dev(out), want_o, "f32", f"f32 eight heads out d={d}")
+    got_lse = lse.cpu().numpy().astype(np.float64)
+    fin = np.isfinite(want_lse)
+    assert np.array_equal(np.isfinite(got_lse), fin)
+    assert np.abs(got_lse[fin] - want_lse[fin]).max() <= LSE_TOL["f32"]
+    want = oracle_lib.backward(x["q"], x["k"], x["v"], x["dout"], x["mask"], N=8, causal=causal)
+    for name, a, b in zip(("dq", "dk", "dv"), (dq, dk, dv), want):
+        report(f"f32 eight heads d={d} causal={causal} {name}",
+               assert_parity(from_dev(a), b, "f32", f"f32 eight heads {name}", grad=True))
+
+
 def test_backward_f32_workload_and_stages(oracle_lib):
     """The fp32 workload's shape (B=1 H=2 L=256 d=64 N=4) with an upstream
     gradient: the one-call backward equals its three stages bit for bit,
