@@ -162,6 +162,7 @@ def test_gelu_is_the_exact_erf_form():
     (2, 192, 256, 4, 1024, 3, (100, 192)),   # chunks of 64, key padding
     (1, 130, 512, 4, 512, 5, None),          # L not a multiple of 64 (chunks of 26 keys)
     (2, 256, 512, 4, 2048, 4, None),         # d = 128
+    (1, 1024, 1024, 8, 4096, 4, (700, 1024)),   # d = 128, E = 1024: 256-column product tiles
 ])
 def test_layer_small_parity(oracle_lib, B, L, E, H, F, N, valid):
     from oracle import layer as OL
