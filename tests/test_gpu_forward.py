@@ -151,9 +151,10 @@ def test_large_scores_stress(oracle_lib):
 def test_late_score_jumps(oracle_lib, jump, H, L, d, causal):
     """Three late keys outscore every other key by jump, jump + 1 and
     jump + 2 natural units (positions in different tiles and chunks, met
-    after other tiles by most ranks). A jump of 25 moves the running base
-    after the weights were used; 60 and 200 overflow them (200 even to
-    infinity), and the workgroup must run its key range again."""
+    after other tiles by most ranks). The weights of those tiles against
+    the running base are 2^36 to 2^289 (the largest overflow to infinity):
+    the base must move to the new maximum and the earlier tiles' sums and
+    products be rescaled, without losing either."""
     dev = device()
     N = 4
     x = inputs(1, H, L, d, seed=int(jump) + L + d, dtype="bf16", scale=0.5)
