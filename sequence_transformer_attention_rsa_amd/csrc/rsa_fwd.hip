@@ -303,9 +303,10 @@ __global__ __launch_bounds__(kThreads) void rsa_fwd_f32(FwdParams p) {
     }
 }
 
-// bf16 forward. Two LDS buffers: right after the barrier that opens tile t,
-// the copy of tile t+1 is issued into the buffer that held tile t-1 and
-// lands while tile t is computed. Chunk-aligned key ranges use copies the
+// bf16 forward. Two LDS buffers: after the barrier that opens tile t (at
+// d = 64 without causal mask or dropout: after tile t's score MFMAs), the
+// copy of tile t+1 is issued into the buffer that held tile t-1 and lands
+// while tile t is computed. Chunk-aligned key ranges use copies the
 // compiler does not track (see rsa_tiles.h), so nothing but the explicit
 // vm_wait before each barrier waits for them. Registers are held to 128 so
 // that four waves run per SIMD at d = 64 (two at d = 128): with several
@@ -346,6 +347,12 @@ void rsa_fwd_bf16(FwdParams p) {
     // rows against keys 32-63; the two halves merge at the end
     constexpr int ROWS = KSPLIT ? 2 * 32 : 4 * 32;
     constexpr int NKB = KSPLIT ? 1 : 2;   // 32-key blocks of a tile per wave
+    // d = 64 without causal mask or dropout: the copy of the next tile is
+    // issued after this tile's score MFMAs rather than before them, so that
+    // the first fragment reads and MFMAs of a tile do not queue behind the
+    // copy instructions (2% at L = 8192; the other instances measured
+    // slower that way)
+    constexpr bool LATE_COPY = D == 64 && !CAUSAL && !DROP;
     __shared__ __attribute__((aligned(1024))) uint8_t smem[NBUF * BUF];
     __shared__ uint8_t tflag_bytes[FULL ? 4 : kFwdMaxTiles / 4];
     const TileTable tflag{tflag_bytes};
@@ -477,7 +484,7 @@ void rsa_fwd_bf16(FwdParams p) {
         vm_wait<0>();
         bare_barrier();   // every wave's part of tile t landed, tile t-1 consumed
         const int tn = next_tile(t);
-        if (tn < tend) load(tn, CB ^ 1);
+        if (!LATE_COPY && tn < tend) load(tn, CB ^ 1);
         const uint8_t* kbuf = smem + CB * BUF;
         const uint8_t* vbuf = kbuf + KTile::BYTES;
 
@@ -506,6 +513,7 @@ void rsa_fwd_bf16(FwdParams p) {
                     for (int qb = 0; qb < QB; ++qb)
                         s[qb][kb] = mfma_32x32x16_bf16(kf[kb][kq], qf[qb][kq], s[qb][kb]);
         }
+        if (LATE_COPY && tn < tend) load(tn, CB ^ 1);
         // ---- key mask and range tail (tiles not fully valid)
         const bool part = FULL ? (CAUSAL && t >= tdiag && t < tpc) : !(tflag.get(t) & 2);
         if (part) {
